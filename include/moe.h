@@ -1,0 +1,201 @@
+/*
+ * moe.h — C ABI of libmoe_mi355x.so, a fused Mixture-of-Experts expert layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one GPU's share, all experts local):
+ *   top-k routing -> permutation of (token, slot) pairs by expert (+ in-kernel
+ *   activation quantisation) -> gate/up grouped GEMM -> SwiGLU (+ dynamic
+ *   per-block requantisation of the intermediate) -> down grouped GEMM ->
+ *   weighted top-k combine.
+ * It is the computation the pages describe for the FlashInfer b12x fused MoE
+ * (one call does routing, W1 GEMM, SwiGLU, W2 GEMM and the reduction; bf16
+ * hidden states are quantised inside) [vLLM PR 40082 report, "Implementation"
+ * item 1 and "Key source excerpts"] and for the MegaMoE NVFP4 / MXFP8 / BF16
+ * kernels [MegaMoE drop workflow, §1].
+ *
+ * Weight formats (canonical, caller-facing):
+ *   MOE_BF16  : W13 bf16 [E, 2I, H], W2 bf16 [E, H, I].
+ *   MOE_MXFP8 : e4m3fn codes, one e8m0 scale byte per 32 along K:
+ *               W13 u8 [E, 2I, H] + u8 [E, 2I, H/32]; W2 u8 [E, H, I] + u8 [E, H, I/32].
+ *   MOE_NVFP4 : e2m1 codes packed two per byte (element 2i in the low nibble),
+ *               one e4m3fn scale per 16 along K, one fp32 dequant multiplier
+ *               alpha per expert and tensor (= 1 / global scale) [vLLM PR
+ *               40082 report, "Key source excerpts": block scale = amax *
+ *               global scale / fp4 max, alpha = 1 / global scale]:
+ *               W13 u8 [E, 2I, H/2] + u8 [E, 2I, H/16] + f32 [E];
+ *               W2  u8 [E, H, I/2]  + u8 [E, H, I/16]  + f32 [E].
+ *   W13 rows [0, I) are the gate projection, rows [I, 2I) the up projection.
+ *
+ * Conventions of every entry point:
+ *   - Buffers are device pointers owned by the caller; the library never
+ *     allocates device memory, never synchronises the stream, never reads
+ *     device data on the host, and never writes its inputs.  Outputs are
+ *     written in place into the caller's buffers.
+ *   - Work is enqueued on `stream` (0 = the null stream) and is asynchronous;
+ *     device-side faults surface at the caller's next synchronisation.
+ *   - Arguments are checked on the host before anything is enqueued; on error
+ *     nothing is enqueued and a negative moe_status is returned.  T == 0 is a
+ *     successful no-op.  No exception or abort crosses the ABI.
+ *   - Expert ids are local ids in [0, E) (E = experts resident on this GPU).
+ *   - Calls are reentrant; the only library state is a per-device cache of
+ *     the compute-unit count and occupancy.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+typedef enum { MOE_BF16 = 0, MOE_MXFP8 = 1, MOE_NVFP4 = 2 } moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, T out of range, bad size */
+  MOE_ERR_UNSUPPORTED = -2, /* shape or dtype outside the supported set */
+  MOE_ERR_WORKSPACE = -3,   /* workspace or packed buffer too small */
+  MOE_ERR_LAUNCH = -4       /* a kernel launch failed (hipGetLastError) */
+} moe_status;
+
+/* Layer shape.  Supported: hidden % 128 == 0, inter % 128 == 0,
+ * 1 <= num_experts <= 1024, 1 <= top_k <= min(num_experts, 32),
+ * 1 <= max_tokens and max_tokens * top_k <= 2^24, dtype a moe_dtype. */
+typedef struct {
+  int32_t hidden;      /* H */
+  int32_t inter;       /* I, per expert */
+  int32_t num_experts; /* E, local */
+  int32_t top_k;       /* k */
+  int32_t max_tokens;  /* workspace capacity in tokens */
+  int32_t dtype;       /* moe_dtype of weights and activations */
+} moe_shape;
+
+/* Text of a status code (static storage). */
+MOE_API const char* moe_status_string(int32_t status);
+
+/* MOE_OK if the shape is supported, else MOE_ERR_UNSUPPORTED / INVALID_ARG. */
+MOE_API moe_status moe_check_shape(const moe_shape* shape);
+
+/* Sizes in bytes (0 for an unsupported shape). */
+MOE_API size_t moe_packed_weight_bytes(const moe_shape* shape);
+/* Workspace of moe_forward for any T <= max_tokens. */
+MOE_API size_t moe_workspace_bytes(const moe_shape* shape);
+/* Quantised activations of T tokens (moe_permute's xq): codes [T, H*b] at
+ * offset 0, then scales [T, H/blk] at moe_xq_scale_offset(shape, T).
+ *   BF16: bf16 [T, H], no scales;  MXFP8: u8 [T, H] + e8m0 [T, H/32];
+ *   NVFP4: packed e2m1 [T, H/2] + e4m3 [T, H/16]. */
+MOE_API size_t moe_xq_bytes(const moe_shape* shape, int32_t T);
+MOE_API size_t moe_xq_scale_offset(const moe_shape* shape, int32_t T);
+/* Requantised intermediate of the T*k pairs in expert-sorted order
+ * (moe_gemm13_swiglu_quant's hq), same scheme along I:
+ *   BF16: bf16 [P, I];  MXFP8: u8 [P, I] + e8m0 [P, I/32];
+ *   NVFP4: packed e2m1 [P, I/2] + e4m3 [P, I/16]  (P = T * k). */
+MOE_API size_t moe_hq_bytes(const moe_shape* shape, int32_t T);
+MOE_API size_t moe_hq_scale_offset(const moe_shape* shape, int32_t T);
+
+/* Quantise fp32 master weights of `count` stacked matrices [count, rows, K]
+ * into the canonical format of `dtype` (the load-time preprocessing step the
+ * pages describe for turning canonical weights into the kernel format
+ * [MegaMoE drop workflow, §3, preprocess_mega_weights]).
+ *   BF16 : codes = bf16 [count, rows, K]; scales, alpha unused (may be NULL).
+ *   MXFP8: codes u8 [count, rows, K], scales e8m0 [count, rows, K/32]; the
+ *          OCP MX rule s = floor(log2 amax) - 8 per block of 32.
+ *   NVFP4: codes packed [count, rows, K/2], scales e4m3 [count, rows, K/16],
+ *          alpha f32 [count] = amax(matrix) / (6 * 448) (1 if all zero);
+ *          block scale = e4m3(fp32(amax_blk / 6) / alpha), code =
+ *          e2m1(w / fp32(scale * alpha)), all fp32 operations correctly rounded.
+ * rows >= 1, K % 32 == 0 (MXFP8) / % 16 == 0 (NVFP4) / % 2 == 0 (BF16). */
+MOE_API moe_status moe_quantize_weights(int32_t dtype, int32_t count, int32_t rows, int32_t K,
+                                const float* w, void* codes, void* scales, float* alpha,
+                                hipStream_t stream);
+
+/* Repack canonical weights into the MFMA-ready tile layout in `packed`
+ * (moe_packed_weight_bytes bytes): per expert, W13 is cut into groups of 32
+ * gate rows + the matching 32 up rows, W2 into groups of 64 rows; each
+ * (row group, 128-wide K slice) is one contiguous block laid out in the
+ * per-lane operand order of the CDNA4 MFMA that consumes it, with scales in
+ * the matching per-lane order.  A pure byte permutation; done once at load
+ * time, not per forward [vLLM PR 40082 report, "Key source excerpts" and
+ * "Review highlights": the MMA-layout scale conversion is cached at load
+ * time; vLLM PR 38050 report, "Implementation": scale conversion and
+ * interleave when preparing weights for the CuteDSL kernel].
+ * Scales / alpha are NULL for BF16; alpha is NULL for MXFP8. */
+MOE_API moe_status moe_prepare_weights(const moe_shape* shape,
+                               const void* w13_codes, const void* w13_scales, const float* w13_alpha,
+                               const void* w2_codes, const void* w2_scales, const float* w2_alpha,
+                               void* packed, size_t packed_bytes, hipStream_t stream);
+
+/* Top-k routing of T tokens [vLLM PR 40082 report, "Implementation" item 1].
+ * logits fp32 [T, E] -> topk_ids int32 [T, k], topk_w fp32 [T, k].
+ * Experts are picked by logit descending, ties to the lower id (-0 == +0);
+ * slot j holds the j-th pick; weights are the softmax over the k picked
+ * logits (= full softmax restricted to the picks and renormalised).
+ * Non-finite logits give unspecified (but in-bounds) results. */
+MOE_API moe_status moe_route(const moe_shape* shape, int32_t T, const float* logits,
+                     int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* Token dispatch: permutation of the P = T*k pairs p = t*k + j by expert
+ * [vLLM PR 40082 report, "Key source excerpts": token dispatch fused with the
+ * GEMMs], plus the in-kernel quantisation of the bf16 hidden states x [T, H]
+ * into xq (layout of moe_xq_bytes; for BF16, xq may equal x: then nothing is
+ * copied) [same report: bf16 hidden states are quantised inside].
+ * Outputs: offsets int32 [E+1] (exclusive prefix of per-expert counts,
+ * offsets[E] = P), sorted_pairs int32 [P] (pairs in (expert, p) order),
+ * pair_pos int32 [P] (inverse: sorted_pairs[pair_pos[p]] == p).
+ * Expert ids must lie in [0, E) (undefined results otherwise).
+ * ws / ws_bytes: unused, may be NULL / 0. */
+MOE_API moe_status moe_permute(const moe_shape* shape, int32_t T, const int32_t* topk_ids, const uint16_t* x,
+                       int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, void* xq,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Gate/up grouped GEMM + SwiGLU + requantisation [vLLM PR 40082 report,
+ * "Implementation" item 1; "Key source excerpts": the intermediate uses
+ * dynamic per-block quantisation with global scale 1].
+ * For each expert e and sorted row r in [offsets[e], offsets[e+1]):
+ *   g, u = W13[e] . xq[sorted_pairs[r] / k]  (fp32 accumulation; NVFP4 scaled
+ *   by the W13 alpha), h = silu(g) * u, hq[r] = requant(h) (layout of
+ *   moe_hq_bytes).  ws / ws_bytes: unused, may be NULL / 0. */
+MOE_API moe_status moe_gemm13_swiglu_quant(const moe_shape* shape, int32_t T, const void* packed,
+                                   const int32_t* offsets, const int32_t* sorted_pairs, const void* xq,
+                                   void* hq, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Down grouped GEMM: for each expert e and sorted row r of it,
+ * y[sorted_pairs[r]] = bf16(W2[e] . hq[r]) (fp32 accumulation, NVFP4 scaled
+ * by the W2 alpha).  y is bf16 [T*k, H], row p = t*k + j (slot-major).
+ * ws / ws_bytes: unused, may be NULL / 0. */
+MOE_API moe_status moe_gemm2(const moe_shape* shape, int32_t T, const void* packed,
+                     const int32_t* offsets, const int32_t* sorted_pairs, const void* hq,
+                     uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Weighted top-k reduction [vLLM PR 40082 report, "Implementation" item 1]:
+ * out[t] = bf16( sum_{j=0..k-1} topk_w[t, j] * y[t*k + j] ), fp32, slot order
+ * (deterministic: the pages note that an in-kernel atomic fc2 reduce makes the
+ * order non-deterministic [MegaMoE drop workflow, §6]). */
+MOE_API moe_status moe_combine(const moe_shape* shape, int32_t T, const uint16_t* y, const float* topk_w,
+                       uint16_t* out, hipStream_t stream);
+
+/* The whole layer: route -> permute (+quant) -> gemm13 -> gemm2 -> combine,
+ * with every intermediate in `ws` (moe_workspace_bytes(shape) bytes, sized
+ * once for max_tokens; any T <= max_tokens reuses it [MegaMoE drop workflow,
+ * §6: knobs and buffers are sized once by the token capacity]).
+ * out bf16 [T, H].  topk_ids / topk_w: optional outputs (NULL = keep them in
+ * the workspace). */
+MOE_API moe_status moe_forward(const moe_shape* shape, int32_t T, const void* packed, const float* logits,
+                       const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

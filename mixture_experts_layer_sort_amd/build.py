@@ -1,0 +1,56 @@
+"""Build libmoe_mi355x.so (the HIP library) in-tree with hipcc for gfx950.
+
+    python -m mixture_experts_layer_sort_amd.build
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+LIB_NAME = "libmoe_mi355x.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+ARCH = "gfx950"
+
+FLAGS = [
+    "-O3",
+    "-std=c++17",
+    f"--offload-arch={ARCH}",
+    "-shared",
+    "-fPIC",
+    # packed fp32 arithmetic off: the compiler must not emit v_pk_{add,mul,fma}_f32
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # fp32 division and sqrt correctly rounded (quantisation decisions depend on it)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fvisibility=hidden",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the MoE library)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source under csrc/ into LIB_PATH; returns its path."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-I", os.path.join(PKG_DIR, "..", "include"), "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed with status {r.returncode}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,234 @@
+// C ABI entry points: host-side argument checks, then kernel launches on the
+// caller's stream.  Nothing here allocates device memory, synchronises, or
+// reads device data.
+#include <atomic>
+#include <climits>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Per-device cache of the compute-unit count (the library's only state).
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// occupancy of each GEMM variant, per device: [dev][dt][g13][nt-1]
+std::atomic<int> g_occ[kMaxDevices][3][2][2];
+
+int gemm_grid(int dt, bool g13, int T, int k, int E) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const int nt = (long long)T * k > 16LL * E ? 2 : 1;
+  int occ = 1;
+  if (dev >= 0 && dev < kMaxDevices) {
+    occ = g_occ[dev][dt][g13][nt - 1].load(std::memory_order_relaxed);
+    if (occ <= 0) {
+      occ = gemm_blocks_per_cu(dt, g13, nt);
+      g_occ[dev][dt][g13][nt - 1].store(occ, std::memory_order_relaxed);
+    }
+  }
+  return device_cu_count() * occ;
+}
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->dtype < MOE_BF16 || s->dtype > MOE_NVFP4) return MOE_ERR_UNSUPPORTED;
+  if (s->hidden <= 0 || s->inter <= 0 || s->hidden % 128 || s->inter % 128) return MOE_ERR_UNSUPPORTED;
+  if (s->hidden > (1 << 20) || s->inter > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  if (s->num_experts < 1 || s->num_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  if (s->top_k < 1 || s->top_k > 32 || s->top_k > s->num_experts) return MOE_ERR_UNSUPPORTED;
+  if (s->max_tokens < 1 || (long long)s->max_tokens * s->top_k > (1LL << 24)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_T(const moe_shape* s, int32_t T) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (T < 0 || T > s->max_tokens) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_WORKSPACE: return "workspace or packed buffer too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+moe_status moe_check_shape(const moe_shape* shape) { return check_shape(shape); }
+
+size_t moe_packed_weight_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return packed_layout(s->dtype, s->num_experts, s->hidden, s->inter).total;
+}
+
+size_t moe_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return workspace_layout(s->dtype, s->num_experts, s->hidden, s->inter, s->top_k, s->max_tokens).total;
+}
+
+size_t moe_xq_bytes(const moe_shape* s, int32_t T) {
+  if (check_T(s, T) != MOE_OK) return 0;
+  return act_bytes(s->dtype, T, s->hidden);
+}
+
+size_t moe_xq_scale_offset(const moe_shape* s, int32_t T) {
+  if (check_T(s, T) != MOE_OK) return 0;
+  return act_scale_offset(s->dtype, T, s->hidden);
+}
+
+size_t moe_hq_bytes(const moe_shape* s, int32_t T) {
+  if (check_T(s, T) != MOE_OK) return 0;
+  return act_bytes(s->dtype, T * s->top_k, s->inter);
+}
+
+size_t moe_hq_scale_offset(const moe_shape* s, int32_t T) {
+  if (check_T(s, T) != MOE_OK) return 0;
+  return act_scale_offset(s->dtype, T * s->top_k, s->inter);
+}
+
+moe_status moe_quantize_weights(int32_t dtype, int32_t count, int32_t rows, int32_t K, const float* w, void* codes,
+                                void* scales, float* alpha, hipStream_t stream) {
+  if (dtype < MOE_BF16 || dtype > MOE_NVFP4) return MOE_ERR_UNSUPPORTED;
+  if (count < 0 || rows < 1 || K < 1) return MOE_ERR_INVALID_ARG;
+  const int blk = dtype == MOE_MXFP8 ? 32 : (dtype == MOE_NVFP4 ? 16 : 8);
+  if (K % blk) return MOE_ERR_UNSUPPORTED;
+  if ((long long)count * rows * K > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  if (count == 0) return MOE_OK;
+  if (!w || !codes) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 && !scales) return MOE_ERR_INVALID_ARG;
+  if (dtype == MOE_NVFP4 && !alpha) return MOE_ERR_INVALID_ARG;
+  return launched(launch_quantize_weights(dtype, count, rows, K, w, codes, scales, alpha, stream));
+}
+
+moe_status moe_prepare_weights(const moe_shape* s, const void* w13_codes, const void* w13_scales,
+                               const float* w13_alpha, const void* w2_codes, const void* w2_scales,
+                               const float* w2_alpha, void* packed, size_t packed_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!w13_codes || !w2_codes || !packed) return MOE_ERR_INVALID_ARG;
+  if (s->dtype != MOE_BF16 && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
+  if (s->dtype == MOE_NVFP4 && (!w13_alpha || !w2_alpha)) return MOE_ERR_INVALID_ARG;
+  if (packed_bytes < moe_packed_weight_bytes(s)) return MOE_ERR_WORKSPACE;
+  return launched(launch_prepare(s->dtype, s->num_experts, s->hidden, s->inter, (const uint8_t*)w13_codes,
+                                 (const uint8_t*)w13_scales, w13_alpha, (const uint8_t*)w2_codes,
+                                 (const uint8_t*)w2_scales, w2_alpha, (uint8_t*)packed, stream));
+}
+
+moe_status moe_route(const moe_shape* s, int32_t T, const float* logits, int32_t* topk_ids, float* topk_w,
+                     hipStream_t stream) {
+  moe_status st = check_T(s, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  return launched(launch_route(logits, T, s->num_experts, s->top_k, topk_ids, topk_w, stream));
+}
+
+moe_status moe_permute(const moe_shape* s, int32_t T, const int32_t* topk_ids, const uint16_t* x, int32_t* offsets,
+                       int32_t* sorted_pairs, int32_t* pair_pos, void* xq, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_T(s, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !x || !offsets || !sorted_pairs || !pair_pos || !xq) return MOE_ERR_INVALID_ARG;
+  return launched(launch_permute(s->dtype, topk_ids, T, s->top_k, s->num_experts, s->hidden, offsets, sorted_pairs,
+                                 pair_pos, x, (uint8_t*)xq, stream));
+}
+
+moe_status moe_gemm13_swiglu_quant(const moe_shape* s, int32_t T, const void* packed, const int32_t* offsets,
+                                   const int32_t* sorted_pairs, const void* xq, void* hq, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_T(s, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!packed || !offsets || !sorted_pairs || !xq || !hq) return MOE_ERR_INVALID_ARG;
+  return launched(launch_gemm13(s->dtype, s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
+                                offsets, sorted_pairs, (const uint8_t*)xq, (uint8_t*)hq,
+                                gemm_grid(s->dtype, true, T, s->top_k, s->num_experts), stream));
+}
+
+moe_status moe_gemm2(const moe_shape* s, int32_t T, const void* packed, const int32_t* offsets,
+                     const int32_t* sorted_pairs, const void* hq, uint16_t* y, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_T(s, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!packed || !offsets || !sorted_pairs || !hq || !y) return MOE_ERR_INVALID_ARG;
+  return launched(launch_gemm2(s->dtype, s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
+                               offsets, sorted_pairs, (const uint8_t*)hq, y,
+                               gemm_grid(s->dtype, false, T, s->top_k, s->num_experts), stream));
+}
+
+moe_status moe_combine(const moe_shape* s, int32_t T, const uint16_t* y, const float* topk_w, uint16_t* out,
+                       hipStream_t stream) {
+  moe_status st = check_T(s, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!y || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  return launched(launch_combine(T, s->hidden, s->top_k, y, topk_w, out, stream));
+}
+
+moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const float* logits, const uint16_t* x,
+                       uint16_t* out, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status st = check_T(s, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!packed || !logits || !x || !out || !ws) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_workspace_bytes(s)) return MOE_ERR_WORKSPACE;
+  const int dt = s->dtype, E = s->num_experts, H = s->hidden, I = s->inter, k = s->top_k;
+  const WorkspaceLayout W = workspace_layout(dt, E, H, I, k, s->max_tokens);
+  uint8_t* base = (uint8_t*)ws;
+  int32_t* ids = topk_ids ? topk_ids : (int32_t*)(base + W.ids);
+  float* wts = topk_w ? topk_w : (float*)(base + W.wts);
+  int32_t* offsets = (int32_t*)(base + W.offsets);
+  int32_t* sorted_pairs = (int32_t*)(base + W.sorted_pairs);
+  int32_t* pair_pos = (int32_t*)(base + W.pair_pos);
+  uint8_t* xq = dt == DT_BF16 ? (uint8_t*)x : base + W.xq;
+  uint8_t* hq = base + W.hq;
+  uint16_t* y = (uint16_t*)(base + W.y);
+  hipError_t e = launch_route(logits, T, E, k, ids, wts, stream);
+  if (e == hipSuccess)
+    e = launch_permute(dt, ids, T, k, E, H, offsets, sorted_pairs, pair_pos, x, xq, stream);
+  if (e == hipSuccess)
+    e = launch_gemm13(dt, E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, xq, hq,
+                      gemm_grid(dt, true, T, k, E), stream);
+  if (e == hipSuccess)
+    e = launch_gemm2(dt, E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, hq, y,
+                     gemm_grid(dt, false, T, k, E), stream);
+  if (e == hipSuccess) e = launch_combine(T, H, k, y, wts, out, stream);
+  return launched(e);
+}
+
+}  // extern "C"

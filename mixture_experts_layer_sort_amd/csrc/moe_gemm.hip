@@ -1,0 +1,505 @@
+// Grouped expert GEMMs (gate/up + SwiGLU + requant, and down), weight
+// repacking and the top-k combine, for gfx950.
+//
+// GEMM work decomposition.  The pairs routed to expert e occupy sorted rows
+// [offsets[e], offsets[e+1]); they are cut into m-tiles of MT = 16*NT rows.
+// One work item = (expert, m-tile, weight row group of 64 rows); items are
+// numbered m-tile-major so neighbouring blocks share activation rows.  The
+// grid is persistent (sized to the resident capacity) and each block walks
+// items blockIdx.x, +gridDim.x, ...; every block derives the item -> expert
+// map from `offsets` itself (a scan of per-expert m-tile counts in LDS), so
+// no host synchronisation or extra launch is needed.  Inside a block the 4
+// waves split K into quarters, each streaming its slice of the 4 weight
+// tiles (16 rows each) through registers into MFMAs with the weights in the
+// M slot and the (<= 16*NT) routed tokens in the N slot, then reduce through
+// LDS.  This is the decode-shaped ("swap A/B") arrangement: weight rows fill
+// the matrix unit's 16-row side so a handful of tokens per expert wastes no
+// weight bandwidth [MegaMoE drop workflow, §1: the NVFP4 kernel package is
+// the "swapab" variant].
+#include "moe_kernels.h"
+
+namespace moe {
+
+constexpr int kGemmThreads = 256;
+
+struct GemmArgs {
+  const uint8_t* wcodes;
+  const uint8_t* wscales;
+  const float* walpha;
+  const int* offsets;
+  const int* sorted_pairs;
+  const uint8_t* act;         // B operand rows: xq (gemm13, row = token) or hq (gemm2, row = sorted row)
+  const uint8_t* act_scales;
+  uint8_t* out;               // hq codes (gemm13) or y (gemm2)
+  uint8_t* out_scales;        // hq scales (gemm13)
+  int E, K, G, KG, k, n_out;
+};
+
+// cum[e] = m-tiles of experts < e (LDS), returns the total.
+__device__ int build_schedule(const int* __restrict__ offsets, int E, int MT, int* cum, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 4 (E <= 1024)
+  const int e0 = tid * per;
+  int cnt[4] = {0, 0, 0, 0}, local = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int e = e0 + j;
+    if (j < per && e < E) {
+      cnt[j] = (offsets[e + 1] - offsets[e] + MT - 1) / MT;
+      local += cnt[j];
+    }
+  }
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int ww = 0; ww < w; ++ww) wbase += wsum[ww];
+  int run = wbase + incl - local;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int e = e0 + j;
+    if (j < per && e < E) {
+      cum[e] = run;
+      run += cnt[j];
+    }
+  }
+  if (tid == kGemmThreads - 1) cum[E] = wbase + incl;
+  __syncthreads();
+  return cum[E];
+}
+
+__device__ __forceinline__ int find_expert(const int* cum, int E, int mtg) {
+  int lo = 0, hi = E;  // cum[lo] <= mtg < cum[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cum[mid] <= mtg) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint8_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+
+// 8 e2m1 codes (one dword, element j in nibble j) times an exact e4m3 scale
+// -> 8 bf16 (exact: <= 6 significant bits).  The hardware convert is used at
+// scale 1.0 (pure conversion); the scale multiply is an fp32 multiply.
+__device__ __forceinline__ bf16x8_t nvfp4_dequant8(uint32_t codes, float sc) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 f[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0),
+                __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1),
+                __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2),
+                __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3)};
+  uint32_t o[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    float lo = f[b][0] * sc, hi = f[b][1] * sc;
+    o[b] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  }
+  bf16x8_t r;
+  __builtin_memcpy(&r, o, 16);
+  return r;
+}
+
+template <int DT, int NT, bool G13>
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
+  constexpr int MT = 16 * NT;
+  __shared__ int cum[1025];
+  __shared__ int wsum[4];
+  __shared__ f32x4_t red[3][4 * NT][64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int total_mt = build_schedule(a.offsets, a.E, MT, cum, wsum);
+  const long long total = (long long)total_mt * a.G;
+  const int kg_begin = (wv * a.KG) / 4, kg_end = ((wv + 1) * a.KG) / 4;
+  const size_t tcode = tile_code_bytes(DT), tscale = tile_scale_bytes(DT);
+
+  for (long long w = blockIdx.x; w < total; w += gridDim.x) {
+    const int mtg = (int)(w / a.G), g = (int)(w % a.G);
+    const int e = find_expert(cum, a.E, mtg);
+    const int r0 = a.offsets[e] + (mtg - cum[e]) * MT, r_end = a.offsets[e + 1];
+    int brow[NT];
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+      int r = r0 + 16 * s + i16;
+      brow[s] = r < r_end ? (G13 ? a.sorted_pairs[r] / a.k : r) : -1;
+    }
+    f32x4_t acc[4][NT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int s = 0; s < NT; ++s) acc[t][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int kg = kg_begin; kg < kg_end; ++kg) {
+      const size_t tile0 = ((size_t)(e * a.G + g) * a.KG + kg) * 4;
+      if constexpr (DT == DT_BF16) {
+        bf16x8_t A[4][4], B[NT][4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) A[t][c] = load_bf16x8(a.wcodes + (tile0 + t) * tcode + c * 1024 + lane * 16);
+#pragma unroll
+        for (int s = 0; s < NT; ++s)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            B[s][c] = brow[s] >= 0 ? load_bf16x8(a.act + ((size_t)brow[s] * a.K + kg * 128 + c * 32 + 8 * q) * 2)
+                                   : bf16x8_t{};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int s = 0; s < NT; ++s)
+              acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][c], B[s][c], acc[t][s], 0, 0, 0);
+      } else if constexpr (DT == DT_MXFP8) {
+        i32x8_t A[4], B[NT];
+        int SA[4], SB[NT];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint8_t* p = a.wcodes + (tile0 + t) * tcode + lane * 32;
+          i32x4_t lo = *reinterpret_cast<const i32x4_t*>(p), hi = *reinterpret_cast<const i32x4_t*>(p + 16);
+          A[t] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          SA[t] = a.wscales[(tile0 + t) * tscale + lane];
+        }
+#pragma unroll
+        for (int s = 0; s < NT; ++s) {
+          if (brow[s] >= 0) {
+            const uint8_t* p = a.act + (size_t)brow[s] * a.K + kg * 128 + 16 * q;
+            i32x4_t lo = *reinterpret_cast<const i32x4_t*>(p), hi = *reinterpret_cast<const i32x4_t*>(p + 64);
+            B[s] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            SB[s] = a.act_scales[(size_t)brow[s] * (a.K / 32) + kg * 4 + q];
+          } else {
+            B[s] = i32x8_t{};
+            SB[s] = 0;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int s = 0; s < NT; ++s)
+            acc[t][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[t], B[s], acc[t][s], 0, 0, 0, SA[t], 0,
+                                                                         SB[s]);
+      } else {  // NVFP4: e2m1 x e4m3 -> exact bf16, bf16 MFMA
+        uint4 AC[4];
+        uint2 AS[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          AC[t] = *reinterpret_cast<const uint4*>(a.wcodes + (tile0 + t) * tcode + lane * 16);
+          AS[t] = *reinterpret_cast<const uint2*>(a.wscales + (tile0 + t) * tscale + i16 * 8);
+        }
+        uint32_t BC[NT][4];
+        uint2 BS[NT];
+#pragma unroll
+        for (int s = 0; s < NT; ++s) {
+          if (brow[s] >= 0) {
+            const uint8_t* p = a.act + (size_t)brow[s] * (a.K / 2) + kg * 64 + 4 * q;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) BC[s][c] = *reinterpret_cast<const uint32_t*>(p + 16 * c);
+            BS[s] = *reinterpret_cast<const uint2*>(a.act_scales + (size_t)brow[s] * (a.K / 16) + kg * 8);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) BC[s][c] = 0;
+            BS[s] = make_uint2(0, 0);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          // scale byte of 16-block 2c + q/2 within this kgroup (bytes 0..3 in .x, 4..7 in .y)
+          const int sb = 2 * c + (q >> 1);
+          bf16x8_t B[NT];
+#pragma unroll
+          for (int s = 0; s < NT; ++s) {
+            uint32_t word = sb < 4 ? BS[s].x : BS[s].y;
+            B[s] = nvfp4_dequant8(BC[s][c], e4m3_to_f32((word >> (8 * (sb & 3))) & 0xFF));
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t cw = c == 0 ? AC[t].x : (c == 1 ? AC[t].y : (c == 2 ? AC[t].z : AC[t].w));
+            const uint32_t sw = sb < 4 ? AS[t].x : AS[t].y;
+            bf16x8_t A = nvfp4_dequant8(cw, e4m3_to_f32((sw >> (8 * (sb & 3))) & 0xFF));
+#pragma unroll
+            for (int s = 0; s < NT; ++s) acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[s], acc[t][s], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // reduce the four K quarters into wave 0
+    if (wv > 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < NT; ++s) red[wv - 1][t * NT + s][lane] = acc[t][s];
+    }
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < NT; ++s) acc[t][s] += red[0][t * NT + s][lane] + red[1][t * NT + s][lane] + red[2][t * NT + s][lane];
+      const float alpha = DT == DT_NVFP4 ? a.walpha[e] : 1.f;
+#pragma unroll
+      for (int s = 0; s < NT; ++s) {
+        const int r = r0 + 16 * s + i16;
+        const bool ok = r < r_end;
+        if constexpr (G13) {
+          // tiles 0,1 = gate rows 32g + 16tp + 4q + j; tiles 2,3 = the matching up rows
+          float h[2][4];
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float gv = acc[tp][s][j] * alpha, uv = acc[2 + tp][s][j] * alpha;
+              h[tp][j] = gv / (1.0f + expf(-gv)) * uv;
+            }
+          const int I = a.n_out;
+          if constexpr (DT == DT_BF16) {
+            if (ok) {
+              uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * g + 4 * q;
+#pragma unroll
+              for (int tp = 0; tp < 2; ++tp) {
+                uint2 v;
+                v.x = f32_to_bf16(h[tp][0]) | ((uint32_t)f32_to_bf16(h[tp][1]) << 16);
+                v.y = f32_to_bf16(h[tp][2]) | ((uint32_t)f32_to_bf16(h[tp][3]) << 16);
+                *reinterpret_cast<uint2*>(o + 16 * tp) = v;
+              }
+            }
+          } else if constexpr (DT == DT_MXFP8) {
+            // one block of 32 along I: [32g, 32g+32), spread over the 4 lanes sharing i16
+            float amax = 0.f;
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(h[tp][j]));
+            amax = wave_max_xor(amax, 16, 32);
+            const int sx = mx_scale_exp(amax);
+            if (ok) {
+              uint8_t* o = a.out + (size_t)r * I + 32 * g + 4 * q;
+#pragma unroll
+              for (int tp = 0; tp < 2; ++tp) {
+                uint32_t v = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v |= e4m3_from_f32(ldexpf(h[tp][j], -sx)) << (8 * j);
+                *reinterpret_cast<uint32_t*>(o + 16 * tp) = v;
+              }
+              if (q == 0) a.out_scales[(size_t)r * (I / 32) + g] = (uint8_t)(sx + 127);
+            }
+          } else {
+            // two blocks of 16 along I: [32g + 16tp, +16)
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+              float amax = fmaxf(fmaxf(fabsf(h[tp][0]), fabsf(h[tp][1])), fmaxf(fabsf(h[tp][2]), fabsf(h[tp][3])));
+              amax = wave_max_xor(amax, 16, 32);
+              const uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
+              const float sc = e4m3_to_f32(sc_code);
+              uint32_t v = 0;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                uint32_t c = sc > 0.f ? e2m1_from_f32(h[tp][j], sc) : ((__float_as_uint(h[tp][j]) >> 28) & 8u);
+                v |= c << (4 * j);
+              }
+              if (ok) {
+                *reinterpret_cast<uint16_t*>(a.out + (size_t)r * (I / 2) + 16 * g + 8 * tp + 2 * q) = (uint16_t)v;
+                if (q == 0) a.out_scales[(size_t)r * (I / 16) + 2 * g + tp] = (uint8_t)sc_code;
+              }
+            }
+          }
+        } else {
+          if (ok) {
+            const int p = a.sorted_pairs[r];
+            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)p * a.n_out + 64 * g + 4 * q;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              uint2 v;
+              v.x = f32_to_bf16(acc[t][s][0] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][1] * alpha) << 16);
+              v.y = f32_to_bf16(acc[t][s][2] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][3] * alpha) << 16);
+              *reinterpret_cast<uint2*>(o + 16 * t) = v;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ prepare (repack)
+
+template <int DT>
+__global__ void prepare_kernel(const uint8_t* __restrict__ src, const uint8_t* __restrict__ src_s, int E, int R,
+                               int K, int G, int KG, int I, int w13, uint8_t* __restrict__ dst,
+                               uint8_t* __restrict__ dst_s) {
+  const long long n = (long long)E * G * KG * 4 * 64;
+  for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < n;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx & 63);
+    const long long tile = idx >> 6;
+    const int t = (int)(tile & 3);
+    long long rest = tile >> 2;
+    const int kg = (int)(rest % KG);
+    rest /= KG;
+    const int g = (int)(rest % G);
+    const int e = (int)(rest / G);
+    const int i = lane & 15, q = lane >> 4;
+    const int row = w13 ? (t < 2 ? 32 * g + 16 * t + i : I + 32 * g + 16 * (t - 2) + i) : 64 * g + 16 * t + i;
+    const size_t rb = (size_t)e * R + row;
+    if constexpr (DT == DT_BF16) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<uint4*>(dst + tile * 4096 + c * 1024 + lane * 16) =
+            *reinterpret_cast<const uint4*>(src + (rb * K + kg * 128 + 32 * c + 8 * q) * 2);
+    } else if constexpr (DT == DT_MXFP8) {
+      const uint8_t* s = src + rb * K + kg * 128 + 16 * q;
+      *reinterpret_cast<uint4*>(dst + tile * 2048 + lane * 32) = *reinterpret_cast<const uint4*>(s);
+      *reinterpret_cast<uint4*>(dst + tile * 2048 + lane * 32 + 16) = *reinterpret_cast<const uint4*>(s + 64);
+      dst_s[tile * 64 + lane] = src_s[rb * (K / 32) + kg * 4 + q];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<uint32_t*>(dst + tile * 1024 + lane * 16 + 4 * c) =
+            *reinterpret_cast<const uint32_t*>(src + rb * (K / 2) + kg * 64 + 16 * c + 4 * q);
+      // row i's 8 scales of this kgroup, two bytes per lane
+      dst_s[tile * 128 + i * 8 + 2 * q] = src_s[rb * (K / 16) + kg * 8 + 2 * q];
+      dst_s[tile * 128 + i * 8 + 2 * q + 1] = src_s[rb * (K / 16) + kg * 8 + 2 * q + 1];
+    }
+  }
+}
+
+__global__ void copy_f32_kernel(const float* __restrict__ s, float* __restrict__ d, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) d[i] = s[i];
+}
+
+// ------------------------------------------------------------------ combine
+// out[t, h] = bf16( sum_j w[t, j] * y[t*k + j, h] ), fp32, slot order.
+__global__ void combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ wts, int T, int H, int k,
+                               uint16_t* __restrict__ out) {
+  const long long n = (long long)T * H / 8;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
+    const long long e0 = i * 8;
+    const int t = (int)(e0 / H), h = (int)(e0 % H);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+      const float wj = wts[(size_t)t * k + j];
+      const uint4 v = *reinterpret_cast<const uint4*>(y + ((size_t)t * k + j) * H + h);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        acc[2 * m] += wj * bf16_to_f32(u[m] & 0xFFFF);
+        acc[2 * m + 1] += wj * bf16_to_f32(u[m] >> 16);
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+    o.y = f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    o.z = f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+    o.w = f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out + e0) = o;
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+template <int DT, int NT, bool G13>
+static hipError_t launch_gemm_t(const GemmArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_kernel<DT, NT, G13>), dim3(grid), dim3(kGemmThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <bool G13>
+static hipError_t dispatch_gemm(int dt, int nt, const GemmArgs& a, int grid, hipStream_t s) {
+  if (dt == DT_BF16) return nt == 1 ? launch_gemm_t<DT_BF16, 1, G13>(a, grid, s) : launch_gemm_t<DT_BF16, 2, G13>(a, grid, s);
+  if (dt == DT_MXFP8) return nt == 1 ? launch_gemm_t<DT_MXFP8, 1, G13>(a, grid, s) : launch_gemm_t<DT_MXFP8, 2, G13>(a, grid, s);
+  return nt == 1 ? launch_gemm_t<DT_NVFP4, 1, G13>(a, grid, s) : launch_gemm_t<DT_NVFP4, 2, G13>(a, grid, s);
+}
+
+// token sub-tiles per item: 1 while an expert sees at most ~16 rows on average
+static int choose_nt(int T, int k, int E) { return (long long)T * k > 16LL * E ? 2 : 1; }
+
+int gemm_blocks_per_cu(int dt, bool g13, int nt) {
+  int n = 0;
+  hipError_t err = hipSuccess;
+#define MOE_OCC(D, N, G)                                                                                  \
+  if (dt == D && nt == N && g13 == G)                                                                     \
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(gemm_kernel<D, N, G>), \
+                                                       kGemmThreads, 0);
+  MOE_OCC(DT_BF16, 1, true) MOE_OCC(DT_BF16, 2, true) MOE_OCC(DT_BF16, 1, false) MOE_OCC(DT_BF16, 2, false)
+  MOE_OCC(DT_MXFP8, 1, true) MOE_OCC(DT_MXFP8, 2, true) MOE_OCC(DT_MXFP8, 1, false) MOE_OCC(DT_MXFP8, 2, false)
+  MOE_OCC(DT_NVFP4, 1, true) MOE_OCC(DT_NVFP4, 2, true) MOE_OCC(DT_NVFP4, 1, false) MOE_OCC(DT_NVFP4, 2, false)
+#undef MOE_OCC
+  if (err != hipSuccess || n < 1) n = 1;
+  return n;
+}
+
+hipError_t launch_gemm13(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const int* offsets,
+                         const int* sorted_pairs, const uint8_t* xq, uint8_t* hq, int grid, hipStream_t s) {
+  const PackedLayout L = packed_layout(dt, E, H, I);
+  GemmArgs a;
+  a.wcodes = packed + L.w13_codes;
+  a.wscales = packed + L.w13_scales;
+  a.walpha = reinterpret_cast<const float*>(packed + L.w13_alpha);
+  a.offsets = offsets;
+  a.sorted_pairs = sorted_pairs;
+  a.act = xq;
+  a.act_scales = xq + act_scale_offset(dt, T, H);
+  a.out = hq;
+  a.out_scales = hq + act_scale_offset(dt, T * k, I);
+  a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
+  return dispatch_gemm<true>(dt, choose_nt(T, k, E), a, grid, s);
+}
+
+hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const int* offsets,
+                        const int* sorted_pairs, const uint8_t* hq, uint16_t* y, int grid, hipStream_t s) {
+  const PackedLayout L = packed_layout(dt, E, H, I);
+  GemmArgs a;
+  a.wcodes = packed + L.w2_codes;
+  a.wscales = packed + L.w2_scales;
+  a.walpha = reinterpret_cast<const float*>(packed + L.w2_alpha);
+  a.offsets = offsets;
+  a.sorted_pairs = sorted_pairs;
+  a.act = hq;
+  a.act_scales = hq + act_scale_offset(dt, T * k, I);
+  a.out = reinterpret_cast<uint8_t*>(y);
+  a.out_scales = nullptr;
+  a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
+  return dispatch_gemm<false>(dt, choose_nt(T, k, E), a, grid, s);
+}
+
+hipError_t launch_prepare(int dt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13s, const float* w13a,
+                          const uint8_t* w2, const uint8_t* w2s, const float* w2a, uint8_t* packed, hipStream_t s) {
+  const PackedLayout L = packed_layout(dt, E, H, I);
+  const int threads = 256;
+  auto blocks = [&](long long n) { return (int)std::min((n + threads - 1) / threads, 1LL << 20); };
+  long long n13 = (long long)E * L.G13 * L.KG13 * 4 * 64, n2 = (long long)E * L.G2 * L.KG2 * 4 * 64;
+#define MOE_PREP(D)                                                                                              \
+  hipLaunchKernelGGL(prepare_kernel<D>, dim3(blocks(n13)), dim3(threads), 0, s, w13, w13s, E, 2 * I, H, L.G13,   \
+                     L.KG13, I, 1, packed + L.w13_codes, packed + L.w13_scales);                               \
+  hipLaunchKernelGGL(prepare_kernel<D>, dim3(blocks(n2)), dim3(threads), 0, s, w2, w2s, E, H, I, L.G2, L.KG2, I, \
+                     0, packed + L.w2_codes, packed + L.w2_scales);
+  if (dt == DT_BF16) { MOE_PREP(DT_BF16) }
+  else if (dt == DT_MXFP8) { MOE_PREP(DT_MXFP8) }
+  else {
+    MOE_PREP(DT_NVFP4)
+    hipLaunchKernelGGL(copy_f32_kernel, dim3((E + 255) / 256), dim3(256), 0, s, w13a,
+                       reinterpret_cast<float*>(packed + L.w13_alpha), E);
+    hipLaunchKernelGGL(copy_f32_kernel, dim3((E + 255) / 256), dim3(256), 0, s, w2a,
+                       reinterpret_cast<float*>(packed + L.w2_alpha), E);
+  }
+#undef MOE_PREP
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* wts, uint16_t* out, hipStream_t s) {
+  const long long n = (long long)T * H / 8;
+  const int threads = 256;
+  int blocks = (int)std::min((n + threads - 1) / threads, 65536LL);
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(threads), 0, s, y, wts, T, H, k, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,36 @@
+// Launchers of the library's kernels (internal).  Each returns the result of
+// hipGetLastError() after enqueueing on stream `s`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_device.h"
+#include "moe_layout.h"
+
+namespace moe {
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* wts, hipStream_t s);
+
+hipError_t launch_permute(int dt, const int* ids, int T, int k, int E, int H, int* offsets, int* sorted_pairs,
+                          int* pair_pos, const uint16_t* x, uint8_t* xq, hipStream_t s);
+
+hipError_t launch_quantize_weights(int dt, int count, int rows, int K, const float* w, void* codes, void* scales,
+                                   float* alpha, hipStream_t s);
+
+hipError_t launch_prepare(int dt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13s, const float* w13a,
+                          const uint8_t* w2, const uint8_t* w2s, const float* w2a, uint8_t* packed, hipStream_t s);
+
+// Grouped GEMMs.  `grid` is the persistent grid size (blocks).
+hipError_t launch_gemm13(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const int* offsets,
+                         const int* sorted_pairs, const uint8_t* xq, uint8_t* hq, int grid, hipStream_t s);
+
+hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const int* offsets,
+                        const int* sorted_pairs, const uint8_t* hq, uint16_t* y, int grid, hipStream_t s);
+
+hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* wts, uint16_t* out, hipStream_t s);
+
+// Blocks of the GEMM kernels that fit on one compute unit at once.
+int gemm_blocks_per_cu(int dt, bool gemm13, int nt);
+
+}  // namespace moe

@@ -1,0 +1,103 @@
+// Byte layouts shared by the host entry points and the kernels: the packed
+// (MFMA-ready) weight buffer, the quantised activation buffers and the
+// forward workspace.
+//
+// Packed weights.  K is cut into 128-wide slices ("kgroups").  A "tile" is 16
+// weight rows x one kgroup, stored in the per-lane operand order of the CDNA4
+// matrix instruction that consumes it (lane l = 16*q + i holds row i):
+//   BF16  (v_mfma_f32_16x16x32_bf16, 4 per kgroup): [chunk c<4][lane][8 bf16],
+//         lane (i,q) of chunk c holds k = 32c + 8q .. +8           (4096 B)
+//   MXFP8 (v_mfma_scale_f32_16x16x128_f8f6f4, fp8 operands): [lane][32 B],
+//         lane (i,q) holds k = 16q..16q+16 then 64+16q..64+16q+16;
+//         scale block q (k = 32q..32q+32) is lane (i,q)'s scale byte (2048 B
+//         codes + 64 B scales)
+//   NVFP4 (dequantised to bf16 in registers, then bf16 MFMA):
+//         [lane][4 chunks x 4 B] of e2m1 nibbles, lane (i,q) of chunk c holds
+//         k = 32c + 8q .. +8; scales [row i][8 e4m3 bytes] in K order, lane
+//         (i,q) of chunk c uses byte 2c + q/2            (1024 B + 128 B)
+// Row groups: W13 group g = gate rows 32g..32g+32 (tiles 0,1) and up rows
+// I+32g..I+32g+32 (tiles 2,3), so SwiGLU pairs sit in the same lanes;
+// W2 group g = rows 64g..64g+64 (tiles 0..3).  Block (e, g, kgroup) holds its
+// 4 tiles contiguously: index ((e * G + g) * KG + kg) * 4 + t.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define MOE_HD __host__ __device__ inline
+#else
+#define MOE_HD inline
+#endif
+
+namespace moe {
+
+enum { DT_BF16 = 0, DT_MXFP8 = 1, DT_NVFP4 = 2 };
+
+constexpr int kKGroup = 128;   // K slice of one tile
+constexpr int kTileRows = 16;  // rows of one tile
+constexpr int kTilesPerGroup = 4;
+
+MOE_HD size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// bytes of one tile's codes / scales
+MOE_HD size_t tile_code_bytes(int dt) { return dt == DT_BF16 ? 4096 : (dt == DT_MXFP8 ? 2048 : 1024); }
+MOE_HD size_t tile_scale_bytes(int dt) { return dt == DT_BF16 ? 0 : (dt == DT_MXFP8 ? 64 : 128); }
+
+// element bytes (x2 for nvfp4: half a byte) and scale block of a format
+MOE_HD size_t row_code_bytes(int dt, int K) { return dt == DT_BF16 ? (size_t)K * 2 : (dt == DT_MXFP8 ? (size_t)K : (size_t)K / 2); }
+MOE_HD int scale_block(int dt) { return dt == DT_MXFP8 ? 32 : (dt == DT_NVFP4 ? 16 : 0); }
+MOE_HD size_t row_scale_bytes(int dt, int K) { return dt == DT_BF16 ? 0 : (size_t)K / scale_block(dt); }
+
+struct PackedLayout {
+  int G13, KG13, G2, KG2;
+  size_t w13_codes, w13_scales, w2_codes, w2_scales, w13_alpha, w2_alpha, total;
+};
+
+MOE_HD PackedLayout packed_layout(int dt, int E, int H, int I) {
+  PackedLayout L;
+  L.G13 = I / 32;
+  L.KG13 = H / kKGroup;
+  L.G2 = H / 64;
+  L.KG2 = I / kKGroup;
+  size_t n13 = (size_t)E * L.G13 * L.KG13 * kTilesPerGroup;  // tiles of W13
+  size_t n2 = (size_t)E * L.G2 * L.KG2 * kTilesPerGroup;     // tiles of W2
+  size_t off = 0;
+  L.w13_codes = off; off = align256(off + n13 * tile_code_bytes(dt));
+  L.w13_scales = off; off = align256(off + n13 * tile_scale_bytes(dt));
+  L.w2_codes = off; off = align256(off + n2 * tile_code_bytes(dt));
+  L.w2_scales = off; off = align256(off + n2 * tile_scale_bytes(dt));
+  L.w13_alpha = off; off = align256(off + (dt == DT_NVFP4 ? (size_t)E * 4 : 0));
+  L.w2_alpha = off; off = align256(off + (dt == DT_NVFP4 ? (size_t)E * 4 : 0));
+  L.total = off;
+  return L;
+}
+
+// Quantised activation rows (xq: rows = tokens, K = H; hq: rows = pairs, K = I):
+// codes [rows, row_code_bytes] at 0, scales [rows, row_scale_bytes] after.
+MOE_HD size_t act_scale_offset(int dt, int rows, int K) { return align256((size_t)rows * row_code_bytes(dt, K)); }
+MOE_HD size_t act_bytes(int dt, int rows, int K) {
+  return act_scale_offset(dt, rows, K) + align256((size_t)rows * row_scale_bytes(dt, K));
+}
+
+// moe_forward workspace, sized for max_tokens.
+struct WorkspaceLayout {
+  size_t ids, wts, offsets, sorted_pairs, pair_pos, xq, hq, y, total;
+};
+
+MOE_HD WorkspaceLayout workspace_layout(int dt, int E, int H, int I, int k, int max_tokens) {
+  WorkspaceLayout W;
+  size_t P = (size_t)max_tokens * k, off = 0;
+  W.ids = off; off = align256(off + P * 4);
+  W.wts = off; off = align256(off + P * 4);
+  W.offsets = off; off = align256(off + (size_t)(E + 1) * 4);
+  W.sorted_pairs = off; off = align256(off + P * 4);
+  W.pair_pos = off; off = align256(off + P * 4);
+  W.xq = off; off = align256(off + (dt == DT_BF16 ? 0 : act_bytes(dt, max_tokens, H)));
+  W.hq = off; off = align256(off + act_bytes(dt, (int)P, I));
+  W.y = off; off = align256(off + P * (size_t)H * 2);
+  W.total = off;
+  return W;
+}
+
+}  // namespace moe

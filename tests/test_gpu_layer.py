@@ -1,0 +1,206 @@
+"""Parity of the HIP library with the CPU oracle at sizes the oracle finishes
+in seconds (several tiles, ragged tails, edge cases).  Bit-exact: routing ids,
+permutation, quantised activations and quantised weights.  Tolerance: router
+weights 1e-6 absolute; layer output relative L2 <= 1e-2 (bf16, MXFP8) or
+3e-2 (NVFP4) and max |diff| <= 5e-2 * RMS."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as gh
+import mixture_experts_layer_sort_amd as lib
+import moe_inputs as mi
+from oracle import moe as omoe
+from oracle import quant as oquant
+
+pytestmark = pytest.mark.gpu
+
+W = mi.WORKLOADS
+SMALL = {
+    "tiny_bf16": W["tiny_bf16"],
+    "bf16_ragged": W["bf16_decode"].scaled(T=33, H=512, I=384, E=16),
+    "mxfp8_decode_small": W["mxfp8_decode"].scaled(T=40, H=640, I=256, E=32),
+    "nvfp4_decode_small": W["nvfp4_decode_t8"].scaled(T=13, H=512, I=256, E=48),
+    "mxfp8_prefill_small": W["mxfp8_prefill"].scaled(T=300, H=512, I=256, E=16, k=4),
+    "nvfp4_prefill_small": W["nvfp4_decode_t128"].scaled(T=96, H=384, I=128, E=8, k=3),
+    "bf16_prefill_small": W["bf16_decode"].scaled(T=150, H=256, I=256, E=6, k=2),
+    "bf16_singleton": W["tiny_bf16"].scaled(E=1, k=1, T=5),
+    "mxfp8_singleton": W["mxfp8_decode"].scaled(E=1, k=1, T=7, H=256, I=128),
+    "nvfp4_singleton": W["nvfp4_decode_t8"].scaled(E=1, k=1, T=3, H=256, I=128),
+    "bf16_k_equals_E": W["tiny_bf16"].scaled(E=4, k=4, T=9, H=128, I=128),
+    "mxfp8_min": W["mxfp8_decode"].scaled(T=1, H=128, I=128, E=3, k=2),
+}
+
+
+def _setup(w):
+    cw, w13f, w2f = gh.canonical_from_host_master(w)
+    Wo = omoe.quantize_weights({e: w13f[e] for e in range(w.E)}, {e: w2f[e] for e in range(w.E)}, w.dtype)
+    return cw, Wo
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_parity_small(name):
+    w = SMALL[name]
+    print(f"case {name}: {w}", flush=True)
+    cw, Wo = _setup(w)
+    # the library's weight quantiser reproduces the oracle's canonical codes bit for bit
+    got = gh.canonical_to_numpy(cw)
+    for n in ("w13", "w2", "w13_s", "w2_s", "w13_a", "w2_a"):
+        ref = getattr(Wo, n)
+        if ref is None:
+            assert got[n] is None
+            continue
+        for e in range(w.E):
+            assert np.array_equal(np.asarray(got[n][e]), np.asarray(ref[e])), (n, e)
+
+    x = mi.host_x(w)
+    logits = mi.host_logits(w)
+    layer = gh.DeviceLayer(w, cw)
+    xd, ld = gh.to_device_x(x), torch.from_numpy(logits).to(gh.dev())
+    r = layer.staged(xd, ld)
+    torch.cuda.synchronize()
+    ref = omoe.moe_layer(x, logits, Wo, w.k, keep=True)
+
+    # routing
+    assert np.array_equal(r["ids"].cpu().numpy(), ref.ids)
+    assert np.max(np.abs(r["wts"].cpu().numpy() - ref.weights)) <= 1e-6
+    # permutation
+    off, sp, pp = omoe.permute(ref.ids, w.E)
+    assert np.array_equal(r["offsets"].cpu().numpy(), off)
+    assert np.array_equal(r["sorted_pairs"].cpu().numpy()[: w.P], sp)
+    assert np.array_equal(r["pair_pos"].cpu().numpy()[: w.P], pp)
+    # quantised activations
+    xc, xs, _ = omoe.quantize_x(x, w.dtype)
+    gc, gs = layer.xq_numpy(r, w.T)
+    assert np.array_equal(gc, xc)
+    if xs is not None:
+        assert np.array_equal(gs, xs)
+    # requantised intermediate, expert-sorted: compare dequantised values
+    hc, hs = layer.hq_numpy(r, w.T)
+    h_got = oquant.dequantize_act(hc, hs, w.dtype)
+    h_ref = np.stack([ref.h[(int(p) // w.k, int(p) % w.k)][2] for p in sp])
+    assert gh.rel_l2(h_got, h_ref) <= gh.out_tolerance(w.dtype)
+    # expert outputs y (bf16, slot-major)
+    y_got = gh.bf16_numpy(r["y"])[: w.P].astype(np.uint32)
+    y_ref = np.stack([ref.y[(p // w.k, p % w.k)] for p in range(w.P)])
+    assert gh.rel_l2((y_got << 16).view(np.float32), y_ref) <= gh.out_tolerance(w.dtype)
+    # the layer output
+    out_staged = gh.bf16_numpy(r["out"])
+    rel, mad = gh.check_out(out_staged, ref.out, w.dtype, name)
+    print(f"  out relL2 {rel:.2e}  max|d|/rms {mad:.2e}", flush=True)
+
+    # the fused entry runs the same kernels: bitwise equal, and reproducible
+    ids = torch.empty(w.T, w.k, dtype=torch.int32, device=gh.dev())
+    wts = torch.empty(w.T, w.k, dtype=torch.float32, device=gh.dev())
+    o1 = layer.forward(xd, ld, ids=ids, wts=wts)
+    o2 = layer.forward(xd, ld)
+    torch.cuda.synchronize()
+    assert np.array_equal(gh.bf16_numpy(o1), out_staged)
+    assert np.array_equal(gh.bf16_numpy(o2), out_staged)
+    assert torch.equal(ids, r["ids"]) and torch.equal(wts, r["wts"])
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (7, 8, 2), (64, 64, 6), (33, 256, 8), (5, 384, 8), (3, 1024, 32),
+                                   (200, 1000, 9), (4, 40, 40)])
+def test_route_parity(T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    l = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    # plant exact ties and signed zeros
+    l[:, : min(E, 5)] = 0.5
+    if E > 8:
+        l[0, 6] = -0.0
+        l[0, 7] = 0.0
+    s = lib.make_shape(128, 128, E, k, T, "bf16")
+    ids = torch.empty(T, k, dtype=torch.int32, device=gh.dev())
+    wts = torch.empty(T, k, dtype=torch.float32, device=gh.dev())
+    lib.moe_route(s, T, torch.from_numpy(l).to(gh.dev()), ids, wts)
+    torch.cuda.synchronize()
+    rid, rw = omoe.route(l, k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.max(np.abs(wts.cpu().numpy() - rw)) <= 1e-6
+
+
+@pytest.mark.parametrize("T,E,k,mode", [(8192, 256, 8, "zipf"), (1, 1, 1, "one"), (100, 64, 6, "all_one_expert"),
+                                        (3000, 1024, 4, "uniform"), (513, 7, 7, "uniform")])
+def test_permute_parity(T, E, k, mode):
+    rng = np.random.default_rng(T + E)
+    if mode == "all_one_expert":
+        ids = np.full((T, k), E - 1, np.int32)
+    elif mode == "zipf":
+        p = np.arange(1, E + 1, dtype=np.float64) ** -1.1
+        ids = rng.choice(E, (T, k), p=p / p.sum()).astype(np.int32)
+    else:
+        ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    H = 128
+    s = lib.make_shape(H, 128, E, k, T, "mxfp8")
+    d = gh.dev()
+    x = mi.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    off = torch.empty(E + 1, dtype=torch.int32, device=d)
+    sp = torch.empty(T * k, dtype=torch.int32, device=d)
+    pp = torch.empty(T * k, dtype=torch.int32, device=d)
+    xq = torch.empty(lib.moe_xq_bytes(s, T), dtype=torch.uint8, device=d)
+    lib.moe_permute(s, T, torch.from_numpy(ids).to(d), gh.to_device_x(x), off, sp, pp, xq)
+    torch.cuda.synchronize()
+    ro, rs, rp = omoe.permute(ids, E)
+    assert np.array_equal(off.cpu().numpy(), ro)
+    assert np.array_equal(sp.cpu().numpy(), rs)
+    assert np.array_equal(pp.cpu().numpy(), rp)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8", "nvfp4"])
+def test_quantize_weights_edge_values(dtype):
+    """Zeros, signed zeros, tiny, huge and tie values through the library's
+    weight quantiser, bit-exact against the oracle's."""
+    rng = np.random.default_rng(5)
+    rows, K = 24, 256
+    w = (rng.standard_normal((3, rows, K)) * np.exp(rng.uniform(-30, 30, (3, rows, 1)))).astype(np.float32)
+    w[0, 0] = 0.0
+    w[0, 1, :16] = -0.0
+    w[0, 2] = np.float32(1e-40)  # fp32 subnormals
+    w[1, 3, :32] = 480.0
+    w[1, 4] = np.float32(3.0e38)
+    w[2] = 0.0  # an all-zero matrix (NVFP4 alpha = 1)
+    d = gh.dev()
+    wd = torch.from_numpy(w).to(d)
+    cb = {"bf16": 2 * K, "mxfp8": K, "nvfp4": K // 2}[dtype]
+    codes = torch.zeros(3, rows, cb, dtype=torch.uint8, device=d)
+    scales = torch.zeros(3, rows, max(K // {"bf16": K, "mxfp8": 32, "nvfp4": 16}[dtype], 1), dtype=torch.uint8, device=d)
+    alpha = torch.zeros(3, dtype=torch.float32, device=d)
+    lib.moe_quantize_weights(dtype, 3, rows, K, wd, codes, scales, alpha)
+    torch.cuda.synchronize()
+    for m in range(3):
+        c, s_, a = oquant.quantize_weight(w[m], dtype)
+        got = codes[m].cpu().numpy()
+        if dtype == "bf16":
+            got = got.view(np.uint16)
+        assert np.array_equal(got, c), m
+        if s_ is not None:
+            assert np.array_equal(scales[m].cpu().numpy(), s_), m
+        if a is not None:
+            assert alpha[m].item() == float(a), m
+
+
+def test_zero_tokens_is_a_noop():
+    w = SMALL["tiny_bf16"]
+    cw, _ = _setup(w)
+    layer = gh.DeviceLayer(w, cw)
+    out = torch.full((1, w.H), 7.0, dtype=torch.bfloat16, device=gh.dev())
+    x = torch.zeros(0, w.H, dtype=torch.bfloat16, device=gh.dev())
+    l = torch.zeros(0, w.E, dtype=torch.float32, device=gh.dev())
+    layer.forward(x, l, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_fewer_tokens_than_capacity_reuses_workspace():
+    """A workspace sized for max_tokens serves any T <= max_tokens."""
+    w = SMALL["mxfp8_decode_small"]
+    cw, Wo = _setup(w)
+    layer = gh.DeviceLayer(w, cw, max_tokens=4 * w.T)
+    x = mi.host_x(w)
+    logits = mi.host_logits(w)
+    for T in (w.T, 5, 1):
+        out = layer.forward(gh.to_device_x(x[:T].copy()), torch.from_numpy(logits[:T].copy()).to(gh.dev()))
+        torch.cuda.synchronize()
+        ref = omoe.moe_layer(x[:T], logits[:T], Wo, w.k)
+        gh.check_out(gh.bf16_numpy(out), ref.out, w.dtype, f"T={T}")
