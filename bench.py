@@ -1,0 +1,267 @@
+"""Benchmark of the fused MoE expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the whole layer over one batch (route -> permute +
+activation quantisation -> gate/up GEMM + SwiGLU + requant -> down GEMM ->
+combine) with inputs and prepared weights already resident in HBM.  The
+default workload is the bf16 decode layer (T=64, H=4096, I=1408, E=64,
+top-6).  Prints one JSON line with tokens/s, the roofline of the dominant
+kernel (gate/up GEMM, timed with HIP events on the launch stream over the
+timed region), the whole-layer HBM fraction and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "nvfp4": 2500.0}  # dense; NVFP4 runs bf16 MFMA
+DEFAULT_WORKLOAD = "bf16_decode"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_sort_amd", "csrc", "moe_gemm.hip")
+
+
+def weight_bytes_per_elem(dtype):
+    # codes + block scales (MXFP8: 1 + 1/32, NVFP4: 1/2 + 1/16)
+    return {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32, "nvfp4": 0.5 + 1.0 / 16}[dtype]
+
+
+def act_bytes_per_elem(dtype):
+    return weight_bytes_per_elem(dtype)
+
+
+def kernel_source_hash():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per gate/up GEMM launch from committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"gemm13_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def build_layer(w, device):
+    """Device inputs (seeded generators), library-quantised canonical weights
+    and the prepared (packed) weights."""
+    import torch
+
+    import mixture_experts_layer_sort_amd as lib
+    import moe_inputs as mi
+    from tests import gpu_harness as gh
+
+    cw = gh.alloc_canonical(w)
+    for e in range(w.E):
+        w13, w2 = mi.device_master_weights(w, e, device)
+        gh.quantize_expert(w, cw, e, w13, w2)
+        del w13, w2
+    layer = gh.DeviceLayer(w, cw)
+    x = mi.device_x(w, device)
+    logits = mi.device_logits(w, device)
+    torch.cuda.synchronize()
+    return lib, gh, cw, layer, x, logits
+
+
+class StagedStep:
+    """The layer as its five entry points on torch's current stream, with HIP
+    events around each kernel launch (the same kernels moe_forward runs)."""
+
+    NAMES = ("route", "permute", "gemm13", "gemm2", "combine")
+
+    def __init__(self, lib, layer, x, logits):
+        import torch
+
+        w, s, d = layer.w, layer.shape, x.device
+        self.lib, self.layer, self.x, self.logits, self.s = lib, layer, x, logits, s
+        T, P = w.T, w.T * w.k
+        self.T = T
+        self.ids = torch.empty(T, w.k, dtype=torch.int32, device=d)
+        self.wts = torch.empty(T, w.k, dtype=torch.float32, device=d)
+        self.off = torch.empty(w.E + 1, dtype=torch.int32, device=d)
+        self.sp = torch.empty(P, dtype=torch.int32, device=d)
+        self.pp = torch.empty(P, dtype=torch.int32, device=d)
+        self.xq = x if w.dtype == "bf16" else torch.empty(lib.moe_xq_bytes(s, T), dtype=torch.uint8, device=d)
+        self.hq = torch.empty(lib.moe_hq_bytes(s, T), dtype=torch.uint8, device=d)
+        self.y = torch.empty(P, w.H, dtype=torch.bfloat16, device=d)
+        self.out = torch.empty(T, w.H, dtype=torch.bfloat16, device=d)
+        self.events = []
+
+    def run(self, timed=False):
+        import torch
+
+        lib, s, T, L = self.lib, self.s, self.T, self.layer
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if timed else None
+        rec = (lambda i: ev[i].record()) if timed else (lambda i: None)
+        rec(0)
+        lib.moe_route(s, T, self.logits, self.ids, self.wts)
+        rec(1)
+        lib.moe_permute(s, T, self.ids, self.x, self.off, self.sp, self.pp, self.xq)
+        rec(2)
+        lib.moe_gemm13_swiglu_quant(s, T, L.packed, self.off, self.sp, self.xq, self.hq)
+        rec(3)
+        lib.moe_gemm2(s, T, L.packed, self.off, self.sp, self.hq, self.y)
+        rec(4)
+        lib.moe_combine(s, T, self.y, self.wts, self.out)
+        rec(5)
+        if timed:
+            self.events.append(ev)
+
+    def kernel_ms(self):
+        """Average duration (ms) of each kernel over the recorded steps."""
+        n = len(self.events)
+        return {name: sum(e[i].elapsed_time(e[i + 1]) for e in self.events) / n for i, name in enumerate(self.NAMES)}
+
+
+def layer_bytes_flops(w, n_active):
+    """Algorithmic bytes and flops of one step: weights (with scales) of the
+    active experts, x in, out, logits; flops 6*H*I per routed pair."""
+    wb = n_active * 3 * w.H * w.I * weight_bytes_per_elem(w.dtype)
+    B = wb + 2 * w.T * w.H * 2 + 4 * w.T * w.E
+    F = w.T * w.k * 6.0 * w.H * w.I
+    return B, F
+
+
+def gemm13_bytes(w, n_active):
+    """Algorithmic bytes of one gate/up GEMM launch: W13 of the active experts
+    (with scales), the quantised activations read, the intermediate written."""
+    return (n_active * 2 * w.I * w.H * weight_bytes_per_elem(w.dtype) + w.T * w.H * act_bytes_per_elem(w.dtype)
+            + w.T * w.k * w.I * act_bytes_per_elem(w.dtype))
+
+
+def cpu_baseline(w, device, ids, max_seconds=25.0):
+    """The CPU oracle on a bounded sample of the same workload (first tokens),
+    with its own weights quantised from the same seeded fp32 masters."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import moe_inputs as mi
+    from oracle import moe as omoe
+
+    x = mi.device_x(w, device).view(torch.int16).cpu().numpy().view(np.uint16)
+    logits = mi.device_logits(w, device).cpu().numpy()
+    # sample size: tokens whose experts' dequantisation + products take ~10-25 s
+    per_expert_s = {"bf16": 0.25, "mxfp8": 2.0, "nvfp4": 2.5}[w.dtype] * (w.H * w.I) / (4096 * 1408)
+    n = 0
+    experts = set()
+    while n < w.T:
+        nxt = experts | set(ids[n].tolist())
+        if n > 0 and len(nxt) * per_expert_s > max_seconds:
+            break
+        experts, n = nxt, n + 1
+    w13, w2 = {}, {}
+    for e in sorted(experts):
+        a, b = mi.device_master_weights(w, e, device)
+        w13[e], w2[e] = a.cpu().numpy(), b.cpu().numpy()
+    Wo = omoe.quantize_weights(w13, w2, w.dtype)  # weight quantisation: not timed
+    del w13, w2
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    t0 = time.perf_counter()
+    omoe.moe_layer(x[:n], logits[:n], Wo, w.k)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens ({len(experts)} experts), fp64 per-token loop, "
+                      f"{dt:.1f} s wall, weight quantisation excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
+              "(expert-parallel sharding across GPUs is not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+
+    device = torch.device("cuda:0")
+    if args.copy_probe:
+        a = torch.ones(1 << 28, dtype=torch.float32, device=device)  # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": a.numel() * 4}))
+        return
+
+    w = mi.WORKLOADS[args.workload]
+    lib, gh, cw, layer, x, logits = build_layer(w, device)
+    del cw
+    step = StagedStep(lib, layer, x, logits)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    ids = step.ids.cpu().numpy()
+    n_active = int(len(np.unique(ids)))
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run(timed=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1e3 * elapsed / args.steps
+    kms = step.kernel_ms()
+
+    B, F = layer_bytes_flops(w, n_active)
+    g13_bytes = gemm13_bytes(w, n_active)
+    g13_gbs = g13_bytes / (kms["gemm13"] * 1e-3) / 1e9
+    layer_gbs = B / (ms_step * 1e-3) / 1e9
+    traffic = load_traffic(w.name)
+    decode = w.T * w.k <= 16 * w.E
+    rec = {
+        "metric": "MoE layer tokens/s; % HBM BW (decode) / % MFMA peak (prefill)",
+        "value": w.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) x and logits, N(0,0.02) weights; random init)",
+        "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.k,
+                   "weights": w.dtype, "routing_skew": w.bias, "active_experts": n_active},
+        "roofline": {"bound": "hbm", "kernel": "gemm13_swiglu_quant", "achieved": g13_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": g13_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": g13_bytes, "avg_launch_ms": kms["gemm13"]},
+        "layer": {"algorithmic_bytes": B, "flops": F, "hbm_gbs": layer_gbs, "hbm_frac": layer_gbs / HBM_PEAK_GBS,
+                  "mfma_tflops": F / (ms_step * 1e-3) / 1e12,
+                  "mfma_frac": F / (ms_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+                  "regime": "decode" if decode else "prefill", "kernel_ms": kms},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, device, ids)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -105,6 +105,23 @@ __device__ __forceinline__ bf16x8_t nvfp4_dequant8(uint32_t codes, float sc) {
   return r;
 }
 
+// 8 e4m3 codes (two dwords, element j in byte j) times 2^(e - 127) (an e8m0
+// scale byte) -> 8 bf16.  Exact: 4 significant bits, and the convert applies
+// the power-of-two scale by exponent arithmetic.  (The gfx950 scaled fp8
+// matrix instruction is not used: its internal accumulation keeps only about
+// 14 bits relative to the sum of |products|, measured.)
+__device__ __forceinline__ bf16x8_t mxfp8_dequant8(uint32_t lo, uint32_t hi, uint32_t e8m0) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const float sc = __uint_as_float(e8m0 << 23);  // 2^(e8m0 - 127); byte 0 -> 0 (all-zero block)
+  bf16x2 r[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false),
+                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true),
+                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false),
+                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true)};
+  bf16x8_t o;
+  __builtin_memcpy(&o, r, 16);
+  return o;
+}
+
 template <int DT, int NT, bool G13>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
   constexpr int MT = 16 * NT;
@@ -157,33 +174,45 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             for (int s = 0; s < NT; ++s)
               acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][c], B[s][c], acc[t][s], 0, 0, 0);
       } else if constexpr (DT == DT_MXFP8) {
-        i32x8_t A[4], B[NT];
-        int SA[4], SB[NT];
+        // e4m3 x 2^s is exact in bf16; the convert applies the power-of-two scale
+        uint4 AC[4][2];
+        uint32_t AS[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const uint8_t* p = a.wcodes + (tile0 + t) * tcode + lane * 32;
-          i32x4_t lo = *reinterpret_cast<const i32x4_t*>(p), hi = *reinterpret_cast<const i32x4_t*>(p + 16);
-          A[t] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          SA[t] = a.wscales[(tile0 + t) * tscale + lane];
+          AC[t][0] = *reinterpret_cast<const uint4*>(p);
+          AC[t][1] = *reinterpret_cast<const uint4*>(p + 16);
+          AS[t] = *reinterpret_cast<const uint32_t*>(a.wscales + (tile0 + t) * tscale + i16 * 4);
         }
+        uint2 BC[NT][4];
+        uint32_t BS[NT];
 #pragma unroll
         for (int s = 0; s < NT; ++s) {
           if (brow[s] >= 0) {
-            const uint8_t* p = a.act + (size_t)brow[s] * a.K + kg * 128 + 16 * q;
-            i32x4_t lo = *reinterpret_cast<const i32x4_t*>(p), hi = *reinterpret_cast<const i32x4_t*>(p + 64);
-            B[s] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            SB[s] = a.act_scales[(size_t)brow[s] * (a.K / 32) + kg * 4 + q];
+            const uint8_t* p = a.act + (size_t)brow[s] * a.K + kg * 128 + 8 * q;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) BC[s][c] = *reinterpret_cast<const uint2*>(p + 32 * c);
+            BS[s] = *reinterpret_cast<const uint32_t*>(a.act_scales + (size_t)brow[s] * (a.K / 32) + kg * 4);
           } else {
-            B[s] = i32x8_t{};
-            SB[s] = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) BC[s][c] = make_uint2(0, 0);
+            BS[s] = 0x7F7F7F7Fu;
           }
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int c = 0; c < 4; ++c) {
+          bf16x8_t B[NT];
 #pragma unroll
-          for (int s = 0; s < NT; ++s)
-            acc[t][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[t], B[s], acc[t][s], 0, 0, 0, SA[t], 0,
-                                                                         SB[s]);
+          for (int s = 0; s < NT; ++s) B[s] = mxfp8_dequant8(BC[s][c].x, BC[s][c].y, (BS[s] >> (8 * c)) & 0xFF);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint4 v = AC[t][c >> 1];
+            const bf16x8_t A = (c & 1) ? mxfp8_dequant8(v.z, v.w, (AS[t] >> (8 * c)) & 0xFF)
+                                       : mxfp8_dequant8(v.x, v.y, (AS[t] >> (8 * c)) & 0xFF);
+#pragma unroll
+            for (int s = 0; s < NT; ++s) acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[s], acc[t][s], 0, 0, 0);
+          }
+        }
       } else {  // NVFP4: e2m1 x e4m3 -> exact bf16, bf16 MFMA
         uint4 AC[4];
         uint2 AS[4];
@@ -354,10 +383,12 @@ __global__ void prepare_kernel(const uint8_t* __restrict__ src, const uint8_t* _
         *reinterpret_cast<uint4*>(dst + tile * 4096 + c * 1024 + lane * 16) =
             *reinterpret_cast<const uint4*>(src + (rb * K + kg * 128 + 32 * c + 8 * q) * 2);
     } else if constexpr (DT == DT_MXFP8) {
-      const uint8_t* s = src + rb * K + kg * 128 + 16 * q;
-      *reinterpret_cast<uint4*>(dst + tile * 2048 + lane * 32) = *reinterpret_cast<const uint4*>(s);
-      *reinterpret_cast<uint4*>(dst + tile * 2048 + lane * 32 + 16) = *reinterpret_cast<const uint4*>(s + 64);
-      dst_s[tile * 64 + lane] = src_s[rb * (K / 32) + kg * 4 + q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<uint2*>(dst + tile * 2048 + lane * 32 + 8 * c) =
+            *reinterpret_cast<const uint2*>(src + rb * K + kg * 128 + 32 * c + 8 * q);
+      // row i's 4 scales of this kgroup, one byte per lane
+      dst_s[tile * 64 + i * 4 + q] = src_s[rb * (K / 32) + kg * 4 + q];
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c)

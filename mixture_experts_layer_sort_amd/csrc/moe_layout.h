@@ -7,10 +7,10 @@
 // matrix instruction that consumes it (lane l = 16*q + i holds row i):
 //   BF16  (v_mfma_f32_16x16x32_bf16, 4 per kgroup): [chunk c<4][lane][8 bf16],
 //         lane (i,q) of chunk c holds k = 32c + 8q .. +8           (4096 B)
-//   MXFP8 (v_mfma_scale_f32_16x16x128_f8f6f4, fp8 operands): [lane][32 B],
-//         lane (i,q) holds k = 16q..16q+16 then 64+16q..64+16q+16;
-//         scale block q (k = 32q..32q+32) is lane (i,q)'s scale byte (2048 B
-//         codes + 64 B scales)
+//   MXFP8 (converted exactly to bf16 in registers, then bf16 MFMA):
+//         [lane][4 chunks x 8 B], lane (i,q) of chunk c holds k = 32c + 8q
+//         .. +8 (so every element of chunk c lies in scale block c);
+//         scales [row i][4 e8m0 bytes]                  (2048 B + 64 B)
 //   NVFP4 (dequantised to bf16 in registers, then bf16 MFMA):
 //         [lane][4 chunks x 4 B] of e2m1 nibbles, lane (i,q) of chunk c holds
 //         k = 32c + 8q .. +8; scales [row i][8 e4m3 bytes] in K order, lane
