@@ -1,0 +1,146 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times.  Inputs come from the seeded device generators; the library
+quantises all experts' fp32 master weights on the GPU.  The oracle checks:
+
+* routing (all tokens), the permutation (all pairs): bit-exact;
+* quantised activations: bit-exact on a sample of token rows;
+* for a few sampled tokens: the oracle quantises the fp32 masters of their
+  experts itself (codes must equal the library's bit for bit) and evaluates
+  the layer for those tokens; intermediate, expert outputs and the layer
+  output must meet the tolerance;
+* moe_forward equals the staged entry points bit for bit on every token.
+"""
+import concurrent.futures as cf
+import multiprocessing as mp
+import os
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as gh
+import moe_inputs as mi
+from oracle import moe as omoe
+from oracle import quant as oquant
+
+pytestmark = pytest.mark.gpu
+
+W = mi.WORKLOADS
+MAX_SAMPLE_EXPERTS = 16
+
+
+def _log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def pool():
+    n = min(16, os.cpu_count() or 4)
+    with cf.ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn")) as ex:
+        yield ex
+
+
+def _quantize_pair(args):
+    w13, w2, dtype = args
+    return oquant.quantize_weight(w13, dtype), oquant.quantize_weight(w2, dtype)
+
+
+def _pick_tokens(ids, k, limit):
+    """The first tokens (in a seeded order) whose experts stay within `limit`."""
+    order = np.random.default_rng(1234).permutation(ids.shape[0])
+    toks, experts = [], set()
+    for t in order:
+        nxt = experts | set(ids[t].tolist())
+        if toks and len(nxt) > limit:
+            continue
+        toks.append(int(t))
+        experts = nxt
+        if len(toks) >= 4:
+            break
+    return sorted(toks), sorted(experts)
+
+
+@pytest.mark.parametrize("name", ["tiny_bf16", "bf16_decode", "mxfp8_decode", "nvfp4_decode_t8",
+                                  "nvfp4_decode_t128", "mxfp8_prefill"])
+def test_fullsize_parity(name, pool):
+    w = W[name]
+    dev = gh.dev()
+    _log(f"{name}: building {w}")
+    cw = gh.alloc_canonical(w)
+    for e in range(w.E):
+        a, b = mi.device_master_weights(w, e, dev)
+        gh.quantize_expert(w, cw, e, a, b)
+    layer = gh.DeviceLayer(w, cw)
+    x = mi.device_x(w, dev)
+    logits = mi.device_logits(w, dev)
+    r = layer.staged(x, logits)
+    out_fwd = layer.forward(x, logits)
+    torch.cuda.synchronize()
+    _log(f"{name}: GPU done")
+
+    x_bits = gh.bf16_numpy(x)
+    l_host = logits.cpu().numpy()
+    # routing and permutation of every token / pair
+    rid, rw = omoe.route(l_host, w.k)
+    ids = r["ids"].cpu().numpy()
+    assert np.array_equal(ids, rid)
+    assert np.max(np.abs(r["wts"].cpu().numpy() - rw)) <= 1e-6
+    off, sp, pp = omoe.permute(rid, w.E)
+    assert np.array_equal(r["offsets"].cpu().numpy(), off)
+    assert np.array_equal(r["sorted_pairs"].cpu().numpy()[: w.P], sp)
+    assert np.array_equal(r["pair_pos"].cpu().numpy()[: w.P], pp)
+    _log(f"{name}: routing + permutation bit-exact; active experts {int(np.sum(np.diff(off) > 0))}")
+    # quantised activations on a sample of rows
+    rows = np.unique(np.random.default_rng(7).integers(0, w.T, min(w.T, 64)))
+    xc, xs, _ = omoe.quantize_x(x_bits[rows], w.dtype)
+    gc, gs = layer.xq_numpy(r, w.T)
+    assert np.array_equal(gc[rows], xc)
+    if xs is not None:
+        assert np.array_equal(gs[rows], xs)
+    # fused == staged on every token
+    assert np.array_equal(gh.bf16_numpy(out_fwd), gh.bf16_numpy(r["out"]))
+
+    # sampled tokens against the oracle, with the oracle's own weight quantisation
+    toks, experts = _pick_tokens(ids, w.k, MAX_SAMPLE_EXPERTS)
+    _log(f"{name}: oracle on tokens {toks} ({len(experts)} experts)")
+    masters = {}
+    for e in experts:
+        a, b = mi.device_master_weights(w, e, dev)
+        masters[e] = (a.cpu().numpy(), b.cpu().numpy())
+    results = list(pool.map(_quantize_pair, [(masters[e][0], masters[e][1], w.dtype) for e in experts]))
+    del masters
+    got = gh.canonical_to_numpy(cw, experts)
+    ow = {n: {} for n in ("w13", "w13_s", "w13_a", "w2", "w2_s", "w2_a")}
+    for e, ((c13, s13, a13), (c2, s2, a2)) in zip(experts, results):
+        ow["w13"][e], ow["w13_s"][e], ow["w13_a"][e] = c13, s13, a13
+        ow["w2"][e], ow["w2_s"][e], ow["w2_a"][e] = c2, s2, a2
+        assert np.array_equal(np.asarray(got["w13"][e]), c13), e
+        assert np.array_equal(np.asarray(got["w2"][e]), c2), e
+        if s13 is not None:
+            assert np.array_equal(got["w13_s"][e], s13) and np.array_equal(got["w2_s"][e], s2), e
+        if a13 is not None:
+            assert float(got["w13_a"][e]) == float(a13) and float(got["w2_a"][e]) == float(a2), e
+    _log(f"{name}: library weight codes of {len(experts)} experts equal the oracle's")
+    if w.dtype == "bf16":
+        Wo = omoe.Weights("bf16", ow["w13"], ow["w2"])
+    elif w.dtype == "mxfp8":
+        Wo = omoe.Weights("mxfp8", ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"])
+    else:
+        Wo = omoe.Weights("nvfp4", ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"], ow["w13_a"], ow["w2_a"])
+    ref = omoe.moe_layer(x_bits, l_host, Wo, w.k, tokens=toks, keep=True)
+    hc, hs = layer.hq_numpy(r, w.T)
+    y = gh.bf16_numpy(r["y"])
+    tol = gh.out_tolerance(w.dtype)
+    for t in toks:
+        for j in range(w.k):
+            p = t * w.k + j
+            row = int(pp[p])
+            h_got = oquant.dequantize_act(hc[row:row + 1], None if hs is None else hs[row:row + 1], w.dtype)[0]
+            assert gh.rel_l2(h_got, ref.h[(t, j)][2]) <= tol, (t, j)
+            y_got = (y[p].astype(np.uint32) << 16).view(np.float32)
+            assert gh.rel_l2(y_got, ref.y[(t, j)]) <= tol, (t, j)
+    rel, mad = gh.check_out(gh.bf16_numpy(r["out"])[toks], ref.out, w.dtype, name)
+    _log(f"{name}: sampled tokens out relL2 {rel:.2e} max|d|/rms {mad:.2e}")
+    del layer, cw, r, out_fwd
+    torch.cuda.empty_cache()
