@@ -91,17 +91,22 @@ MOE_API size_t moe_packed_weight_bytes(const moe_shape* shape);
 /* Workspace of moe_forward for any T <= max_tokens. */
 MOE_API size_t moe_workspace_bytes(const moe_shape* shape);
 /* Quantised activations of T tokens (moe_permute's xq): codes [T, H*b] at
- * offset 0, then scales [T, H/blk] at moe_xq_scale_offset(shape, T).
- *   BF16: bf16 [T, H], no scales;  MXFP8: u8 [T, H] + e8m0 [T, H/32];
- *   NVFP4: packed e2m1 [T, H/2] + e4m3 [T, H/16]. */
+ * offset 0, then scales [T, H/blk] at moe_xq_scale_offset(shape, T), then
+ * (MXFP8, NVFP4) the exact dequantised values [T, H] as bf16 (MXFP8) or
+ * fp16 (NVFP4) at moe_xq_dequant_offset(shape, T) — the operand the grouped
+ * GEMM reads, produced once per token instead of once per expert tile.
+ *   BF16: bf16 [T, H], no scales;  MXFP8: u8 [T, H] + e8m0 [T, H/32] + bf16;
+ *   NVFP4: packed e2m1 [T, H/2] + e4m3 [T, H/16] + fp16. */
 MOE_API size_t moe_xq_bytes(const moe_shape* shape, int32_t T);
 MOE_API size_t moe_xq_scale_offset(const moe_shape* shape, int32_t T);
+MOE_API size_t moe_xq_dequant_offset(const moe_shape* shape, int32_t T);
 /* Requantised intermediate of the T*k pairs in expert-sorted order
  * (moe_gemm13_swiglu_quant's hq), same scheme along I:
- *   BF16: bf16 [P, I];  MXFP8: u8 [P, I] + e8m0 [P, I/32];
- *   NVFP4: packed e2m1 [P, I/2] + e4m3 [P, I/16]  (P = T * k). */
+ *   BF16: bf16 [P, I];  MXFP8: u8 [P, I] + e8m0 [P, I/32] + bf16 [P, I];
+ *   NVFP4: packed e2m1 [P, I/2] + e4m3 [P, I/16] + fp16 [P, I]  (P = T * k). */
 MOE_API size_t moe_hq_bytes(const moe_shape* shape, int32_t T);
 MOE_API size_t moe_hq_scale_offset(const moe_shape* shape, int32_t T);
+MOE_API size_t moe_hq_dequant_offset(const moe_shape* shape, int32_t T);
 
 /* Quantise fp32 master weights of `count` stacked matrices [count, rows, K]
  * into the canonical format of `dtype` (the load-time preprocessing step the

@@ -26,8 +26,10 @@ EXPORTED = [
     "moe_workspace_bytes",
     "moe_xq_bytes",
     "moe_xq_scale_offset",
+    "moe_xq_dequant_offset",
     "moe_hq_bytes",
     "moe_hq_scale_offset",
+    "moe_hq_dequant_offset",
     "moe_quantize_weights",
     "moe_prepare_weights",
     "moe_route",
@@ -77,6 +79,8 @@ def _load():
         "moe_xq_scale_offset": (SZ, [S, I32]),
         "moe_hq_bytes": (SZ, [S, I32]),
         "moe_hq_scale_offset": (SZ, [S, I32]),
+        "moe_xq_dequant_offset": (SZ, [S, I32]),
+        "moe_hq_dequant_offset": (SZ, [S, I32]),
         "moe_quantize_weights": (I32, [I32, I32, I32, I32, P, P, P, P, P]),
         "moe_prepare_weights": (I32, [S, P, P, P, P, P, P, P, SZ, P]),
         "moe_route": (I32, [S, I32, P, P, P, P]),
@@ -169,6 +173,14 @@ def moe_hq_bytes(shape: moe_shape, T: int) -> int:
 
 def moe_hq_scale_offset(shape: moe_shape, T: int) -> int:
     return _lib.moe_hq_scale_offset(ctypes.byref(shape), T)
+
+
+def moe_xq_dequant_offset(shape: moe_shape, T: int) -> int:
+    return _lib.moe_xq_dequant_offset(ctypes.byref(shape), T)
+
+
+def moe_hq_dequant_offset(shape: moe_shape, T: int) -> int:
+    return _lib.moe_hq_dequant_offset(ctypes.byref(shape), T)
 
 
 # ----------------------------------------------------------------- entry points

@@ -102,6 +102,16 @@ size_t moe_xq_scale_offset(const moe_shape* s, int32_t T) {
   return act_scale_offset(s->dtype, T, s->hidden);
 }
 
+size_t moe_xq_dequant_offset(const moe_shape* s, int32_t T) {
+  if (check_T(s, T) != MOE_OK) return 0;
+  return act_dequant_offset(s->dtype, T, s->hidden);
+}
+
+size_t moe_hq_dequant_offset(const moe_shape* s, int32_t T) {
+  if (check_T(s, T) != MOE_OK) return 0;
+  return act_dequant_offset(s->dtype, T * s->top_k, s->inter);
+}
+
 size_t moe_hq_bytes(const moe_shape* s, int32_t T) {
   if (check_T(s, T) != MOE_OK) return 0;
   return act_bytes(s->dtype, T * s->top_k, s->inter);

@@ -28,10 +28,10 @@ struct GemmArgs {
   const float* walpha;
   const int* offsets;
   const int* sorted_pairs;
-  const uint8_t* act;         // B operand rows: xq (gemm13, row = token) or hq (gemm2, row = sorted row)
-  const uint8_t* act_scales;
+  const uint8_t* act;         // B operand rows, 16-bit: xq (gemm13, row = token) or hq (gemm2, row = sorted row)
   uint8_t* out;               // hq codes (gemm13) or y (gemm2)
   uint8_t* out_scales;        // hq scales (gemm13)
+  uint16_t* out_deq;          // hq dequantised 16-bit copy (gemm13; MXFP8, NVFP4)
   int E, K, G, KG, k, n_out;
 };
 
@@ -85,24 +85,21 @@ __device__ __forceinline__ int find_expert(const int* cum, int E, int mtg) {
 
 __device__ __forceinline__ bf16x8_t load_bf16x8(const uint8_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
-// 8 e2m1 codes (one dword, element j in nibble j) times an exact e4m3 scale
-// -> 8 bf16 (exact: <= 6 significant bits).  The hardware convert is used at
-// scale 1.0 (pure conversion); the scale multiply is an fp32 multiply.
-__device__ __forceinline__ bf16x8_t nvfp4_dequant8(uint32_t codes, float sc) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  f32x2 f[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0),
-                __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1),
-                __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2),
-                __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3)};
-  uint32_t o[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    float lo = f[b][0] * sc, hi = f[b][1] * sc;
-    o[b] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-  }
-  bf16x8_t r;
-  __builtin_memcpy(&r, o, 16);
-  return r;
+// 8 e2m1 codes (one dword, element j in nibble j) times an e4m3 scale (one
+// byte) -> 8 fp16, exactly: e2m1 (2 significant bits) x e4m3 (4 bits) fits
+// fp16's 11 bits and its exponent range.  Hardware converts at scale 1 (pure
+// conversion) and one packed fp16 multiply per pair.
+__device__ __forceinline__ f16x8_t nvfp4_dequant8(uint32_t codes, uint32_t e4m3_byte) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 sc = __builtin_amdgcn_cvt_scalef32_f16_fp8(f16x2{}, e4m3_byte, 1.0f, 0, false);
+  sc[1] = sc[0];
+  f16x2 r[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sc,
+                __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * sc,
+                __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * sc,
+                __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * sc};
+  f16x8_t o;
+  __builtin_memcpy(&o, r, 16);
+  return o;
 }
 
 // 8 e4m3 codes (two dwords, element j in byte j) times 2^(e - 127) (an e8m0
@@ -122,9 +119,133 @@ __device__ __forceinline__ bf16x8_t mxfp8_dequant8(uint32_t lo, uint32_t hi, uin
   return o;
 }
 
+// ------------------------------------------------------------------ K-slice fragments
+// Raw bytes of one 128-wide K slice ("kgroup") for the 4 weight tiles of a
+// work item and its NT token sub-tiles, as loaded from memory; converted and
+// fed to the matrix unit by mma_kfrag.
+template <int DT>
+struct KW {  // words per lane per tile: codes (uint4) / scales (dwords)
+  static constexpr int A = DT == DT_BF16 ? 4 : (DT == DT_MXFP8 ? 2 : 1);
+  static constexpr int AS = DT == DT_NVFP4 ? 2 : 1;
+};
+
+template <int DT, int NT>
+struct KFrag {
+  uint4 ac[4][KW<DT>::A];
+  uint32_t as[4][KW<DT>::AS];
+  uint4 bc[NT][4];  // 16-bit activation operand, 4 chunks of 8
+};
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool NTLD>
+__device__ __forceinline__ uint4 ld_w16(const uint8_t* p) {
+  if constexpr (NTLD) {
+    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+
+template <int DT, int NT, bool G13, bool NTLD>
+__device__ __forceinline__ void load_kfrag(KFrag<DT, NT>& f, const GemmArgs& a, size_t tile0, int kg,
+                                           const int (&brow)[NT], int lane, int i16, int q) {
+  const size_t tcode = tile_code_bytes(DT), tscale = tile_scale_bytes(DT);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint8_t* pc = a.wcodes + (tile0 + t) * tcode;
+    if constexpr (DT == DT_BF16) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) f.ac[t][c] = ld_w16<NTLD>(pc + c * 1024 + lane * 16);
+    } else if constexpr (DT == DT_MXFP8) {
+      f.ac[t][0] = ld_w16<NTLD>(pc + lane * 16);
+      f.ac[t][1] = ld_w16<NTLD>(pc + 1024 + lane * 16);
+      f.as[t][0] = *reinterpret_cast<const uint32_t*>(a.wscales + (tile0 + t) * tscale + i16 * 4);
+    } else {
+      f.ac[t][0] = ld_w16<NTLD>(pc + lane * 16);
+      const uint2 sv = *reinterpret_cast<const uint2*>(a.wscales + (tile0 + t) * tscale + i16 * 8);
+      f.as[t][0] = sv.x;
+      f.as[t][1] = sv.y;
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < NT; ++s) {
+    const bool ok = brow[s] >= 0;
+    const uint8_t* p = a.act + ((size_t)(ok ? brow[s] : 0) * a.K + kg * 128 + 8 * q) * 2;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) f.bc[s][c] = ok ? *reinterpret_cast<const uint4*>(p + c * 64) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+template <int DT, int NT>
+__device__ __forceinline__ void mma_kfrag(f32x4_t (&acc)[4][NT], const KFrag<DT, NT>& f, int q) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (DT == DT_NVFP4) {
+        const int sb = 2 * c + (q >> 1);  // 16-block of this lane's 8 k's
+        const uint32_t sw = sb < 4 ? f.as[t][0] : f.as[t][1];
+        const f16x8_t A = nvfp4_dequant8(u4_word(f.ac[t][0], c), (sw >> (8 * (sb & 3))) & 0xFF);
+#pragma unroll
+        for (int s = 0; s < NT; ++s) {
+          f16x8_t B;
+          __builtin_memcpy(&B, &f.bc[s][c], 16);
+          acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[t][s], 0, 0, 0);
+        }
+      } else {
+        bf16x8_t A;
+        if constexpr (DT == DT_BF16) {
+          __builtin_memcpy(&A, &f.ac[t][c], 16);
+        } else {
+          const uint4& v = f.ac[t][c >> 1];
+          A = (c & 1) ? mxfp8_dequant8(v.z, v.w, (f.as[t][0] >> (8 * c)) & 0xFF)
+                      : mxfp8_dequant8(v.x, v.y, (f.as[t][0] >> (8 * c)) & 0xFF);
+        }
+#pragma unroll
+        for (int s = 0; s < NT; ++s) {
+          bf16x8_t B;
+          __builtin_memcpy(&B, &f.bc[s][c], 16);
+          acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t][s], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Compile-time tuning knobs of the grouped GEMMs.
+#ifndef MOE_GEMM_PIPELINE  // 1: double-buffer K steps (prefetch the next while computing)
+#define MOE_GEMM_PIPELINE 1
+#endif
+#ifndef MOE_GEMM_NTLOAD  // 1: non-temporal weight loads on the decode path
+#define MOE_GEMM_NTLOAD 1
+#endif
+#ifndef MOE_GEMM_U_BF16  // kgroups per step, per weight format
+#define MOE_GEMM_U_BF16 1
+#endif
+#ifndef MOE_GEMM_U_MXFP8
+#define MOE_GEMM_U_MXFP8 1
+#endif
+#ifndef MOE_GEMM_U_NVFP4
+#define MOE_GEMM_U_NVFP4 1
+#endif
+
+// kgroups per pipeline step: enough bytes in flight per wave for each format
+template <int DT>
+struct StepK {
+  static constexpr int U = DT == DT_BF16 ? MOE_GEMM_U_BF16 : (DT == DT_MXFP8 ? MOE_GEMM_U_MXFP8 : MOE_GEMM_U_NVFP4);
+};
+
 template <int DT, int NT, bool G13>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
   constexpr int MT = 16 * NT;
+  constexpr int U = StepK<DT>::U;
+  constexpr bool NTLD = MOE_GEMM_NTLOAD && NT == 1;  // decode: weights are streamed once
   __shared__ int cum[1025];
   __shared__ int wsum[4];
   __shared__ f32x4_t red[3][4 * NT][64];
@@ -133,8 +254,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
   const int i16 = lane & 15, q = lane >> 4;
   const int total_mt = build_schedule(a.offsets, a.E, MT, cum, wsum);
   const long long total = (long long)total_mt * a.G;
-  const int kg_begin = (wv * a.KG) / 4, kg_end = ((wv + 1) * a.KG) / 4;
-  const size_t tcode = tile_code_bytes(DT), tscale = tile_scale_bytes(DT);
+  // K slices are dealt to the 4 waves in rounds of 4U consecutive kgroups
+  // (wave w takes kgroups 4U*j + U*w .. +U), so a block streams one
+  // contiguous region; steps are double-buffered.
+  const int nrounds = (a.KG + 4 * U - 1) / (4 * U);
 
   for (long long w = blockIdx.x; w < total; w += gridDim.x) {
     const int mtg = (int)(w / a.G), g = (int)(w % a.G);
@@ -152,113 +275,40 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int s = 0; s < NT; ++s) acc[t][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int kg = kg_begin; kg < kg_end; ++kg) {
-      const size_t tile0 = ((size_t)(e * a.G + g) * a.KG + kg) * 4;
-      if constexpr (DT == DT_BF16) {
-        bf16x8_t A[4][4], B[NT][4];
+    const size_t tbase = (size_t)(e * a.G + g) * a.KG;
+    KFrag<DT, NT> F0[U], F1[U];
+    auto load_step = [&](KFrag<DT, NT>(&F)[U], int j) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+      for (int u = 0; u < U; ++u) {
+        const int kg = 4 * U * j + U * wv + u;
+        if (kg < a.KG) load_kfrag<DT, NT, G13, NTLD>(F[u], a, (tbase + kg) * 4, kg, brow, lane, i16, q);
+      }
+    };
+    auto mma_step = [&](const KFrag<DT, NT>(&F)[U], int j) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) A[t][c] = load_bf16x8(a.wcodes + (tile0 + t) * tcode + c * 1024 + lane * 16);
-#pragma unroll
-        for (int s = 0; s < NT; ++s)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            B[s][c] = brow[s] >= 0 ? load_bf16x8(a.act + ((size_t)brow[s] * a.K + kg * 128 + c * 32 + 8 * q) * 2)
-                                   : bf16x8_t{};
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int s = 0; s < NT; ++s)
-              acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][c], B[s][c], acc[t][s], 0, 0, 0);
-      } else if constexpr (DT == DT_MXFP8) {
-        // e4m3 x 2^s is exact in bf16; the convert applies the power-of-two scale
-        uint4 AC[4][2];
-        uint32_t AS[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint8_t* p = a.wcodes + (tile0 + t) * tcode + lane * 32;
-          AC[t][0] = *reinterpret_cast<const uint4*>(p);
-          AC[t][1] = *reinterpret_cast<const uint4*>(p + 16);
-          AS[t] = *reinterpret_cast<const uint32_t*>(a.wscales + (tile0 + t) * tscale + i16 * 4);
+      for (int u = 0; u < U; ++u) {
+        const int kg = 4 * U * j + U * wv + u;
+        if (kg < a.KG) mma_kfrag<DT, NT>(acc, F[u], q);
+      }
+    };
+    if constexpr (MOE_GEMM_PIPELINE) {
+      load_step(F0, 0);
+      for (int j = 0; j < nrounds; j += 2) {
+        if (j + 1 < nrounds) load_step(F1, j + 1);
+        mma_step(F0, j);
+        if (j + 1 < nrounds) {
+          if (j + 2 < nrounds) load_step(F0, j + 2);
+          mma_step(F1, j + 1);
         }
-        uint2 BC[NT][4];
-        uint32_t BS[NT];
-#pragma unroll
-        for (int s = 0; s < NT; ++s) {
-          if (brow[s] >= 0) {
-            const uint8_t* p = a.act + (size_t)brow[s] * a.K + kg * 128 + 8 * q;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) BC[s][c] = *reinterpret_cast<const uint2*>(p + 32 * c);
-            BS[s] = *reinterpret_cast<const uint32_t*>(a.act_scales + (size_t)brow[s] * (a.K / 32) + kg * 4);
-          } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) BC[s][c] = make_uint2(0, 0);
-            BS[s] = 0x7F7F7F7Fu;
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          bf16x8_t B[NT];
-#pragma unroll
-          for (int s = 0; s < NT; ++s) B[s] = mxfp8_dequant8(BC[s][c].x, BC[s][c].y, (BS[s] >> (8 * c)) & 0xFF);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint4 v = AC[t][c >> 1];
-            const bf16x8_t A = (c & 1) ? mxfp8_dequant8(v.z, v.w, (AS[t] >> (8 * c)) & 0xFF)
-                                       : mxfp8_dequant8(v.x, v.y, (AS[t] >> (8 * c)) & 0xFF);
-#pragma unroll
-            for (int s = 0; s < NT; ++s) acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[s], acc[t][s], 0, 0, 0);
-          }
-        }
-      } else {  // NVFP4: e2m1 x e4m3 -> exact bf16, bf16 MFMA
-        uint4 AC[4];
-        uint2 AS[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          AC[t] = *reinterpret_cast<const uint4*>(a.wcodes + (tile0 + t) * tcode + lane * 16);
-          AS[t] = *reinterpret_cast<const uint2*>(a.wscales + (tile0 + t) * tscale + i16 * 8);
-        }
-        uint32_t BC[NT][4];
-        uint2 BS[NT];
-#pragma unroll
-        for (int s = 0; s < NT; ++s) {
-          if (brow[s] >= 0) {
-            const uint8_t* p = a.act + (size_t)brow[s] * (a.K / 2) + kg * 64 + 4 * q;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) BC[s][c] = *reinterpret_cast<const uint32_t*>(p + 16 * c);
-            BS[s] = *reinterpret_cast<const uint2*>(a.act_scales + (size_t)brow[s] * (a.K / 16) + kg * 8);
-          } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) BC[s][c] = 0;
-            BS[s] = make_uint2(0, 0);
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          // scale byte of 16-block 2c + q/2 within this kgroup (bytes 0..3 in .x, 4..7 in .y)
-          const int sb = 2 * c + (q >> 1);
-          bf16x8_t B[NT];
-#pragma unroll
-          for (int s = 0; s < NT; ++s) {
-            uint32_t word = sb < 4 ? BS[s].x : BS[s].y;
-            B[s] = nvfp4_dequant8(BC[s][c], e4m3_to_f32((word >> (8 * (sb & 3))) & 0xFF));
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t cw = c == 0 ? AC[t].x : (c == 1 ? AC[t].y : (c == 2 ? AC[t].z : AC[t].w));
-            const uint32_t sw = sb < 4 ? AS[t].x : AS[t].y;
-            bf16x8_t A = nvfp4_dequant8(cw, e4m3_to_f32((sw >> (8 * (sb & 3))) & 0xFF));
-#pragma unroll
-            for (int s = 0; s < NT; ++s) acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[s], acc[t][s], 0, 0, 0);
-          }
-        }
+      }
+    } else {
+      for (int j = 0; j < nrounds; ++j) {
+        load_step(F0, j);
+        mma_step(F0, j);
       }
     }
 
-    // reduce the four K quarters into wave 0
+    // reduce the four waves' partial sums into wave 0
     if (wv > 0) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -309,12 +359,18 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             const int sx = mx_scale_exp(amax);
             if (ok) {
               uint8_t* o = a.out + (size_t)r * I + 32 * g + 4 * q;
+              uint16_t* od = a.out_deq + (size_t)r * I + 32 * g + 4 * q;
 #pragma unroll
               for (int tp = 0; tp < 2; ++tp) {
-                uint32_t v = 0;
+                uint32_t v = 0, d[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v |= e4m3_from_f32(ldexpf(h[tp][j], -sx)) << (8 * j);
+                for (int j = 0; j < 4; ++j) {
+                  const uint32_t c = e4m3_from_f32(ldexpf(h[tp][j], -sx));
+                  v |= c << (8 * j);
+                  d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), sx)) >> 16;  // exact in bf16
+                }
                 *reinterpret_cast<uint32_t*>(o + 16 * tp) = v;
+                *reinterpret_cast<uint2*>(od + 16 * tp) = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
               }
               if (q == 0) a.out_scales[(size_t)r * (I / 32) + g] = (uint8_t)(sx + 127);
             }
@@ -326,15 +382,18 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
               amax = wave_max_xor(amax, 16, 32);
               const uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
               const float sc = e4m3_to_f32(sc_code);
-              uint32_t v = 0;
+              uint32_t v = 0, d[4];
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 uint32_t c = sc > 0.f ? e2m1_from_f32(h[tp][j], sc) : ((__float_as_uint(h[tp][j]) >> 28) & 8u);
                 v |= c << (4 * j);
+                d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
               }
               if (ok) {
                 *reinterpret_cast<uint16_t*>(a.out + (size_t)r * (I / 2) + 16 * g + 8 * tp + 2 * q) = (uint16_t)v;
                 if (q == 0) a.out_scales[(size_t)r * (I / 16) + 2 * g + tp] = (uint8_t)sc_code;
+                *reinterpret_cast<uint2*>(a.out_deq + (size_t)r * I + 32 * g + 16 * tp + 4 * q) =
+                    make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
               }
             }
           }
@@ -384,8 +443,8 @@ __global__ void prepare_kernel(const uint8_t* __restrict__ src, const uint8_t* _
             *reinterpret_cast<const uint4*>(src + (rb * K + kg * 128 + 32 * c + 8 * q) * 2);
     } else if constexpr (DT == DT_MXFP8) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint2*>(dst + tile * 2048 + lane * 32 + 8 * c) =
+      for (int c = 0; c < 4; ++c)  // half c/2, bytes 8*(c%2) of the lane's 16
+        *reinterpret_cast<uint2*>(dst + tile * 2048 + (c >> 1) * 1024 + lane * 16 + 8 * (c & 1)) =
             *reinterpret_cast<const uint2*>(src + rb * K + kg * 128 + 32 * c + 8 * q);
       // row i's 4 scales of this kgroup, one byte per lane
       dst_s[tile * 64 + i * 4 + q] = src_s[rb * (K / 32) + kg * 4 + q];
@@ -476,10 +535,10 @@ hipError_t launch_gemm13(int dt, int E, int H, int I, int k, int T, const uint8_
   a.walpha = reinterpret_cast<const float*>(packed + L.w13_alpha);
   a.offsets = offsets;
   a.sorted_pairs = sorted_pairs;
-  a.act = xq;
-  a.act_scales = xq + act_scale_offset(dt, T, H);
+  a.act = xq + act_operand_offset(dt, T, H);
   a.out = hq;
   a.out_scales = hq + act_scale_offset(dt, T * k, I);
+  a.out_deq = reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
   a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
   return dispatch_gemm<true>(dt, choose_nt(T, k, E), a, grid, s);
 }
@@ -493,10 +552,10 @@ hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t
   a.walpha = reinterpret_cast<const float*>(packed + L.w2_alpha);
   a.offsets = offsets;
   a.sorted_pairs = sorted_pairs;
-  a.act = hq;
-  a.act_scales = hq + act_scale_offset(dt, T * k, I);
+  a.act = hq + act_operand_offset(dt, T * k, I);
   a.out = reinterpret_cast<uint8_t*>(y);
   a.out_scales = nullptr;
+  a.out_deq = nullptr;
   a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
   return dispatch_gemm<false>(dt, choose_nt(T, k, E), a, grid, s);
 }

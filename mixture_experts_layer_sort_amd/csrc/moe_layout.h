@@ -8,10 +8,11 @@
 //   BF16  (v_mfma_f32_16x16x32_bf16, 4 per kgroup): [chunk c<4][lane][8 bf16],
 //         lane (i,q) of chunk c holds k = 32c + 8q .. +8           (4096 B)
 //   MXFP8 (converted exactly to bf16 in registers, then bf16 MFMA):
-//         [lane][4 chunks x 8 B], lane (i,q) of chunk c holds k = 32c + 8q
-//         .. +8 (so every element of chunk c lies in scale block c);
+//         [half h<2][lane][2 chunks x 8 B], lane (i,q) of chunk c = 2h + j
+//         holds k = 32c + 8q .. +8 (so every element of chunk c lies in scale
+//         block c); each half is one contiguous 1 KB wave load;
 //         scales [row i][4 e8m0 bytes]                  (2048 B + 64 B)
-//   NVFP4 (dequantised to bf16 in registers, then bf16 MFMA):
+//   NVFP4 (dequantised exactly to fp16 in registers, then fp16 MFMA):
 //         [lane][4 chunks x 4 B] of e2m1 nibbles, lane (i,q) of chunk c holds
 //         k = 32c + 8q .. +8; scales [row i][8 e4m3 bytes] in K order, lane
 //         (i,q) of chunk c uses byte 2c + q/2            (1024 B + 128 B)
@@ -74,11 +75,18 @@ MOE_HD PackedLayout packed_layout(int dt, int E, int H, int I) {
 }
 
 // Quantised activation rows (xq: rows = tokens, K = H; hq: rows = pairs, K = I):
-// codes [rows, row_code_bytes] at 0, scales [rows, row_scale_bytes] after.
+// codes [rows, row_code_bytes] at 0, scales [rows, row_scale_bytes] after,
+// then (MXFP8, NVFP4) the exact dequantised values as 16-bit floats [rows, K]
+// (bf16 for MXFP8, fp16 for NVFP4), the matrix-unit operand of the next GEMM.
 MOE_HD size_t act_scale_offset(int dt, int rows, int K) { return align256((size_t)rows * row_code_bytes(dt, K)); }
-MOE_HD size_t act_bytes(int dt, int rows, int K) {
+MOE_HD size_t act_dequant_offset(int dt, int rows, int K) {
   return act_scale_offset(dt, rows, K) + align256((size_t)rows * row_scale_bytes(dt, K));
 }
+MOE_HD size_t act_bytes(int dt, int rows, int K) {
+  return act_dequant_offset(dt, rows, K) + (dt == DT_BF16 ? 0 : align256((size_t)rows * K * 2));
+}
+// 16-bit operand rows of an activation buffer: the codes for BF16, else the dequantised copy
+MOE_HD size_t act_operand_offset(int dt, int rows, int K) { return dt == DT_BF16 ? 0 : act_dequant_offset(dt, rows, K); }
 
 // moe_forward workspace, sized for max_tokens.
 struct WorkspaceLayout {

@@ -142,7 +142,8 @@ __device__ void permute_block(const int* __restrict__ ids, int P, int E, int* __
 
 template <int DT>
 __device__ void quantize_x_blocks(const uint16_t* __restrict__ x, long long n_elem, uint8_t* __restrict__ codes,
-                                  uint8_t* __restrict__ scales, long long gtid, long long gstride) {
+                                  uint8_t* __restrict__ scales, uint16_t* __restrict__ deq, long long gtid,
+                                  long long gstride) {
   if constexpr (DT == DT_BF16) {
     // copy 8 bf16 per thread
     const uint4* src = reinterpret_cast<const uint4*>(x);
@@ -163,25 +164,32 @@ __device__ void quantize_x_blocks(const uint16_t* __restrict__ x, long long n_el
       const long long blk = i / LPB;
       if constexpr (DT == DT_MXFP8) {
         int s = mx_scale_exp(amax);
-        uint32_t out = 0;
+        uint32_t out = 0, d[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out |= e4m3_from_f32(ldexpf(v[j], -s)) << (8 * j);
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t c = e4m3_from_f32(ldexpf(v[j], -s));
+          out |= c << (8 * j);
+          d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), s)) >> 16;  // exact in bf16
+        }
         if (ok) {
           reinterpret_cast<uint32_t*>(codes)[i] = out;
           if (sub == 0) scales[blk] = (uint8_t)(s + 127);
+          reinterpret_cast<uint2*>(deq)[i] = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
         }
       } else {
         uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
         float sc = e4m3_to_f32(sc_code);
-        uint32_t out = 0;
+        uint32_t out = 0, d[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           uint32_t c = sc > 0.f ? e2m1_from_f32(v[j], sc) : ((__float_as_uint(v[j]) >> 28) & 8u);
           out |= c << (4 * j);
+          d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
         }
         if (ok) {
           reinterpret_cast<uint16_t*>(codes)[i] = (uint16_t)out;
           if (sub == 0) scales[blk] = (uint8_t)sc_code;
+          reinterpret_cast<uint2*>(deq)[i] = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
         }
       }
     }
@@ -195,7 +203,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_quant_kernel(const int* 
                                                                      int* __restrict__ pair_pos,
                                                                      const uint16_t* __restrict__ x, long long n_elem,
                                                                      uint8_t* __restrict__ xq_codes,
-                                                                     uint8_t* __restrict__ xq_scales, int do_quant) {
+                                                                     uint8_t* __restrict__ xq_scales,
+                                                                     uint16_t* __restrict__ xq_deq, int do_quant) {
   if (blockIdx.x == 0) {
     permute_block(ids, P, E, offsets, sorted_pairs, pair_pos);
     return;
@@ -203,7 +212,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_quant_kernel(const int* 
   if (!do_quant) return;
   const long long gtid = (long long)(blockIdx.x - 1) * kPermThreads + threadIdx.x;
   const long long gstride = (long long)(gridDim.x - 1) * kPermThreads;
-  quantize_x_blocks<DT>(x, n_elem, xq_codes, xq_scales, gtid, gstride);
+  quantize_x_blocks<DT>(x, n_elem, xq_codes, xq_scales, xq_deq, gtid, gstride);
 }
 
 // ------------------------------------------------------------------ weight quantisation
@@ -307,20 +316,21 @@ hipError_t launch_permute(int dt, const int* ids, int T, int k, int E, int H, in
   const long long n_elem = (long long)T * H;
   const int do_quant = !(dt == DT_BF16 && (const void*)xq == (const void*)x);
   uint8_t* xq_scales = xq + act_scale_offset(dt, T, H);
+  uint16_t* xq_deq = reinterpret_cast<uint16_t*>(xq + act_dequant_offset(dt, T, H));
   long long work = dt == DT_BF16 ? n_elem / 8 : n_elem / 4;
   int qblocks = do_quant ? (int)min((work + kPermThreads - 1) / kPermThreads, (long long)4096) : 0;
   switch (dt) {
     case DT_BF16:
       hipLaunchKernelGGL(permute_quant_kernel<DT_BF16>, dim3(1 + qblocks), dim3(kPermThreads), 0, s, ids, P, E,
-                         offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, do_quant);
+                         offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, xq_deq, do_quant);
       break;
     case DT_MXFP8:
       hipLaunchKernelGGL(permute_quant_kernel<DT_MXFP8>, dim3(1 + qblocks), dim3(kPermThreads), 0, s, ids, P, E,
-                         offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, do_quant);
+                         offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, xq_deq, do_quant);
       break;
     default:
       hipLaunchKernelGGL(permute_quant_kernel<DT_NVFP4>, dim3(1 + qblocks), dim3(kPermThreads), 0, s, ids, P, E,
-                         offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, do_quant);
+                         offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, xq_deq, do_quant);
       break;
   }
   return hipGetLastError();

@@ -155,6 +155,20 @@ class DeviceLayer:
     def hq_numpy(self, r, T):
         return self.split_act(r["hq"], T * self.w.k, self.w.I, lib.moe_hq_scale_offset(self.shape, T))
 
+    def dequant_numpy(self, buf: torch.Tensor, rows: int, K: int, off: int) -> np.ndarray:
+        """The 16-bit dequantised copy of an MXFP8 (bf16) / NVFP4 (fp16) activation
+        buffer, widened to float64."""
+        a = buf[off: off + rows * K * 2].cpu().numpy().view(np.uint16).reshape(rows, K)
+        if self.w.dtype == "mxfp8":
+            return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return a.view(np.float16).astype(np.float64)
+
+    def xq_dequant(self, r, T):
+        return self.dequant_numpy(r["xq"], T, self.w.H, lib.moe_xq_dequant_offset(self.shape, T))
+
+    def hq_dequant(self, r, T):
+        return self.dequant_numpy(r["hq"], T * self.w.k, self.w.I, lib.moe_hq_dequant_offset(self.shape, T))
+
 
 def bf16_numpy(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

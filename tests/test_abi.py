@@ -64,7 +64,9 @@ def test_sizes_match_layouts():
     T = 37
     s = S(512, 256, 8, 4, 64, "mxfp8")
     assert lib.moe_xq_scale_offset(s, T) == ((T * 512 + 255) // 256) * 256
-    assert lib.moe_xq_bytes(s, T) == lib.moe_xq_scale_offset(s, T) + ((T * 16 + 255) // 256) * 256
+    dq = lib.moe_xq_scale_offset(s, T) + ((T * 16 + 255) // 256) * 256
+    assert lib.moe_xq_dequant_offset(s, T) == dq
+    assert lib.moe_xq_bytes(s, T) == dq + ((T * 512 * 2 + 255) // 256) * 256
     assert lib.moe_hq_scale_offset(s, T) == ((T * 4 * 256 + 255) // 256) * 256
     s = S(512, 256, 8, 4, 64, "nvfp4")
     assert lib.moe_xq_scale_offset(s, T) == ((T * 256 + 255) // 256) * 256

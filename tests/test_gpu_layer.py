@@ -70,14 +70,18 @@ def test_layer_parity_small(name):
     assert np.array_equal(r["sorted_pairs"].cpu().numpy()[: w.P], sp)
     assert np.array_equal(r["pair_pos"].cpu().numpy()[: w.P], pp)
     # quantised activations
-    xc, xs, _ = omoe.quantize_x(x, w.dtype)
+    xc, xs, xh = omoe.quantize_x(x, w.dtype)
     gc, gs = layer.xq_numpy(r, w.T)
     assert np.array_equal(gc, xc)
     if xs is not None:
         assert np.array_equal(gs, xs)
+        # the 16-bit dequantised copy the GEMM reads equals the exact values
+        assert np.array_equal(layer.xq_dequant(r, w.T), xh)
     # requantised intermediate, expert-sorted: compare dequantised values
     hc, hs = layer.hq_numpy(r, w.T)
     h_got = oquant.dequantize_act(hc, hs, w.dtype)
+    if hs is not None:
+        assert np.array_equal(layer.hq_dequant(r, w.T), h_got)
     h_ref = np.stack([ref.h[(int(p) // w.k, int(p) % w.k)][2] for p in sp])
     assert gh.rel_l2(h_got, h_ref) <= gh.out_tolerance(w.dtype)
     # expert outputs y (bf16, slot-major)
