@@ -4,12 +4,14 @@
 
 One step = one pass of the whole layer over one batch (route -> permute +
 activation quantisation -> gate/up GEMM + SwiGLU + requant -> down GEMM ->
-combine) with inputs and prepared weights already resident in HBM.  The
-default workload is the bf16 decode layer (T=64, H=4096, I=1408, E=64,
-top-6).  Prints one JSON line with tokens/s, the roofline of the dominant
-kernel (gate/up GEMM, timed with HIP events on the launch stream over the
-timed region), the whole-layer HBM fraction and the CPU oracle timed on a
-bounded sample of the same workload.
+combine), i.e. one moe_forward call, with inputs and prepared weights already resident in HBM.  The default
+workload is the bf16 decode layer (T=64, H=4096, I=1408, E=64, top-6).
+Prints one JSON line with tokens/s (K steps of moe_forward: the five stage
+kernels back to back on torch's stream, no events between them), the
+roofline of the dominant kernel (the gate/up GEMM, timed with HIP events on
+its launch stream over a second region of K steps through the staged entry
+points), whole-layer HBM / MFMA fractions, the single-launch entry's step
+time, and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -24,10 +26,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "nvfp4": 2500.0}  # dense; NVFP4 runs bf16 MFMA
+# dense MFMA peak of the arithmetic the contraction runs in: bf16 MFMA for bf16
+# and MXFP8 (exact fp8 -> bf16), fp16 MFMA for NVFP4 (exact e2m1 x e4m3 -> fp16)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 2500.0, "nvfp4": 2500.0}
+FP8_PEAK_TFLOPS = 5000.0
 DEFAULT_WORKLOAD = "bf16_decode"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_sort_amd", "csrc", "moe_gemm.hip")
+CSRC = os.path.join(ROOT, "mixture_experts_layer_sort_amd", "csrc")
 
 
 def weight_bytes_per_elem(dtype):
@@ -40,8 +45,12 @@ def act_bytes_per_elem(dtype):
 
 
 def kernel_source_hash():
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every kernel source (the counters describe one build)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload):
@@ -213,28 +222,78 @@ def main():
     w = mi.WORKLOADS[args.workload]
     lib, gh, cw, layer, x, logits = build_layer(w, device)
     del cw
-    step = StagedStep(lib, layer, x, logits)
+    out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=device)
+    ids_t = torch.empty(w.T, w.k, dtype=torch.int32, device=device)
+    wts_t = torch.empty(w.T, w.k, dtype=torch.float32, device=device)
+
+    def forward():
+        lib.moe_forward(layer.shape, w.T, layer.packed, logits, x, out, layer.ws, topk_ids=ids_t, topk_w=wts_t)
+
     for _ in range(args.warmup):
-        step.run()
+        forward()
     torch.cuda.synchronize()
-    ids = step.ids.cpu().numpy()
+    ids = ids_t.cpu().numpy()
     n_active = int(len(np.unique(ids)))
 
+    # timed region: K steps of moe_forward (five kernels each) on torch's stream,
+    # one HIP event pair around the whole region; no events between kernels
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for _ in range(args.steps):
-        step.run(timed=True)
+        forward()
+    ev1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = 1e3 * elapsed / args.steps
+    gpu_ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # kernel timing region: K steps of the same kernels through the staged entry
+    # points, HIP events around every kernel (the events themselves add gaps)
+    step = StagedStep(lib, layer, x, logits)
+    for _ in range(3):
+        step.run()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step.run(timed=True)
+    torch.cuda.synchronize()
     kms = step.kernel_ms()
 
+    # the single-launch entry, for comparison
+    def fused():
+        lib.moe_forward_fused(layer.shape, w.T, layer.packed, logits, x, out, layer.ws)
+
+    for _ in range(3):
+        fused()
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(args.steps):
+        fused()
+    f1.record()
+    torch.cuda.synchronize()
+    fused_ms = f0.elapsed_time(f1) / args.steps
+    if layer.sync_words()[2]:
+        raise RuntimeError("the single-launch kernel reported a spin timeout")
+
     B, F = layer_bytes_flops(w, n_active)
-    g13_bytes = gemm13_bytes(w, n_active)
-    g13_gbs = g13_bytes / (kms["gemm13"] * 1e-3) / 1e9
-    layer_gbs = B / (ms_step * 1e-3) / 1e9
+    layer_gbs = B / (gpu_ms_step * 1e-3) / 1e9
+    tflops = F / (gpu_ms_step * 1e-3) / 1e12
+    g13b = gemm13_bytes(w, n_active)
+    g13_gbs = g13b / (kms["gemm13"] * 1e-3) / 1e9
+    g13_tflops = w.T * w.k * 4.0 * w.H * w.I / (kms["gemm13"] * 1e-3) / 1e12
     traffic = load_traffic(w.name)
     decode = w.T * w.k <= 16 * w.E
+    if decode:
+        roof = {"bound": "hbm", "kernel": "gemm13_swiglu_quant", "achieved": g13_gbs, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": g13_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                "algorithmic_bytes_per_launch": g13b, "avg_launch_ms": kms["gemm13"]}
+    else:
+        roof = {"bound": "mfma", "kernel": "gemm13_swiglu_quant", "achieved": g13_tflops,
+                "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s", "frac": g13_tflops / MFMA_PEAK_TFLOPS[w.dtype],
+                "traffic": traffic, "algorithmic_flops_per_launch": w.T * w.k * 4.0 * w.H * w.I,
+                "avg_launch_ms": kms["gemm13"]}
     rec = {
         "metric": "MoE layer tokens/s; % HBM BW (decode) / % MFMA peak (prefill)",
         "value": w.T / (ms_step * 1e-3),
@@ -250,13 +309,13 @@ def main():
         "data": "synthetic (seeded N(0,1) x and logits, N(0,0.02) weights; random init)",
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.k,
                    "weights": w.dtype, "routing_skew": w.bias, "active_experts": n_active},
-        "roofline": {"bound": "hbm", "kernel": "gemm13_swiglu_quant", "achieved": g13_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": g13_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": g13_bytes, "avg_launch_ms": kms["gemm13"]},
-        "layer": {"algorithmic_bytes": B, "flops": F, "hbm_gbs": layer_gbs, "hbm_frac": layer_gbs / HBM_PEAK_GBS,
-                  "mfma_tflops": F / (ms_step * 1e-3) / 1e12,
-                  "mfma_frac": F / (ms_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
-                  "regime": "decode" if decode else "prefill", "kernel_ms": kms},
+        "roofline": roof,
+        "layer": {"algorithmic_bytes": B, "flops": F, "gpu_ms_per_step": gpu_ms_step, "hbm_gbs": layer_gbs,
+                  "hbm_frac": layer_gbs / HBM_PEAK_GBS, "mfma_tflops": tflops,
+                  "mfma_frac": tflops / MFMA_PEAK_TFLOPS[w.dtype],
+                  "mfma_frac_of_fp8_peak": tflops / FP8_PEAK_TFLOPS if w.dtype == "mxfp8" else None,
+                  "regime": "decode" if decode else "prefill", "staged_kernel_ms": kms,
+                  "single_launch_ms_per_step": fused_ms},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, device, ids)

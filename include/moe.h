@@ -189,15 +189,37 @@ MOE_API moe_status moe_gemm2(const moe_shape* shape, int32_t T, const void* pack
 MOE_API moe_status moe_combine(const moe_shape* shape, int32_t T, const uint16_t* y, const float* topk_w,
                        uint16_t* out, hipStream_t stream);
 
-/* The whole layer: route -> permute (+quant) -> gemm13 -> gemm2 -> combine,
- * with every intermediate in `ws` (moe_workspace_bytes(shape) bytes, sized
- * once for max_tokens; any T <= max_tokens reuses it [MegaMoE drop workflow,
- * §6: knobs and buffers are sized once by the token capacity]).
+/* The whole layer: route -> permute (+quant) -> gemm13 -> gemm2 -> combine
+ * [vLLM PR 40082 report, "Implementation" item 1: one call does routing, W1
+ * GEMM, SwiGLU, W2 GEMM and the reduction], enqueued as the five stage
+ * kernels back to back on `stream` (bitwise the same results as the staged
+ * entry points).  Every intermediate lives in `ws` (moe_workspace_bytes(shape)
+ * bytes, sized once for max_tokens; any T <= max_tokens reuses it [MegaMoE
+ * drop workflow, §6: buffers are sized once by the token capacity]).
  * out bf16 [T, H].  topk_ids / topk_w: optional outputs (NULL = keep them in
  * the workspace). */
 MOE_API moe_status moe_forward(const moe_shape* shape, int32_t T, const void* packed, const float* logits,
                        const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The same layer in ONE cooperative launch of a persistent kernel: grid
+ * barriers separate routing, the permutation, the two GEMMs and the combine;
+ * results are bitwise equal to moe_forward.  On MI355X a device-wide barrier
+ * costs ~10 us (measured), more than a kernel boundary on one stream, so
+ * moe_forward is the faster entry; this one serves callers that need a
+ * single dispatch.  The workspace opens with synchronisation words that must
+ * be zero before the first call (moe_workspace_init, or a zeroed allocation)
+ * and are left zero by every call; calls on one workspace must be
+ * stream-ordered.  Spin-waits are bounded: a timeout (a bug, never expected)
+ * sets the third synchronisation word and lets the kernel finish.
+ * MOE_ERR_UNSUPPORTED if the device cannot host the cooperative grid. */
+MOE_API moe_status moe_forward_fused(const moe_shape* shape, int32_t T, const void* packed, const float* logits,
+                                     const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Zero the synchronisation words at the start of a workspace (enqueued on
+ * `stream`); needed once per workspace before moe_forward_fused. */
+MOE_API moe_status moe_workspace_init(const moe_shape* shape, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -38,6 +38,8 @@ EXPORTED = [
     "moe_gemm2",
     "moe_combine",
     "moe_forward",
+    "moe_forward_fused",
+    "moe_workspace_init",
 ]
 
 
@@ -89,6 +91,8 @@ def _load():
         "moe_gemm2": (I32, [S, I32, P, P, P, P, P, P, SZ, P]),
         "moe_combine": (I32, [S, I32, P, P, P, P]),
         "moe_forward": (I32, [S, I32, P, P, P, P, P, P, P, SZ, P]),
+        "moe_forward_fused": (I32, [S, I32, P, P, P, P, P, P, P, SZ, P]),
+        "moe_workspace_init": (I32, [S, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -230,3 +234,14 @@ def moe_forward(shape, T, packed, logits, x, out, ws, ws_bytes=None, topk_ids=No
     nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
     _check(_lib.moe_forward(ctypes.byref(shape), T, _ptr(packed), _ptr(logits), _ptr(x), _ptr(out),
                             _ptr(topk_ids), _ptr(topk_w), _ptr(ws), nbytes, _stream(stream)), "moe_forward")
+
+
+def moe_forward_fused(shape, T, packed, logits, x, out, ws, ws_bytes=None, topk_ids=None, topk_w=None, stream=None):
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(_lib.moe_forward_fused(ctypes.byref(shape), T, _ptr(packed), _ptr(logits), _ptr(x), _ptr(out),
+                                  _ptr(topk_ids), _ptr(topk_w), _ptr(ws), nbytes, _stream(stream)), "moe_forward_fused")
+
+
+def moe_workspace_init(shape, ws, ws_bytes=None, stream=None):
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(_lib.moe_workspace_init(ctypes.byref(shape), _ptr(ws), nbytes, _stream(stream)), "moe_workspace_init")

@@ -33,7 +33,7 @@ std::atomic<int> g_occ[kMaxDevices][3][2][2];
 int gemm_grid(int dt, bool g13, int T, int k, int E) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  const int nt = (long long)T * k > 16LL * E ? 2 : 1;
+  const int nt = gemm_nt(T, k, E);
   int occ = 1;
   if (dev >= 0 && dev < kMaxDevices) {
     occ = g_occ[dev][dt][g13][nt - 1].load(std::memory_order_relaxed);
@@ -43,6 +43,21 @@ int gemm_grid(int dt, bool g13, int T, int k, int E) {
     }
   }
   return device_cu_count() * occ;
+}
+
+// co-resident blocks of the fused kernel, per device: [dev][dt][nt-1]; -1 = unusable
+std::atomic<int> g_fused_occ[kMaxDevices][3][2];
+
+int fused_grid(int dt, int T, int k, int E) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  const int nt = gemm_nt(T, k, E);
+  int occ = g_fused_occ[dev][dt][nt - 1].load(std::memory_order_relaxed);
+  if (occ == 0) {
+    occ = fused_blocks_per_cu(dt, nt);
+    g_fused_occ[dev][dt][nt - 1].store(occ > 0 ? occ : -1, std::memory_order_relaxed);
+  }
+  return occ > 0 ? occ * device_cu_count() : 0;
 }
 
 moe_status check_shape(const moe_shape* s) {
@@ -150,6 +165,15 @@ moe_status moe_prepare_weights(const moe_shape* s, const void* w13_codes, const 
                                  (const uint8_t*)w2_scales, w2_alpha, (uint8_t*)packed, stream));
 }
 
+moe_status moe_workspace_init(const moe_shape* s, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_workspace_bytes(s)) return MOE_ERR_WORKSPACE;
+  return launched(launch_zero_sync((uint8_t*)ws, s->dtype, s->num_experts, s->hidden, s->inter, s->top_k,
+                                   s->max_tokens, stream));
+}
+
 moe_status moe_route(const moe_shape* s, int32_t T, const float* logits, int32_t* topk_ids, float* topk_w,
                      hipStream_t stream) {
   moe_status st = check_T(s, T);
@@ -209,14 +233,22 @@ moe_status moe_combine(const moe_shape* s, int32_t T, const uint16_t* y, const f
   return launched(launch_combine(T, s->hidden, s->top_k, y, topk_w, out, stream));
 }
 
-moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const float* logits, const uint16_t* x,
-                       uint16_t* out, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+// Shared argument checks of the two whole-layer entry points.
+static moe_status check_forward(const moe_shape* s, int32_t T, const void* packed, const float* logits,
+                                const uint16_t* x, uint16_t* out, void* ws, size_t ws_bytes) {
   moe_status st = check_T(s, T);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!packed || !logits || !x || !out || !ws) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe_workspace_bytes(s)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const float* logits, const uint16_t* x,
+                       uint16_t* out, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status st = check_forward(s, T, packed, logits, x, out, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
   const int dt = s->dtype, E = s->num_experts, H = s->hidden, I = s->inter, k = s->top_k;
   const WorkspaceLayout W = workspace_layout(dt, E, H, I, k, s->max_tokens);
   uint8_t* base = (uint8_t*)ws;
@@ -239,6 +271,22 @@ moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const 
                      gemm_grid(dt, false, T, k, E), stream);
   if (e == hipSuccess) e = launch_combine(T, H, k, y, wts, out, stream);
   return launched(e);
+}
+
+moe_status moe_forward_fused(const moe_shape* s, int32_t T, const void* packed, const float* logits,
+                             const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_forward(s, T, packed, logits, x, out, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  const int dt = s->dtype, E = s->num_experts, H = s->hidden, I = s->inter, k = s->top_k;
+  const WorkspaceLayout W = workspace_layout(dt, E, H, I, k, s->max_tokens);
+  uint8_t* base = (uint8_t*)ws;
+  int32_t* ids = topk_ids ? topk_ids : (int32_t*)(base + W.ids);
+  float* wts = topk_w ? topk_w : (float*)(base + W.wts);
+  const int grid = fused_grid(dt, T, k, E);
+  if (grid <= 0) return MOE_ERR_UNSUPPORTED;
+  return launched(launch_fused(dt, E, H, I, k, T, (const uint8_t*)packed, logits, x, out, ids, wts, base, ws_bytes,
+                               s->max_tokens, grid, stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,218 @@
+// The whole layer in one cooperative launch (moe_forward): one b12x-style
+// call that routes, dispatches, runs the gate/up GEMM + SwiGLU, the down GEMM
+// and the reduction [vLLM PR 40082 report, "Implementation" item 1].
+//
+// Phases of the persistent grid (all blocks co-resident; cooperative launch):
+//   1. route every token (one wave per token) and quantise x (grid-stride)
+//      -- grid barrier --
+//   2. block 0 sorts the pairs by expert (counting sort in LDS)
+//      -- grid barrier --
+//   3. the gate/up items, -- grid barrier --, the down items (default), or
+//      (MOE_FUSED_GEMM_BARRIER=0) every gate/up item then every down item,
+//      where a finished gate/up item bumps its expert's counter (release) and
+//      a down item of expert e waits for all of e's gate/up items (acquire).
+//      Items are dealt in index order, so a block only ever waits on items
+//      that precede its own: with all blocks resident this cannot deadlock.
+//      Measured on MI355X the per-item release/acquire costs more than the
+//      barrier it saves, hence the default.
+//      -- grid barrier --
+//   4. combine (slot order, deterministic)
+// Every spin-wait is bounded: on timeout it sets an error word and moves on
+// (garbage output, never a hang).  The last block out resets every
+// synchronisation word to zero for the next launch.
+#include "moe_gemm_item.h"
+#include "moe_stages.h"
+
+namespace moe {
+
+struct FusedArgs {
+  GemmArgs g13, g2;
+  const float* logits;
+  const uint16_t* x;
+  uint16_t* out;
+  int* ids;
+  float* wts;
+  int* offsets;
+  int* sorted_pairs;
+  int* pair_pos;
+  uint8_t* xq;
+  uint8_t* xq_scales;
+  uint16_t* xq_deq;
+  uint16_t* y;
+  unsigned* sync;  // [0] barrier arrivals, [1] exits, [2] timeout flag, [kSyncHeader + e] gate/up items done
+  int quant_x, T, E, H, I, k;
+};
+
+constexpr unsigned kSpinLimit = 1u << 22;  // ~10^8-10^9 cycles with the sleep below
+
+// Poll with relaxed device-scope loads (no cache invalidation per poll), then
+// one acquire fence once the count is reached.
+__device__ __forceinline__ void spin_until_geq(unsigned* p, unsigned target, unsigned* timeout_flag) {
+  unsigned n = 0;
+  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++n > kSpinLimit) {
+      __hip_atomic_store(timeout_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+#ifndef MOE_FUSED_GEMM_BARRIER  // 1: grid barrier between the GEMMs instead of per-expert counters
+#define MOE_FUSED_GEMM_BARRIER 1
+#endif
+
+// Monotonic grid barrier: the n-th barrier of a launch waits for n * gridDim.x arrivals.
+__device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned target) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    spin_until_geq(&sync[0], target, &sync[2]);
+  }
+  __syncthreads();
+}
+
+template <int DT, int NT>
+__global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
+  __shared__ int cum[1025];
+  __shared__ int wsum[4];
+  __shared__ f32x4_t red[3][4 * NT][64];
+  const unsigned G = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const long long gtid = (long long)blockIdx.x * kGemmThreads + tid, gstride = (long long)G * kGemmThreads;
+  unsigned* done13 = a.sync + kSyncHeader;
+
+  // 1. routing (one wave per token) and x quantisation
+  for (int t = (int)(gtid >> 6); t < a.T; t += (int)(gstride >> 6)) route_token(a.logits, t, a.E, a.k, a.ids, a.wts, lane);
+  if (a.quant_x) quantize_x_blocks<DT>(a.x, (long long)a.T * a.H, a.xq, a.xq_scales, a.xq_deq, gtid, gstride);
+  grid_barrier(a.sync, G);
+
+  // 2. permutation
+  if (blockIdx.x == 0) permute_block<kGemmThreads / 64>(a.ids, a.T * a.k, a.E, a.offsets, a.sorted_pairs, a.pair_pos);
+  grid_barrier(a.sync, 2 * G);
+
+  // 3. the two grouped GEMMs
+  const int total_mt = build_schedule(a.offsets, a.E, 16 * NT, cum, wsum);
+  const long long n13 = (long long)total_mt * a.g13.G, n2 = (long long)total_mt * a.g2.G;
+  if constexpr (MOE_FUSED_GEMM_BARRIER) {
+    for (long long w = blockIdx.x; w < n13; w += G) gemm_item<DT, NT, true>(a.g13, w, cum, red);
+    grid_barrier(a.sync, 3 * G);
+    for (long long w = blockIdx.x; w < n2; w += G) gemm_item<DT, NT, false>(a.g2, w, cum, red);
+    grid_barrier(a.sync, 4 * G);
+  } else {
+  for (long long w = blockIdx.x; w < n13 + n2; w += G) {
+    if (w < n13) {
+      const int e = gemm_item<DT, NT, true>(a.g13, w, cum, red);
+      if (tid == 0) __hip_atomic_fetch_add(&done13[e], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const long long w2 = w - n13;
+      const int e = find_expert(cum, a.E, (int)(w2 / a.g2.G));
+      if (tid == 0) spin_until_geq(&done13[e], (unsigned)((cum[e + 1] - cum[e]) * a.g13.G), &a.sync[2]);
+      __syncthreads();
+      gemm_item<DT, NT, false>(a.g2, w2, cum, red);
+    }
+  }
+  grid_barrier(a.sync, 3 * G);
+  }
+
+  // 4. combine
+  combine_range(a.y, a.wts, a.T, a.H, a.k, a.out, gtid, gstride);
+
+  // the last block out clears the synchronisation words (the timeout flag stays)
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = __hip_atomic_fetch_add(&a.sync[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == G - 1) {
+      for (int e = 0; e < a.E; ++e) __hip_atomic_store(&done13[e], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.sync[1], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+__global__ void zero_u32_kernel(unsigned* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+template <int DT, int NT>
+static const void* fused_fn() {
+  return reinterpret_cast<const void*>(fused_kernel<DT, NT>);
+}
+
+static const void* fused_ptr(int dt, int nt) {
+  if (dt == DT_BF16) return nt == 1 ? fused_fn<DT_BF16, 1>() : fused_fn<DT_BF16, 2>();
+  if (dt == DT_MXFP8) return nt == 1 ? fused_fn<DT_MXFP8, 1>() : fused_fn<DT_MXFP8, 2>();
+  return nt == 1 ? fused_fn<DT_NVFP4, 1>() : fused_fn<DT_NVFP4, 2>();
+}
+
+int fused_blocks_per_cu(int dt, int nt) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_ptr(dt, nt), kGemmThreads, 0) != hipSuccess || n < 1)
+    return 0;
+  return n;
+}
+
+hipError_t launch_fused(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const float* logits,
+                        const uint16_t* x, uint16_t* out, int* ids, float* wts, uint8_t* ws, size_t ws_bytes,
+                        int max_tokens, int grid, hipStream_t s) {
+  const WorkspaceLayout W = workspace_layout(dt, E, H, I, k, max_tokens);
+  const PackedLayout L = packed_layout(dt, E, H, I);
+  FusedArgs f;
+  f.logits = logits;
+  f.x = x;
+  f.out = out;
+  f.ids = ids;
+  f.wts = wts;
+  f.offsets = reinterpret_cast<int*>(ws + W.offsets);
+  f.sorted_pairs = reinterpret_cast<int*>(ws + W.sorted_pairs);
+  f.pair_pos = reinterpret_cast<int*>(ws + W.pair_pos);
+  uint8_t* xq = dt == DT_BF16 ? const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(x)) : ws + W.xq;
+  uint8_t* hq = ws + W.hq;
+  f.xq = xq;
+  f.xq_scales = xq + act_scale_offset(dt, T, H);
+  f.xq_deq = reinterpret_cast<uint16_t*>(xq + act_dequant_offset(dt, T, H));
+  f.y = reinterpret_cast<uint16_t*>(ws + W.y);
+  f.sync = reinterpret_cast<unsigned*>(ws + W.sync);
+  f.quant_x = dt != DT_BF16;
+  f.T = T;
+  f.E = E;
+  f.H = H;
+  f.I = I;
+  f.k = k;
+  GemmArgs& g = f.g13;
+  g.wcodes = packed + L.w13_codes;
+  g.wscales = packed + L.w13_scales;
+  g.walpha = reinterpret_cast<const float*>(packed + L.w13_alpha);
+  g.offsets = f.offsets;
+  g.sorted_pairs = f.sorted_pairs;
+  g.act = xq + act_operand_offset(dt, T, H);
+  g.out = hq;
+  g.out_scales = hq + act_scale_offset(dt, T * k, I);
+  g.out_deq = reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
+  g.E = E; g.K = H; g.G = L.G13; g.KG = L.KG13; g.k = k; g.n_out = I;
+  GemmArgs& h = f.g2;
+  h.wcodes = packed + L.w2_codes;
+  h.wscales = packed + L.w2_scales;
+  h.walpha = reinterpret_cast<const float*>(packed + L.w2_alpha);
+  h.offsets = f.offsets;
+  h.sorted_pairs = f.sorted_pairs;
+  h.act = hq + act_operand_offset(dt, T * k, I);
+  h.out = reinterpret_cast<uint8_t*>(f.y);
+  h.out_scales = nullptr;
+  h.out_deq = nullptr;
+  h.E = E; h.K = I; h.G = L.G2; h.KG = L.KG2; h.k = k; h.n_out = H;
+  (void)ws_bytes;
+  void* args[] = {&f};
+  return hipLaunchCooperativeKernel(fused_ptr(dt, gemm_nt(T, k, E)), dim3(grid), dim3(kGemmThreads), args, 0, s);
+}
+
+hipError_t launch_zero_sync(uint8_t* ws, int dt, int E, int H, int I, int k, int max_tokens, hipStream_t s) {
+  const WorkspaceLayout W = workspace_layout(dt, E, H, I, k, max_tokens);
+  const int n = (int)(W.sync_bytes / 4);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, reinterpret_cast<unsigned*>(ws + W.sync),
+                     n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -16,404 +16,19 @@
 // the matrix unit's 16-row side so a handful of tokens per expert wastes no
 // weight bandwidth [MegaMoE drop workflow, §1: the NVFP4 kernel package is
 // the "swapab" variant].
-#include "moe_kernels.h"
+#include "moe_gemm_item.h"
+#include "moe_stages.h"
 
 namespace moe {
 
-constexpr int kGemmThreads = 256;
-
-struct GemmArgs {
-  const uint8_t* wcodes;
-  const uint8_t* wscales;
-  const float* walpha;
-  const int* offsets;
-  const int* sorted_pairs;
-  const uint8_t* act;         // B operand rows, 16-bit: xq (gemm13, row = token) or hq (gemm2, row = sorted row)
-  uint8_t* out;               // hq codes (gemm13) or y (gemm2)
-  uint8_t* out_scales;        // hq scales (gemm13)
-  uint16_t* out_deq;          // hq dequantised 16-bit copy (gemm13; MXFP8, NVFP4)
-  int E, K, G, KG, k, n_out;
-};
-
-// cum[e] = m-tiles of experts < e (LDS), returns the total.
-__device__ int build_schedule(const int* __restrict__ offsets, int E, int MT, int* cum, int* wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 4 (E <= 1024)
-  const int e0 = tid * per;
-  int cnt[4] = {0, 0, 0, 0}, local = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int e = e0 + j;
-    if (j < per && e < E) {
-      cnt[j] = (offsets[e + 1] - offsets[e] + MT - 1) / MT;
-      local += cnt[j];
-    }
-  }
-  int incl = local;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  int wbase = 0;
-  for (int ww = 0; ww < w; ++ww) wbase += wsum[ww];
-  int run = wbase + incl - local;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int e = e0 + j;
-    if (j < per && e < E) {
-      cum[e] = run;
-      run += cnt[j];
-    }
-  }
-  if (tid == kGemmThreads - 1) cum[E] = wbase + incl;
-  __syncthreads();
-  return cum[E];
-}
-
-__device__ __forceinline__ int find_expert(const int* cum, int E, int mtg) {
-  int lo = 0, hi = E;  // cum[lo] <= mtg < cum[hi]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (cum[mid] <= mtg) lo = mid;
-    else hi = mid;
-  }
-  return lo;
-}
-
-__device__ __forceinline__ bf16x8_t load_bf16x8(const uint8_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
-
-// 8 e2m1 codes (one dword, element j in nibble j) times an e4m3 scale (one
-// byte) -> 8 fp16, exactly: e2m1 (2 significant bits) x e4m3 (4 bits) fits
-// fp16's 11 bits and its exponent range.  Hardware converts at scale 1 (pure
-// conversion) and one packed fp16 multiply per pair.
-__device__ __forceinline__ f16x8_t nvfp4_dequant8(uint32_t codes, uint32_t e4m3_byte) {
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  f16x2 sc = __builtin_amdgcn_cvt_scalef32_f16_fp8(f16x2{}, e4m3_byte, 1.0f, 0, false);
-  sc[1] = sc[0];
-  f16x2 r[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sc,
-                __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * sc,
-                __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * sc,
-                __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * sc};
-  f16x8_t o;
-  __builtin_memcpy(&o, r, 16);
-  return o;
-}
-
-// 8 e4m3 codes (two dwords, element j in byte j) times 2^(e - 127) (an e8m0
-// scale byte) -> 8 bf16.  Exact: 4 significant bits, and the convert applies
-// the power-of-two scale by exponent arithmetic.  (The gfx950 scaled fp8
-// matrix instruction is not used: its internal accumulation keeps only about
-// 14 bits relative to the sum of |products|, measured.)
-__device__ __forceinline__ bf16x8_t mxfp8_dequant8(uint32_t lo, uint32_t hi, uint32_t e8m0) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const float sc = __uint_as_float(e8m0 << 23);  // 2^(e8m0 - 127); byte 0 -> 0 (all-zero block)
-  bf16x2 r[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false),
-                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true),
-                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false),
-                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true)};
-  bf16x8_t o;
-  __builtin_memcpy(&o, r, 16);
-  return o;
-}
-
-// ------------------------------------------------------------------ K-slice fragments
-// Raw bytes of one 128-wide K slice ("kgroup") for the 4 weight tiles of a
-// work item and its NT token sub-tiles, as loaded from memory; converted and
-// fed to the matrix unit by mma_kfrag.
-template <int DT>
-struct KW {  // words per lane per tile: codes (uint4) / scales (dwords)
-  static constexpr int A = DT == DT_BF16 ? 4 : (DT == DT_MXFP8 ? 2 : 1);
-  static constexpr int AS = DT == DT_NVFP4 ? 2 : 1;
-};
-
-template <int DT, int NT>
-struct KFrag {
-  uint4 ac[4][KW<DT>::A];
-  uint32_t as[4][KW<DT>::AS];
-  uint4 bc[NT][4];  // 16-bit activation operand, 4 chunks of 8
-};
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-template <bool NTLD>
-__device__ __forceinline__ uint4 ld_w16(const uint8_t* p) {
-  if constexpr (NTLD) {
-    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-  } else {
-    return *reinterpret_cast<const uint4*>(p);
-  }
-}
-
-template <int DT, int NT, bool G13, bool NTLD>
-__device__ __forceinline__ void load_kfrag(KFrag<DT, NT>& f, const GemmArgs& a, size_t tile0, int kg,
-                                           const int (&brow)[NT], int lane, int i16, int q) {
-  const size_t tcode = tile_code_bytes(DT), tscale = tile_scale_bytes(DT);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint8_t* pc = a.wcodes + (tile0 + t) * tcode;
-    if constexpr (DT == DT_BF16) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) f.ac[t][c] = ld_w16<NTLD>(pc + c * 1024 + lane * 16);
-    } else if constexpr (DT == DT_MXFP8) {
-      f.ac[t][0] = ld_w16<NTLD>(pc + lane * 16);
-      f.ac[t][1] = ld_w16<NTLD>(pc + 1024 + lane * 16);
-      f.as[t][0] = *reinterpret_cast<const uint32_t*>(a.wscales + (tile0 + t) * tscale + i16 * 4);
-    } else {
-      f.ac[t][0] = ld_w16<NTLD>(pc + lane * 16);
-      const uint2 sv = *reinterpret_cast<const uint2*>(a.wscales + (tile0 + t) * tscale + i16 * 8);
-      f.as[t][0] = sv.x;
-      f.as[t][1] = sv.y;
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < NT; ++s) {
-    const bool ok = brow[s] >= 0;
-    const uint8_t* p = a.act + ((size_t)(ok ? brow[s] : 0) * a.K + kg * 128 + 8 * q) * 2;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) f.bc[s][c] = ok ? *reinterpret_cast<const uint4*>(p + c * 64) : make_uint4(0, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-template <int DT, int NT>
-__device__ __forceinline__ void mma_kfrag(f32x4_t (&acc)[4][NT], const KFrag<DT, NT>& f, int q) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if constexpr (DT == DT_NVFP4) {
-        const int sb = 2 * c + (q >> 1);  // 16-block of this lane's 8 k's
-        const uint32_t sw = sb < 4 ? f.as[t][0] : f.as[t][1];
-        const f16x8_t A = nvfp4_dequant8(u4_word(f.ac[t][0], c), (sw >> (8 * (sb & 3))) & 0xFF);
-#pragma unroll
-        for (int s = 0; s < NT; ++s) {
-          f16x8_t B;
-          __builtin_memcpy(&B, &f.bc[s][c], 16);
-          acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[t][s], 0, 0, 0);
-        }
-      } else {
-        bf16x8_t A;
-        if constexpr (DT == DT_BF16) {
-          __builtin_memcpy(&A, &f.ac[t][c], 16);
-        } else {
-          const uint4& v = f.ac[t][c >> 1];
-          A = (c & 1) ? mxfp8_dequant8(v.z, v.w, (f.as[t][0] >> (8 * c)) & 0xFF)
-                      : mxfp8_dequant8(v.x, v.y, (f.as[t][0] >> (8 * c)) & 0xFF);
-        }
-#pragma unroll
-        for (int s = 0; s < NT; ++s) {
-          bf16x8_t B;
-          __builtin_memcpy(&B, &f.bc[s][c], 16);
-          acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t][s], 0, 0, 0);
-        }
-      }
-    }
-  }
-}
-
-// Compile-time tuning knobs of the grouped GEMMs.
-#ifndef MOE_GEMM_PIPELINE  // 1: double-buffer K steps (prefetch the next while computing)
-#define MOE_GEMM_PIPELINE 1
-#endif
-#ifndef MOE_GEMM_NTLOAD  // 1: non-temporal weight loads on the decode path
-#define MOE_GEMM_NTLOAD 1
-#endif
-#ifndef MOE_GEMM_U_BF16  // kgroups per step, per weight format
-#define MOE_GEMM_U_BF16 1
-#endif
-#ifndef MOE_GEMM_U_MXFP8
-#define MOE_GEMM_U_MXFP8 1
-#endif
-#ifndef MOE_GEMM_U_NVFP4
-#define MOE_GEMM_U_NVFP4 1
-#endif
-
-// kgroups per pipeline step: enough bytes in flight per wave for each format
-template <int DT>
-struct StepK {
-  static constexpr int U = DT == DT_BF16 ? MOE_GEMM_U_BF16 : (DT == DT_MXFP8 ? MOE_GEMM_U_MXFP8 : MOE_GEMM_U_NVFP4);
-};
-
 template <int DT, int NT, bool G13>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
-  constexpr int MT = 16 * NT;
-  constexpr int U = StepK<DT>::U;
-  constexpr bool NTLD = MOE_GEMM_NTLOAD && NT == 1;  // decode: weights are streamed once
   __shared__ int cum[1025];
   __shared__ int wsum[4];
   __shared__ f32x4_t red[3][4 * NT][64];
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int i16 = lane & 15, q = lane >> 4;
-  const int total_mt = build_schedule(a.offsets, a.E, MT, cum, wsum);
+  const int total_mt = build_schedule(a.offsets, a.E, 16 * NT, cum, wsum);
   const long long total = (long long)total_mt * a.G;
-  // K slices are dealt to the 4 waves in rounds of 4U consecutive kgroups
-  // (wave w takes kgroups 4U*j + U*w .. +U), so a block streams one
-  // contiguous region; steps are double-buffered.
-  const int nrounds = (a.KG + 4 * U - 1) / (4 * U);
-
-  for (long long w = blockIdx.x; w < total; w += gridDim.x) {
-    const int mtg = (int)(w / a.G), g = (int)(w % a.G);
-    const int e = find_expert(cum, a.E, mtg);
-    const int r0 = a.offsets[e] + (mtg - cum[e]) * MT, r_end = a.offsets[e + 1];
-    int brow[NT];
-#pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      int r = r0 + 16 * s + i16;
-      brow[s] = r < r_end ? (G13 ? a.sorted_pairs[r] / a.k : r) : -1;
-    }
-    f32x4_t acc[4][NT];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int s = 0; s < NT; ++s) acc[t][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const size_t tbase = (size_t)(e * a.G + g) * a.KG;
-    KFrag<DT, NT> F0[U], F1[U];
-    auto load_step = [&](KFrag<DT, NT>(&F)[U], int j) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kg = 4 * U * j + U * wv + u;
-        if (kg < a.KG) load_kfrag<DT, NT, G13, NTLD>(F[u], a, (tbase + kg) * 4, kg, brow, lane, i16, q);
-      }
-    };
-    auto mma_step = [&](const KFrag<DT, NT>(&F)[U], int j) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kg = 4 * U * j + U * wv + u;
-        if (kg < a.KG) mma_kfrag<DT, NT>(acc, F[u], q);
-      }
-    };
-    if constexpr (MOE_GEMM_PIPELINE) {
-      load_step(F0, 0);
-      for (int j = 0; j < nrounds; j += 2) {
-        if (j + 1 < nrounds) load_step(F1, j + 1);
-        mma_step(F0, j);
-        if (j + 1 < nrounds) {
-          if (j + 2 < nrounds) load_step(F0, j + 2);
-          mma_step(F1, j + 1);
-        }
-      }
-    } else {
-      for (int j = 0; j < nrounds; ++j) {
-        load_step(F0, j);
-        mma_step(F0, j);
-      }
-    }
-
-    // reduce the four waves' partial sums into wave 0
-    if (wv > 0) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int s = 0; s < NT; ++s) red[wv - 1][t * NT + s][lane] = acc[t][s];
-    }
-    __syncthreads();
-    if (wv == 0) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int s = 0; s < NT; ++s) acc[t][s] += red[0][t * NT + s][lane] + red[1][t * NT + s][lane] + red[2][t * NT + s][lane];
-      const float alpha = DT == DT_NVFP4 ? a.walpha[e] : 1.f;
-#pragma unroll
-      for (int s = 0; s < NT; ++s) {
-        const int r = r0 + 16 * s + i16;
-        const bool ok = r < r_end;
-        if constexpr (G13) {
-          // tiles 0,1 = gate rows 32g + 16tp + 4q + j; tiles 2,3 = the matching up rows
-          float h[2][4];
-#pragma unroll
-          for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              float gv = acc[tp][s][j] * alpha, uv = acc[2 + tp][s][j] * alpha;
-              h[tp][j] = gv / (1.0f + expf(-gv)) * uv;
-            }
-          const int I = a.n_out;
-          if constexpr (DT == DT_BF16) {
-            if (ok) {
-              uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * g + 4 * q;
-#pragma unroll
-              for (int tp = 0; tp < 2; ++tp) {
-                uint2 v;
-                v.x = f32_to_bf16(h[tp][0]) | ((uint32_t)f32_to_bf16(h[tp][1]) << 16);
-                v.y = f32_to_bf16(h[tp][2]) | ((uint32_t)f32_to_bf16(h[tp][3]) << 16);
-                *reinterpret_cast<uint2*>(o + 16 * tp) = v;
-              }
-            }
-          } else if constexpr (DT == DT_MXFP8) {
-            // one block of 32 along I: [32g, 32g+32), spread over the 4 lanes sharing i16
-            float amax = 0.f;
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(h[tp][j]));
-            amax = wave_max_xor(amax, 16, 32);
-            const int sx = mx_scale_exp(amax);
-            if (ok) {
-              uint8_t* o = a.out + (size_t)r * I + 32 * g + 4 * q;
-              uint16_t* od = a.out_deq + (size_t)r * I + 32 * g + 4 * q;
-#pragma unroll
-              for (int tp = 0; tp < 2; ++tp) {
-                uint32_t v = 0, d[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                  const uint32_t c = e4m3_from_f32(ldexpf(h[tp][j], -sx));
-                  v |= c << (8 * j);
-                  d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), sx)) >> 16;  // exact in bf16
-                }
-                *reinterpret_cast<uint32_t*>(o + 16 * tp) = v;
-                *reinterpret_cast<uint2*>(od + 16 * tp) = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
-              }
-              if (q == 0) a.out_scales[(size_t)r * (I / 32) + g] = (uint8_t)(sx + 127);
-            }
-          } else {
-            // two blocks of 16 along I: [32g + 16tp, +16)
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-              float amax = fmaxf(fmaxf(fabsf(h[tp][0]), fabsf(h[tp][1])), fmaxf(fabsf(h[tp][2]), fabsf(h[tp][3])));
-              amax = wave_max_xor(amax, 16, 32);
-              const uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
-              const float sc = e4m3_to_f32(sc_code);
-              uint32_t v = 0, d[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                uint32_t c = sc > 0.f ? e2m1_from_f32(h[tp][j], sc) : ((__float_as_uint(h[tp][j]) >> 28) & 8u);
-                v |= c << (4 * j);
-                d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
-              }
-              if (ok) {
-                *reinterpret_cast<uint16_t*>(a.out + (size_t)r * (I / 2) + 16 * g + 8 * tp + 2 * q) = (uint16_t)v;
-                if (q == 0) a.out_scales[(size_t)r * (I / 16) + 2 * g + tp] = (uint8_t)sc_code;
-                *reinterpret_cast<uint2*>(a.out_deq + (size_t)r * I + 32 * g + 16 * tp + 4 * q) =
-                    make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
-              }
-            }
-          }
-        } else {
-          if (ok) {
-            const int p = a.sorted_pairs[r];
-            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)p * a.n_out + 64 * g + 4 * q;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              uint2 v;
-              v.x = f32_to_bf16(acc[t][s][0] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][1] * alpha) << 16);
-              v.y = f32_to_bf16(acc[t][s][2] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][3] * alpha) << 16);
-              *reinterpret_cast<uint2*>(o + 16 * t) = v;
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
+  for (long long w = blockIdx.x; w < total; w += gridDim.x) gemm_item<DT, NT, G13>(a, w, cum, red);
 }
 
 // ------------------------------------------------------------------ prepare (repack)
@@ -466,31 +81,10 @@ __global__ void copy_f32_kernel(const float* __restrict__ s, float* __restrict__
 }
 
 // ------------------------------------------------------------------ combine
-// out[t, h] = bf16( sum_j w[t, j] * y[t*k + j, h] ), fp32, slot order.
 __global__ void combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ wts, int T, int H, int k,
                                uint16_t* __restrict__ out) {
-  const long long n = (long long)T * H / 8;
-  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
-    const long long e0 = i * 8;
-    const int t = (int)(e0 / H), h = (int)(e0 % H);
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const float wj = wts[(size_t)t * k + j];
-      const uint4 v = *reinterpret_cast<const uint4*>(y + ((size_t)t * k + j) * H + h);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        acc[2 * m] += wj * bf16_to_f32(u[m] & 0xFFFF);
-        acc[2 * m + 1] += wj * bf16_to_f32(u[m] >> 16);
-      }
-    }
-    uint4 o;
-    o.x = f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-    o.y = f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-    o.z = f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
-    o.w = f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
-    *reinterpret_cast<uint4*>(out + e0) = o;
-  }
+  combine_range(y, wts, T, H, k, out, blockIdx.x * (long long)blockDim.x + threadIdx.x,
+                (long long)gridDim.x * blockDim.x);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -508,8 +102,6 @@ static hipError_t dispatch_gemm(int dt, int nt, const GemmArgs& a, int grid, hip
   return nt == 1 ? launch_gemm_t<DT_NVFP4, 1, G13>(a, grid, s) : launch_gemm_t<DT_NVFP4, 2, G13>(a, grid, s);
 }
 
-// token sub-tiles per item: 1 while an expert sees at most ~16 rows on average
-static int choose_nt(int T, int k, int E) { return (long long)T * k > 16LL * E ? 2 : 1; }
 
 int gemm_blocks_per_cu(int dt, bool g13, int nt) {
   int n = 0;
@@ -540,7 +132,7 @@ hipError_t launch_gemm13(int dt, int E, int H, int I, int k, int T, const uint8_
   a.out_scales = hq + act_scale_offset(dt, T * k, I);
   a.out_deq = reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
   a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
-  return dispatch_gemm<true>(dt, choose_nt(T, k, E), a, grid, s);
+  return dispatch_gemm<true>(dt, gemm_nt(T, k, E), a, grid, s);
 }
 
 hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const int* offsets,
@@ -557,7 +149,7 @@ hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t
   a.out_scales = nullptr;
   a.out_deq = nullptr;
   a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
-  return dispatch_gemm<false>(dt, choose_nt(T, k, E), a, grid, s);
+  return dispatch_gemm<false>(dt, gemm_nt(T, k, E), a, grid, s);
 }
 
 hipError_t launch_prepare(int dt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13s, const float* w13a,

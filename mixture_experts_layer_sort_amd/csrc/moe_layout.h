@@ -88,14 +88,21 @@ MOE_HD size_t act_bytes(int dt, int rows, int K) {
 // 16-bit operand rows of an activation buffer: the codes for BF16, else the dequantised copy
 MOE_HD size_t act_operand_offset(int dt, int rows, int K) { return dt == DT_BF16 ? 0 : act_dequant_offset(dt, rows, K); }
 
-// moe_forward workspace, sized for max_tokens.
+// moe_forward workspace, sized for max_tokens.  It opens with the fused
+// kernel's synchronisation words (kSyncHeader words, then one per expert),
+// which must be zero before the first forward and are left zero by it.
+constexpr int kSyncHeader = 4;
+
 struct WorkspaceLayout {
-  size_t ids, wts, offsets, sorted_pairs, pair_pos, xq, hq, y, total;
+  size_t sync, sync_bytes, ids, wts, offsets, sorted_pairs, pair_pos, xq, hq, y, total;
 };
 
 MOE_HD WorkspaceLayout workspace_layout(int dt, int E, int H, int I, int k, int max_tokens) {
   WorkspaceLayout W;
   size_t P = (size_t)max_tokens * k, off = 0;
+  W.sync = off;
+  W.sync_bytes = align256((size_t)(kSyncHeader + E) * 4);
+  off += W.sync_bytes;
   W.ids = off; off = align256(off + P * 4);
   W.wts = off; off = align256(off + P * 4);
   W.offsets = off; off = align256(off + (size_t)(E + 1) * 4);

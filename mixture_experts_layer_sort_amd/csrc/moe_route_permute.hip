@@ -1,5 +1,5 @@
 // Routing, token permutation and activation / weight quantisation kernels.
-#include "moe_kernels.h"
+#include "moe_stages.h"
 
 namespace moe {
 
@@ -11,190 +11,13 @@ namespace moe {
 // "Implementation" item 1: routing inside the fused call].
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                     int* __restrict__ ids, float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  float v[16];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    int e = lane + 64 * i;
-    float x = e < E ? row[e] : -INFINITY;
-    v[i] = (x == x) ? x : -INFINITY;  // NaN never wins; results stay in range
-    if (e >= E) taken |= 1u << i;
-  }
-  float my_val = 0.f;
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int id = lane + 64 * i;
-      bool better = !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && id < bi));
-      bv = better ? v[i] : bv;
-      bi = better ? id : bi;
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      float ov = __shfl_xor(bv, m, 64);
-      int oi = __shfl_xor(bi, m, 64);
-      bool better = ov > bv || (ov == bv && oi < bi);
-      bv = better ? ov : bv;
-      bi = better ? oi : bi;
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) {
-      my_val = bv;
-      my_id = bi;
-    }
-  }
-  const float m0 = __shfl(my_val, 0, 64);
-  float ex = lane < k ? expf(my_val - m0) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m, 64);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    wts[(size_t)t * k + lane] = ex / sum;
-  }
+  if (t < T) route_token(logits, t, E, k, ids, wts, threadIdx.x & 63);
 }
 
-// ------------------------------------------------------------------ permutation
-// Block 0: stable counting sort of the P = T*k pairs by expert.  Each of the 8
-// waves owns a contiguous segment of pairs; pass 1 builds per-wave expert
-// histograms in LDS, a scan turns them into per-(wave, expert) start
-// positions, pass 2 walks each segment in order and ranks pairs of equal
-// expert inside a 64-pair step with ballots on the id bits.
-// Blocks 1..: in-kernel quantisation of the bf16 hidden states.
+// Block 0: the stable counting sort (permute_block); blocks 1..: in-kernel
+// quantisation of the bf16 hidden states.
 constexpr int kPermThreads = 512;
-constexpr int kPermWaves = kPermThreads / 64;
-
-__device__ void permute_block(const int* __restrict__ ids, int P, int E, int* __restrict__ offsets,
-                              int* __restrict__ sorted_pairs, int* __restrict__ pair_pos) {
-  __shared__ int hist[kPermWaves][1024];
-  __shared__ int scan_tmp[kPermThreads];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int i = tid; i < kPermWaves * 1024; i += kPermThreads) (&hist[0][0])[i] = 0;
-  __syncthreads();
-  const int S = ((P + kPermWaves * 64 - 1) / (kPermWaves * 64)) * 64;  // segment, multiple of 64
-  const int seg0 = min(P, w * S), seg1 = min(P, (w + 1) * S);
-  // ids outside [0, E) are clamped: results are then unspecified but every access stays in bounds
-  for (int p = seg0 + lane; p < seg1; p += 64) atomicAdd(&hist[w][min(max(ids[p], 0), E - 1)], 1);
-  __syncthreads();
-  // per-thread experts 2*tid, 2*tid+1: totals, block exclusive scan
-  int e0 = 2 * tid, local = 0;
-  int tot[2] = {0, 0};
-  for (int j = 0; j < 2; ++j) {
-    int e = e0 + j;
-    if (e < E)
-      for (int ww = 0; ww < kPermWaves; ++ww) tot[j] += hist[ww][e];
-    local += tot[j];
-  }
-  scan_tmp[tid] = local;
-  __syncthreads();
-  for (int d = 1; d < kPermThreads; d <<= 1) {  // Hillis-Steele inclusive scan
-    int add = tid >= d ? scan_tmp[tid - d] : 0;
-    __syncthreads();
-    scan_tmp[tid] += add;
-    __syncthreads();
-  }
-  int base = scan_tmp[tid] - local;
-  for (int j = 0; j < 2; ++j) {
-    int e = e0 + j;
-    if (e < E) {
-      offsets[e] = base;
-      int b = base;
-      for (int ww = 0; ww < kPermWaves; ++ww) {
-        int c = hist[ww][e];
-        hist[ww][e] = b;
-        b += c;
-      }
-      base += tot[j];
-    }
-  }
-  if (tid == 0) offsets[E] = P;
-  __syncthreads();
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int p0 = seg0; p0 < seg1; p0 += 64) {
-    const int p = p0 + lane;
-    const bool valid = p < seg1;
-    const int id = valid ? min(max(ids[p], 0), E - 1) : 0;
-    unsigned long long m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      bool bit = (id >> b) & 1;
-      unsigned long long bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
-    }
-    if (valid) {
-      int pos = hist[w][id] + __popcll(m & lt);
-      sorted_pairs[pos] = p;
-      pair_pos[p] = pos;
-      if (lane == 63 - __clzll(m)) hist[w][id] += __popcll(m);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
-template <int DT>
-__device__ void quantize_x_blocks(const uint16_t* __restrict__ x, long long n_elem, uint8_t* __restrict__ codes,
-                                  uint8_t* __restrict__ scales, uint16_t* __restrict__ deq, long long gtid,
-                                  long long gstride) {
-  if constexpr (DT == DT_BF16) {
-    // copy 8 bf16 per thread
-    const uint4* src = reinterpret_cast<const uint4*>(x);
-    uint4* dst = reinterpret_cast<uint4*>(codes);
-    for (long long i = gtid; i < n_elem / 8; i += gstride) dst[i] = src[i];
-  } else {
-    // MXFP8: 8 lanes x 4 elements per block of 32; NVFP4: 4 lanes x 4 per 16
-    constexpr int LPB = DT == DT_MXFP8 ? 8 : 4;
-    const long long nthreads = n_elem / 4;
-    for (long long i = gtid; i < ((nthreads + 63) / 64) * 64; i += gstride) {
-      const bool ok = i < nthreads;
-      uint2 raw = ok ? reinterpret_cast<const uint2*>(x)[i] : make_uint2(0, 0);
-      float v[4] = {bf16_to_f32(raw.x & 0xFFFF), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xFFFF),
-                    bf16_to_f32(raw.y >> 16)};
-      float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-      amax = wave_max_xor(amax, 1, LPB / 2);
-      const int sub = (int)(i % LPB);
-      const long long blk = i / LPB;
-      if constexpr (DT == DT_MXFP8) {
-        int s = mx_scale_exp(amax);
-        uint32_t out = 0, d[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t c = e4m3_from_f32(ldexpf(v[j], -s));
-          out |= c << (8 * j);
-          d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), s)) >> 16;  // exact in bf16
-        }
-        if (ok) {
-          reinterpret_cast<uint32_t*>(codes)[i] = out;
-          if (sub == 0) scales[blk] = (uint8_t)(s + 127);
-          reinterpret_cast<uint2*>(deq)[i] = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
-        }
-      } else {
-        uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
-        float sc = e4m3_to_f32(sc_code);
-        uint32_t out = 0, d[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t c = sc > 0.f ? e2m1_from_f32(v[j], sc) : ((__float_as_uint(v[j]) >> 28) & 8u);
-          out |= c << (4 * j);
-          d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
-        }
-        if (ok) {
-          reinterpret_cast<uint16_t*>(codes)[i] = (uint16_t)out;
-          if (sub == 0) scales[blk] = (uint8_t)sc_code;
-          reinterpret_cast<uint2*>(deq)[i] = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
-        }
-      }
-    }
-  }
-}
 
 template <int DT>
 __global__ __launch_bounds__(kPermThreads) void permute_quant_kernel(const int* __restrict__ ids, int P, int E,
@@ -206,7 +29,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_quant_kernel(const int* 
                                                                      uint8_t* __restrict__ xq_scales,
                                                                      uint16_t* __restrict__ xq_deq, int do_quant) {
   if (blockIdx.x == 0) {
-    permute_block(ids, P, E, offsets, sorted_pairs, pair_pos);
+    permute_block<kPermThreads / 64>(ids, P, E, offsets, sorted_pairs, pair_pos);
     return;
   }
   if (!do_quant) return;

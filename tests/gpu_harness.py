@@ -111,6 +111,7 @@ class DeviceLayer:
         self.packed = torch.empty(nbytes, dtype=torch.uint8, device=dev())
         lib.moe_prepare_weights(self.shape, cw.w13, cw.w13_s, cw.w13_a, cw.w2, cw.w2_s, cw.w2_a, self.packed)
         self.ws = torch.empty(lib.moe_workspace_bytes(self.shape), dtype=torch.uint8, device=dev())
+        lib.moe_workspace_init(self.shape, self.ws)
 
     def staged(self, x: torch.Tensor, logits: torch.Tensor) -> dict:
         """Run the five staged entry points; returns device tensors."""
@@ -138,6 +139,17 @@ class DeviceLayer:
         out = torch.empty(T, self.w.H, dtype=torch.bfloat16, device=dev()) if out is None else out
         lib.moe_forward(self.shape, T, self.packed, logits, x, out, self.ws, topk_ids=ids, topk_w=wts)
         return out
+
+    def forward_fused(self, x: torch.Tensor, logits: torch.Tensor, out=None, ids=None, wts=None) -> torch.Tensor:
+        T = x.shape[0]
+        out = torch.empty(T, self.w.H, dtype=torch.bfloat16, device=dev()) if out is None else out
+        lib.moe_forward_fused(self.shape, T, self.packed, logits, x, out, self.ws, topk_ids=ids, topk_w=wts)
+        return out
+
+    def sync_words(self) -> np.ndarray:
+        """The fused kernel's synchronisation words (zero between launches;
+        word 2 is its spin-timeout flag)."""
+        return self.ws[: 4 * (4 + self.w.E)].cpu().numpy().view(np.uint32)
 
     # --------------------------------------------------------- unpacking
     def split_act(self, buf: torch.Tensor, rows: int, K: int, scale_off: int):

@@ -76,7 +76,9 @@ def test_fullsize_parity(name, pool):
     logits = mi.device_logits(w, dev)
     r = layer.staged(x, logits)
     out_fwd = layer.forward(x, logits)
+    out_fused = layer.forward_fused(x, logits)
     torch.cuda.synchronize()
+    assert not layer.sync_words().any()
     _log(f"{name}: GPU done")
 
     x_bits = gh.bf16_numpy(x)
@@ -98,8 +100,9 @@ def test_fullsize_parity(name, pool):
     assert np.array_equal(gc[rows], xc)
     if xs is not None:
         assert np.array_equal(gs[rows], xs)
-    # fused == staged on every token
+    # both whole-layer entries == the staged entry points on every token
     assert np.array_equal(gh.bf16_numpy(out_fwd), gh.bf16_numpy(r["out"]))
+    assert np.array_equal(gh.bf16_numpy(out_fused), gh.bf16_numpy(r["out"]))
 
     # sampled tokens against the oracle, with the oracle's own weight quantisation
     toks, experts = _pick_tokens(ids, w.k, MAX_SAMPLE_EXPERTS)
@@ -142,5 +145,5 @@ def test_fullsize_parity(name, pool):
             assert gh.rel_l2(y_got, ref.y[(t, j)]) <= tol, (t, j)
     rel, mad = gh.check_out(gh.bf16_numpy(r["out"])[toks], ref.out, w.dtype, name)
     _log(f"{name}: sampled tokens out relL2 {rel:.2e} max|d|/rms {mad:.2e}")
-    del layer, cw, r, out_fwd
+    del layer, cw, r, out_fwd, out_fused
     torch.cuda.empty_cache()

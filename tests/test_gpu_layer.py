@@ -93,15 +93,22 @@ def test_layer_parity_small(name):
     rel, mad = gh.check_out(out_staged, ref.out, w.dtype, name)
     print(f"  out relL2 {rel:.2e}  max|d|/rms {mad:.2e}", flush=True)
 
-    # the fused entry runs the same kernels: bitwise equal, and reproducible
+    # both whole-layer entries run the same device code: bitwise equal, reproducible
     ids = torch.empty(w.T, w.k, dtype=torch.int32, device=gh.dev())
     wts = torch.empty(w.T, w.k, dtype=torch.float32, device=gh.dev())
     o1 = layer.forward(xd, ld, ids=ids, wts=wts)
     o2 = layer.forward(xd, ld)
+    ids_f = torch.empty_like(ids)
+    wts_f = torch.empty_like(wts)
+    o3 = layer.forward_fused(xd, ld, ids=ids_f, wts=wts_f)
+    o4 = layer.forward_fused(xd, ld)
     torch.cuda.synchronize()
-    assert np.array_equal(gh.bf16_numpy(o1), out_staged)
-    assert np.array_equal(gh.bf16_numpy(o2), out_staged)
+    for o in (o1, o2, o3, o4):
+        assert np.array_equal(gh.bf16_numpy(o), out_staged)
     assert torch.equal(ids, r["ids"]) and torch.equal(wts, r["wts"])
+    assert torch.equal(ids_f, r["ids"]) and torch.equal(wts_f, r["wts"])
+    # the single-launch kernel left its synchronisation words zero and never timed out
+    assert not layer.sync_words().any()
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (7, 8, 2), (64, 64, 6), (33, 256, 8), (5, 384, 8), (3, 1024, 32),
