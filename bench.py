@@ -196,6 +196,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-single-launch", action="store_true", help="do not time moe_forward_fused")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -264,18 +265,20 @@ def main():
     def fused():
         lib.moe_forward_fused(layer.shape, w.T, layer.packed, logits, x, out, layer.ws)
 
-    for _ in range(3):
-        fused()
-    torch.cuda.synchronize()
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record()
-    for _ in range(args.steps):
-        fused()
-    f1.record()
-    torch.cuda.synchronize()
-    fused_ms = f0.elapsed_time(f1) / args.steps
-    if layer.sync_words()[2]:
-        raise RuntimeError("the single-launch kernel reported a spin timeout")
+    fused_ms = None
+    if not args.skip_single_launch:
+        for _ in range(3):
+            fused()
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for _ in range(args.steps):
+            fused()
+        f1.record()
+        torch.cuda.synchronize()
+        fused_ms = f0.elapsed_time(f1) / args.steps
+        if layer.sync_words()[2]:
+            raise RuntimeError("the single-launch kernel reported a spin timeout")
 
     B, F = layer_bytes_flops(w, n_active)
     layer_gbs = B / (gpu_ms_step * 1e-3) / 1e9
