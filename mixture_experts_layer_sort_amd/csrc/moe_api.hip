@@ -27,35 +27,35 @@ int device_cu_count() {
   return n;
 }
 
-// occupancy of each GEMM variant, per device: [dev][dt][g13][nt-1]
-std::atomic<int> g_occ[kMaxDevices][3][2][2];
+// occupancy of each GEMM variant, per device: [dev][dt][g13][variant]
+std::atomic<int> g_occ[kMaxDevices][3][2][3];
 
 int gemm_grid(int dt, bool g13, int T, int k, int E) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  const int nt = gemm_nt(T, k, E);
+  const int v = gemm_variant(T, k, E);
   int occ = 1;
   if (dev >= 0 && dev < kMaxDevices) {
-    occ = g_occ[dev][dt][g13][nt - 1].load(std::memory_order_relaxed);
+    occ = g_occ[dev][dt][g13][v].load(std::memory_order_relaxed);
     if (occ <= 0) {
-      occ = gemm_blocks_per_cu(dt, g13, nt);
-      g_occ[dev][dt][g13][nt - 1].store(occ, std::memory_order_relaxed);
+      occ = v == 2 ? prefill_blocks_per_cu(dt, g13) : gemm_blocks_per_cu(dt, g13, v + 1);
+      g_occ[dev][dt][g13][v].store(occ, std::memory_order_relaxed);
     }
   }
   return device_cu_count() * occ;
 }
 
-// co-resident blocks of the fused kernel, per device: [dev][dt][nt-1]; -1 = unusable
-std::atomic<int> g_fused_occ[kMaxDevices][3][2];
+// co-resident blocks of the fused kernel, per device: [dev][dt][variant]; -1 = unusable
+std::atomic<int> g_fused_occ[kMaxDevices][3][3];
 
 int fused_grid(int dt, int T, int k, int E) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  const int nt = gemm_nt(T, k, E);
-  int occ = g_fused_occ[dev][dt][nt - 1].load(std::memory_order_relaxed);
+  const int v = gemm_variant(T, k, E);
+  int occ = g_fused_occ[dev][dt][v].load(std::memory_order_relaxed);
   if (occ == 0) {
-    occ = fused_blocks_per_cu(dt, nt);
-    g_fused_occ[dev][dt][nt - 1].store(occ > 0 ? occ : -1, std::memory_order_relaxed);
+    occ = fused_blocks_per_cu(dt, v);
+    g_fused_occ[dev][dt][v].store(occ > 0 ? occ : -1, std::memory_order_relaxed);
   }
   return occ > 0 ? occ * device_cu_count() : 0;
 }

@@ -21,6 +21,7 @@
 // (garbage output, never a hang).  The last block out resets every
 // synchronisation word to zero for the next launch.
 #include "moe_gemm_item.h"
+#include "moe_prefill_item.h"
 #include "moe_stages.h"
 
 namespace moe {
@@ -73,11 +74,24 @@ __device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned target) {
   __syncthreads();
 }
 
-template <int DT, int NT>
+// LDS of one block, reused phase by phase: the permutation's histograms, then
+// the GEMM items' cross-wave reduction (decode items) or operand stages
+// (prefill items).  V is the GEMM variant: 0 / 1 decode items of 16 / 32
+// rows, 2 prefill items.
+template <int V>
+constexpr size_t fused_lds_bytes() {
+  constexpr size_t perm = sizeof(int) * permute_lds_ints<kGemmThreads / 64>();
+  constexpr size_t gemm = V == 2 ? sizeof(u32x4_t) * 2 * 2 * kPfSlots : sizeof(f32x4_t) * 3 * 4 * (V + 1) * 64;
+  return perm > gemm ? perm : gemm;
+}
+
+template <int DT, int V>
 __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
+  constexpr int NT = V == 2 ? 1 : V + 1;  // decode items: token sub-tiles of 16
+  constexpr int MT = V == 2 ? kPfRows : 16 * NT;
   __shared__ int cum[1025];
   __shared__ int wsum[4];
-  __shared__ f32x4_t red[3][4 * NT][64];
+  __shared__ __align__(16) unsigned char smem[fused_lds_bytes<V>()];
   const unsigned G = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const long long gtid = (long long)blockIdx.x * kGemmThreads + tid, gstride = (long long)G * kGemmThreads;
@@ -89,31 +103,46 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   grid_barrier(a.sync, G);
 
   // 2. permutation
-  if (blockIdx.x == 0) permute_block<kGemmThreads / 64>(a.ids, a.T * a.k, a.E, a.offsets, a.sorted_pairs, a.pair_pos);
+  if (blockIdx.x == 0) {
+    int* lds = reinterpret_cast<int*>(smem);
+    permute_block<kGemmThreads / 64>(a.ids, a.T * a.k, a.E, a.offsets, a.sorted_pairs, a.pair_pos,
+                                     reinterpret_cast<int(*)[1024]>(lds), lds + (kGemmThreads / 64) * 1024);
+  }
   grid_barrier(a.sync, 2 * G);
 
   // 3. the two grouped GEMMs
-  const int total_mt = build_schedule(a.offsets, a.E, 16 * NT, cum, wsum);
-  const long long n13 = (long long)total_mt * a.g13.G, n2 = (long long)total_mt * a.g2.G;
+  // items per m-tile: one per 64-row weight group (decode) or per pair of groups (prefill)
+  const int per13 = V == 2 ? a.g13.G / 2 : a.g13.G, per2 = V == 2 ? a.g2.G / 2 : a.g2.G;
+  auto item = [&](const GemmArgs& g, bool g13, long long w) -> int {
+    if constexpr (V == 2) {
+      auto* lds = reinterpret_cast<u32x4_t(*)[2][kPfSlots]>(smem);
+      return g13 ? prefill_item<DT, true>(g, w, cum, lds) : prefill_item<DT, false>(g, w, cum, lds);
+    } else {
+      auto* red = reinterpret_cast<f32x4_t(*)[4 * NT][64]>(smem);
+      return g13 ? gemm_item<DT, NT, true>(g, w, cum, red) : gemm_item<DT, NT, false>(g, w, cum, red);
+    }
+  };
+  const int total_mt = build_schedule(a.offsets, a.E, MT, cum, wsum);
+  const long long n13 = (long long)total_mt * per13, n2 = (long long)total_mt * per2;
   if constexpr (MOE_FUSED_GEMM_BARRIER) {
-    for (long long w = blockIdx.x; w < n13; w += G) gemm_item<DT, NT, true>(a.g13, w, cum, red);
+    for (long long w = blockIdx.x; w < n13; w += G) item(a.g13, true, w);
     grid_barrier(a.sync, 3 * G);
-    for (long long w = blockIdx.x; w < n2; w += G) gemm_item<DT, NT, false>(a.g2, w, cum, red);
+    for (long long w = blockIdx.x; w < n2; w += G) item(a.g2, false, w);
     grid_barrier(a.sync, 4 * G);
   } else {
-  for (long long w = blockIdx.x; w < n13 + n2; w += G) {
-    if (w < n13) {
-      const int e = gemm_item<DT, NT, true>(a.g13, w, cum, red);
-      if (tid == 0) __hip_atomic_fetch_add(&done13[e], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const long long w2 = w - n13;
-      const int e = find_expert(cum, a.E, (int)(w2 / a.g2.G));
-      if (tid == 0) spin_until_geq(&done13[e], (unsigned)((cum[e + 1] - cum[e]) * a.g13.G), &a.sync[2]);
-      __syncthreads();
-      gemm_item<DT, NT, false>(a.g2, w2, cum, red);
+    for (long long w = blockIdx.x; w < n13 + n2; w += G) {
+      if (w < n13) {
+        const int e = item(a.g13, true, w);
+        if (tid == 0) __hip_atomic_fetch_add(&done13[e], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        const long long w2 = w - n13;
+        const int e = find_expert(cum, a.E, (int)(w2 / per2));
+        if (tid == 0) spin_until_geq(&done13[e], (unsigned)((cum[e + 1] - cum[e]) * per13), &a.sync[2]);
+        __syncthreads();
+        item(a.g2, false, w2);
+      }
     }
-  }
-  grid_barrier(a.sync, 3 * G);
+    grid_barrier(a.sync, 3 * G);
   }
 
   // 4. combine
@@ -135,20 +164,22 @@ __global__ void zero_u32_kernel(unsigned* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
 }
 
-template <int DT, int NT>
-static const void* fused_fn() {
-  return reinterpret_cast<const void*>(fused_kernel<DT, NT>);
+template <int DT>
+static const void* fused_fn(int v) {
+  if (v == 0) return reinterpret_cast<const void*>(fused_kernel<DT, 0>);
+  if (v == 1) return reinterpret_cast<const void*>(fused_kernel<DT, 1>);
+  return reinterpret_cast<const void*>(fused_kernel<DT, 2>);
 }
 
-static const void* fused_ptr(int dt, int nt) {
-  if (dt == DT_BF16) return nt == 1 ? fused_fn<DT_BF16, 1>() : fused_fn<DT_BF16, 2>();
-  if (dt == DT_MXFP8) return nt == 1 ? fused_fn<DT_MXFP8, 1>() : fused_fn<DT_MXFP8, 2>();
-  return nt == 1 ? fused_fn<DT_NVFP4, 1>() : fused_fn<DT_NVFP4, 2>();
+static const void* fused_ptr(int dt, int v) {
+  if (dt == DT_BF16) return fused_fn<DT_BF16>(v);
+  if (dt == DT_MXFP8) return fused_fn<DT_MXFP8>(v);
+  return fused_fn<DT_NVFP4>(v);
 }
 
-int fused_blocks_per_cu(int dt, int nt) {
+int fused_blocks_per_cu(int dt, int v) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_ptr(dt, nt), kGemmThreads, 0) != hipSuccess || n < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_ptr(dt, v), kGemmThreads, 0) != hipSuccess || n < 1)
     return 0;
   return n;
 }
@@ -204,7 +235,8 @@ hipError_t launch_fused(int dt, int E, int H, int I, int k, int T, const uint8_t
   h.E = E; h.K = I; h.G = L.G2; h.KG = L.KG2; h.k = k; h.n_out = H;
   (void)ws_bytes;
   void* args[] = {&f};
-  return hipLaunchCooperativeKernel(fused_ptr(dt, gemm_nt(T, k, E)), dim3(grid), dim3(kGemmThreads), args, 0, s);
+  return hipLaunchCooperativeKernel(fused_ptr(dt, gemm_variant(T, k, E)), dim3(grid), dim3(kGemmThreads), args, 0,
+                                    s);
 }
 
 hipError_t launch_zero_sync(uint8_t* ws, int dt, int E, int H, int I, int k, int max_tokens, hipStream_t s) {

@@ -132,6 +132,7 @@ hipError_t launch_gemm13(int dt, int E, int H, int I, int k, int T, const uint8_
   a.out_scales = hq + act_scale_offset(dt, T * k, I);
   a.out_deq = reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
   a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
+  if (gemm_prefill(T, k, E)) return launch_prefill(dt, true, a, grid, s);
   return dispatch_gemm<true>(dt, gemm_nt(T, k, E), a, grid, s);
 }
 
@@ -149,6 +150,7 @@ hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t
   a.out_scales = nullptr;
   a.out_deq = nullptr;
   a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
+  if (gemm_prefill(T, k, E)) return launch_prefill(dt, false, a, grid, s);
   return dispatch_gemm<false>(dt, gemm_nt(T, k, E), a, grid, s);
 }
 

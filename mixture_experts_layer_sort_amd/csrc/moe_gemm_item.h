@@ -227,6 +227,107 @@ struct StepK {
   static constexpr int U = DT == DT_BF16 ? MOE_GEMM_U_BF16 : (DT == DT_MXFP8 ? MOE_GEMM_U_MXFP8 : MOE_GEMM_U_NVFP4);
 };
 
+// Epilogue of one wave's accumulators acc[4 tiles][NT token sub-tiles] for
+// sorted rows r0 + 16s + (lane % 16) (valid below r_end) and weight row group
+// g of expert e.  Gate/up GEMM: tiles 0,1 = gate rows 32g + 16tp + 4q + j,
+// tiles 2,3 = the matching up rows; h = silu(g) * u is requantised into hq
+// (codes, scales, exact 16-bit copy).  Down GEMM: y rows at the pair index.
+template <int DT, int NT, bool G13>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[4][NT], int r0, int r_end, int g,
+                                              int e, int lane) {
+  const int i16 = lane & 15, q = lane >> 4;
+  const float alpha = DT == DT_NVFP4 ? a.walpha[e] : 1.f;
+#pragma unroll
+  for (int s = 0; s < NT; ++s) {
+    const int r = r0 + 16 * s + i16;
+    const bool ok = r < r_end;
+    if constexpr (G13) {
+      // tiles 0,1 = gate rows 32g + 16tp + 4q + j; tiles 2,3 = the matching up rows
+      float h[2][4];
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float gv = acc[tp][s][j] * alpha, uv = acc[2 + tp][s][j] * alpha;
+          h[tp][j] = gv / (1.0f + expf(-gv)) * uv;
+        }
+      const int I = a.n_out;
+      if constexpr (DT == DT_BF16) {
+        if (ok) {
+          uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * g + 4 * q;
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp) {
+            uint2 v;
+            v.x = f32_to_bf16(h[tp][0]) | ((uint32_t)f32_to_bf16(h[tp][1]) << 16);
+            v.y = f32_to_bf16(h[tp][2]) | ((uint32_t)f32_to_bf16(h[tp][3]) << 16);
+            *reinterpret_cast<uint2*>(o + 16 * tp) = v;
+          }
+        }
+      } else if constexpr (DT == DT_MXFP8) {
+        // one block of 32 along I: [32g, 32g+32), spread over the 4 lanes sharing i16
+        float amax = 0.f;
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(h[tp][j]));
+        amax = wave_max_xor(amax, 16, 32);
+        const int sx = mx_scale_exp(amax);
+        if (ok) {
+          uint8_t* o = a.out + (size_t)r * I + 32 * g + 4 * q;
+          uint16_t* od = a.out_deq + (size_t)r * I + 32 * g + 4 * q;
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp) {
+            uint32_t v = 0, d[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t c = e4m3_from_f32(ldexpf(h[tp][j], -sx));
+              v |= c << (8 * j);
+              d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), sx)) >> 16;  // exact in bf16
+            }
+            *reinterpret_cast<uint32_t*>(o + 16 * tp) = v;
+            *reinterpret_cast<uint2*>(od + 16 * tp) = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+          }
+          if (q == 0) a.out_scales[(size_t)r * (I / 32) + g] = (uint8_t)(sx + 127);
+        }
+      } else {
+        // two blocks of 16 along I: [32g + 16tp, +16)
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          float amax = fmaxf(fmaxf(fabsf(h[tp][0]), fabsf(h[tp][1])), fmaxf(fabsf(h[tp][2]), fabsf(h[tp][3])));
+          amax = wave_max_xor(amax, 16, 32);
+          const uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
+          const float sc = e4m3_to_f32(sc_code);
+          uint32_t v = 0, d[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint32_t c = sc > 0.f ? e2m1_from_f32(h[tp][j], sc) : ((__float_as_uint(h[tp][j]) >> 28) & 8u);
+            v |= c << (4 * j);
+            d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
+          }
+          if (ok) {
+            *reinterpret_cast<uint16_t*>(a.out + (size_t)r * (I / 2) + 16 * g + 8 * tp + 2 * q) = (uint16_t)v;
+            if (q == 0) a.out_scales[(size_t)r * (I / 16) + 2 * g + tp] = (uint8_t)sc_code;
+            *reinterpret_cast<uint2*>(a.out_deq + (size_t)r * I + 32 * g + 16 * tp + 4 * q) =
+                make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+          }
+        }
+      }
+    } else {
+      if (ok) {
+        const int p = a.sorted_pairs[r];
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)p * a.n_out + 64 * g + 4 * q;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          uint2 v;
+          v.x = f32_to_bf16(acc[t][s][0] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][1] * alpha) << 16);
+          v.y = f32_to_bf16(acc[t][s][2] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][3] * alpha) << 16);
+          *reinterpret_cast<uint2*>(o + 16 * t) = v;
+        }
+      }
+    }
+  }
+}
+
 // One work item (expert, m-tile, 64-row weight group) of a grouped GEMM:
 // the four waves stream their K slices into MFMAs, reduce through LDS, and
 // wave 0 runs the epilogue (SwiGLU + requantisation for the gate/up GEMM,
@@ -306,99 +407,12 @@ __device__ __forceinline__ int gemm_item(const GemmArgs& a, long long w, const i
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int s = 0; s < NT; ++s) acc[t][s] += red[0][t * NT + s][lane] + red[1][t * NT + s][lane] + red[2][t * NT + s][lane];
-    const float alpha = DT == DT_NVFP4 ? a.walpha[e] : 1.f;
-#pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      const int r = r0 + 16 * s + i16;
-      const bool ok = r < r_end;
-      if constexpr (G13) {
-        // tiles 0,1 = gate rows 32g + 16tp + 4q + j; tiles 2,3 = the matching up rows
-        float h[2][4];
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float gv = acc[tp][s][j] * alpha, uv = acc[2 + tp][s][j] * alpha;
-            h[tp][j] = gv / (1.0f + expf(-gv)) * uv;
-          }
-        const int I = a.n_out;
-        if constexpr (DT == DT_BF16) {
-          if (ok) {
-            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * g + 4 * q;
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-              uint2 v;
-              v.x = f32_to_bf16(h[tp][0]) | ((uint32_t)f32_to_bf16(h[tp][1]) << 16);
-              v.y = f32_to_bf16(h[tp][2]) | ((uint32_t)f32_to_bf16(h[tp][3]) << 16);
-              *reinterpret_cast<uint2*>(o + 16 * tp) = v;
-            }
-          }
-        } else if constexpr (DT == DT_MXFP8) {
-          // one block of 32 along I: [32g, 32g+32), spread over the 4 lanes sharing i16
-          float amax = 0.f;
-#pragma unroll
-          for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(h[tp][j]));
-          amax = wave_max_xor(amax, 16, 32);
-          const int sx = mx_scale_exp(amax);
-          if (ok) {
-            uint8_t* o = a.out + (size_t)r * I + 32 * g + 4 * q;
-            uint16_t* od = a.out_deq + (size_t)r * I + 32 * g + 4 * q;
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-              uint32_t v = 0, d[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const uint32_t c = e4m3_from_f32(ldexpf(h[tp][j], -sx));
-                v |= c << (8 * j);
-                d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), sx)) >> 16;  // exact in bf16
-              }
-              *reinterpret_cast<uint32_t*>(o + 16 * tp) = v;
-              *reinterpret_cast<uint2*>(od + 16 * tp) = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
-            }
-            if (q == 0) a.out_scales[(size_t)r * (I / 32) + g] = (uint8_t)(sx + 127);
-          }
-        } else {
-          // two blocks of 16 along I: [32g + 16tp, +16)
-#pragma unroll
-          for (int tp = 0; tp < 2; ++tp) {
-            float amax = fmaxf(fmaxf(fabsf(h[tp][0]), fabsf(h[tp][1])), fmaxf(fabsf(h[tp][2]), fabsf(h[tp][3])));
-            amax = wave_max_xor(amax, 16, 32);
-            const uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
-            const float sc = e4m3_to_f32(sc_code);
-            uint32_t v = 0, d[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              uint32_t c = sc > 0.f ? e2m1_from_f32(h[tp][j], sc) : ((__float_as_uint(h[tp][j]) >> 28) & 8u);
-              v |= c << (4 * j);
-              d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
-            }
-            if (ok) {
-              *reinterpret_cast<uint16_t*>(a.out + (size_t)r * (I / 2) + 16 * g + 8 * tp + 2 * q) = (uint16_t)v;
-              if (q == 0) a.out_scales[(size_t)r * (I / 16) + 2 * g + tp] = (uint8_t)sc_code;
-              *reinterpret_cast<uint2*>(a.out_deq + (size_t)r * I + 32 * g + 16 * tp + 4 * q) =
-                  make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
-            }
-          }
-        }
-      } else {
-        if (ok) {
-          const int p = a.sorted_pairs[r];
-          uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)p * a.n_out + 64 * g + 4 * q;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            uint2 v;
-            v.x = f32_to_bf16(acc[t][s][0] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][1] * alpha) << 16);
-            v.y = f32_to_bf16(acc[t][s][2] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][3] * alpha) << 16);
-            *reinterpret_cast<uint2*>(o + 16 * t) = v;
-          }
-        }
-      }
-    }
+    gemm_epilogue<DT, NT, G13>(a, acc, r0, r_end, g, e, lane);
   }
   __syncthreads();
   return e;
 }
+
+hipError_t launch_prefill(int dt, bool g13, const GemmArgs& a, int grid, hipStream_t s);
 
 }  // namespace moe

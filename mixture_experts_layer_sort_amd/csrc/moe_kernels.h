@@ -33,16 +33,22 @@ hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* w
 // Blocks of the GEMM kernels that fit on one compute unit at once.
 int gemm_blocks_per_cu(int dt, bool gemm13, int nt);
 
-// Token sub-tiles (of 16) per GEMM work item: 1 while experts see about 16
-// routed rows or fewer on average, else 2.
+// Token sub-tiles (of 16) per decode GEMM work item: 1 while experts see
+// about 16 routed rows or fewer on average, else 2.
 inline int gemm_nt(int T, int k, int E) { return (long long)T * k > 16LL * E ? 2 : 1; }
+// The prefill-shaped GEMM (LDS-staged, 128-row tiles) once experts see 64 or
+// more routed rows on average.
+inline bool gemm_prefill(int T, int k, int E) { return (long long)T * k >= 64LL * E; }
+// GEMM variant index for caches: 0 decode NT=1, 1 decode NT=2, 2 prefill.
+inline int gemm_variant(int T, int k, int E) { return gemm_prefill(T, k, E) ? 2 : gemm_nt(T, k, E) - 1; }
+int prefill_blocks_per_cu(int dt, bool g13);
 
 // The whole layer in one cooperative launch; `grid` must not exceed the
 // co-resident capacity (fused_blocks_per_cu * compute units).
 hipError_t launch_fused(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const float* logits,
                         const uint16_t* x, uint16_t* out, int* ids, float* wts, uint8_t* ws, size_t ws_bytes,
                         int max_tokens, int grid, hipStream_t s);
-int fused_blocks_per_cu(int dt, int nt);
+int fused_blocks_per_cu(int dt, int variant);  // variant as gemm_variant
 // Zero the workspace's synchronisation words.
 hipError_t launch_zero_sync(uint8_t* ws, int dt, int E, int H, int I, int k, int max_tokens, hipStream_t s);
 

@@ -66,13 +66,16 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
 // the NWAVES waves owns a contiguous segment of pairs; pass 1 builds per-wave
 // expert histograms in LDS, a scan turns them into per-(wave, expert) start
 // positions, pass 2 walks each segment in order and ranks pairs of equal
-// expert inside a 64-pair step with ballots on the id bits.
+// expert inside a 64-pair step with ballots on the id bits.  `hist` and
+// `scan_tmp` are LDS of NWAVES*1024 and 64*NWAVES ints.
+template <int NWAVES>
+constexpr int permute_lds_ints() { return NWAVES * 1024 + 64 * NWAVES; }
+
 template <int NWAVES>
 __device__ void permute_block(const int* __restrict__ ids, int P, int E, int* __restrict__ offsets,
-                              int* __restrict__ sorted_pairs, int* __restrict__ pair_pos) {
+                              int* __restrict__ sorted_pairs, int* __restrict__ pair_pos, int (*hist)[1024],
+                              int* scan_tmp) {
   constexpr int kPermWaves = NWAVES, kPermThreads = 64 * NWAVES, kPer = 1024 / kPermThreads;
-  __shared__ int hist[kPermWaves][1024];
-  __shared__ int scan_tmp[kPermThreads];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int i = tid; i < kPermWaves * 1024; i += kPermThreads) (&hist[0][0])[i] = 0;
   __syncthreads();
@@ -136,6 +139,15 @@ __device__ void permute_block(const int* __restrict__ ids, int P, int E, int* __
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// The same with its own static LDS.
+template <int NWAVES>
+__device__ void permute_block(const int* __restrict__ ids, int P, int E, int* __restrict__ offsets,
+                              int* __restrict__ sorted_pairs, int* __restrict__ pair_pos) {
+  __shared__ int hist[NWAVES][1024];
+  __shared__ int scan_tmp[64 * NWAVES];
+  permute_block<NWAVES>(ids, P, E, offsets, sorted_pairs, pair_pos, hist, scan_tmp);
 }
 
 template <int DT>

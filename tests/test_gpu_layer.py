@@ -24,6 +24,11 @@ SMALL = {
     "mxfp8_prefill_small": W["mxfp8_prefill"].scaled(T=300, H=512, I=256, E=16, k=4),
     "nvfp4_prefill_small": W["nvfp4_decode_t128"].scaled(T=96, H=384, I=128, E=8, k=3),
     "bf16_prefill_small": W["bf16_decode"].scaled(T=150, H=256, I=256, E=6, k=2),
+    # >= 64 routed rows per expert on average: the LDS-staged prefill GEMM
+    # (128-row m-tiles with ragged tails, several n-tiles and K steps)
+    "bf16_prefill_tiles": W["bf16_decode"].scaled(T=300, H=384, I=256, E=4, k=2),
+    "nvfp4_prefill_tiles": W["nvfp4_decode_t128"].scaled(T=200, H=384, I=128, E=4, k=2),
+    "mxfp8_prefill_skewed": W["mxfp8_prefill"].scaled(T=520, H=256, I=384, E=8, k=2),
     "bf16_singleton": W["tiny_bf16"].scaled(E=1, k=1, T=5),
     "mxfp8_singleton": W["mxfp8_decode"].scaled(E=1, k=1, T=7, H=256, I=128),
     "nvfp4_singleton": W["nvfp4_decode_t8"].scaled(E=1, k=1, T=3, H=256, I=128),
