@@ -75,13 +75,13 @@ __device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned target) {
 }
 
 // LDS of one block, reused phase by phase: the permutation's histograms, then
-// the GEMM items' cross-wave reduction (decode items) or operand stages
-// (prefill items).  V is the GEMM variant: 0 / 1 decode items of 16 / 32
-// rows, 2 prefill items.
+// the decode items' cross-wave reduction.  (Prefill items keep their token
+// stages in LDS objects of their own.)  V is the GEMM variant: 0 / 1 decode
+// items of 16 / 32 rows, 2 prefill items.
 template <int V>
 constexpr size_t fused_lds_bytes() {
   constexpr size_t perm = sizeof(int) * permute_lds_ints<kGemmThreads / 64>();
-  constexpr size_t gemm = V == 2 ? sizeof(u32x4_t) * 2 * 2 * kPfSlots : sizeof(f32x4_t) * 3 * 4 * (V + 1) * 64;
+  constexpr size_t gemm = V == 2 ? 0 : sizeof(f32x4_t) * 3 * 4 * (V + 1) * 64;
   return perm > gemm ? perm : gemm;
 }
 
@@ -111,12 +111,15 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   grid_barrier(a.sync, 2 * G);
 
   // 3. the two grouped GEMMs
-  // items per m-tile: one per 64-row weight group (decode) or per pair of groups (prefill)
-  const int per13 = V == 2 ? a.g13.G / 2 : a.g13.G, per2 = V == 2 ? a.g2.G / 2 : a.g2.G;
+  // items per m-tile: one per 64-row weight group (decode) or per 4 groups (prefill)
+  const int per13 = V == 2 ? (a.g13.G + kPfGroups - 1) / kPfGroups : a.g13.G;
+  const int per2 = V == 2 ? (a.g2.G + kPfGroups - 1) / kPfGroups : a.g2.G;
   auto item = [&](const GemmArgs& g, bool g13, long long w) -> int {
     if constexpr (V == 2) {
-      auto* lds = reinterpret_cast<u32x4_t(*)[2][kPfSlots]>(smem);
-      return g13 ? prefill_item<DT, true>(g, w, cum, lds) : prefill_item<DT, false>(g, w, cum, lds);
+      __shared__ u32x4_t s0[kPfStageSlots], s1[kPfStageSlots], s2[kPfStageSlots], s3[kPfStageSlots];
+      static_assert(kPfStages == 4, "stage objects");
+      const PfStages st{{&s0, &s1, &s2, &s3}};
+      return g13 ? prefill_item<DT, true>(g, w, cum, st) : prefill_item<DT, false>(g, w, cum, st);
     } else {
       auto* red = reinterpret_cast<f32x4_t(*)[4 * NT][64]>(smem);
       return g13 ? gemm_item<DT, NT, true>(g, w, cum, red) : gemm_item<DT, NT, false>(g, w, cum, red);
@@ -124,13 +127,14 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   };
   const int total_mt = build_schedule(a.offsets, a.E, MT, cum, wsum);
   const long long n13 = (long long)total_mt * per13, n2 = (long long)total_mt * per2;
+  const int lb = V == 2 ? xcd_logical_block() : (int)blockIdx.x;
   if constexpr (MOE_FUSED_GEMM_BARRIER) {
-    for (long long w = blockIdx.x; w < n13; w += G) item(a.g13, true, w);
+    for (long long w = lb; w < n13; w += G) item(a.g13, true, w);
     grid_barrier(a.sync, 3 * G);
-    for (long long w = blockIdx.x; w < n2; w += G) item(a.g2, false, w);
+    for (long long w = lb; w < n2; w += G) item(a.g2, false, w);
     grid_barrier(a.sync, 4 * G);
   } else {
-    for (long long w = blockIdx.x; w < n13 + n2; w += G) {
+    for (long long w = lb; w < n13 + n2; w += G) {
       if (w < n13) {
         const int e = item(a.g13, true, w);
         if (tid == 0) __hip_atomic_fetch_add(&done13[e], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);

@@ -1,21 +1,10 @@
 // Prefill-shaped grouped GEMMs: many routed rows per expert, so weight tiles
-// are reused across tokens through LDS instead of being streamed once.
-//
-// Work item = (expert, 128-row m-tile of its sorted rows, n-tile of two
-// weight row groups = 128 weight rows).  Items are numbered expert-major,
-// then n-tile, with the m-tile fastest, so consecutive items (and blocks)
-// share the same weight tiles in L2 / the Infinity Cache.  The grid is
-// persistent and derives the item map from `offsets` on the device.
-//
-// A block of 4 waves computes the 128 x 128 item as a 2 x 2 grid of 64 x 64
-// wave tiles (16 MFMAs of 16x16x32 per 32-wide K chunk).  K advances in steps
-// of 64 through two LDS buffers: while the waves compute step s from one
-// buffer, every thread already holds step s+1's global data in registers and
-// writes it (converted to bf16 / fp16) into the other buffer afterwards; one
-// barrier per step.  Both operands sit in LDS in the matrix instruction's
-// per-lane order (the packed weight layout is already in that order), so each
-// lane's fragment is one conflict-free 16-byte LDS read.  The epilogue (SwiGLU
-// + requantisation, or y rows) is the decode kernel's.
+// are reused across tokens instead of being streamed once.  The work item
+// (256 weight rows x 128 routed rows, weights streamed into registers,
+// tokens through a 3-stage direct-to-LDS ring) is in moe_prefill_item.h.
+// The grid is persistent, derives the item map from `offsets` on the device
+// and walks items in XCD-contiguous order.  The epilogue (SwiGLU +
+// requantisation, or y rows) is the decode kernel's.
 #include "moe_prefill_item.h"
 
 namespace moe {
@@ -24,10 +13,12 @@ template <int DT, bool G13>
 __global__ __launch_bounds__(kGemmThreads) void gemm_prefill_kernel(GemmArgs a) {
   __shared__ int cum[1025];
   __shared__ int wsum[4];
-  __shared__ u32x4_t lds[2][2][kPfSlots];  // [buffer][A weights / B tokens][slot]
+  __shared__ u32x4_t s0[kPfStageSlots], s1[kPfStageSlots], s2[kPfStageSlots], s3[kPfStageSlots];
+  static_assert(kPfStages == 4, "stage objects");
+  const PfStages st{{&s0, &s1, &s2, &s3}};
   const int total_mt = build_schedule(a.offsets, a.E, kPfRows, cum, wsum);
-  const long long total = (long long)total_mt * (a.G / 2);
-  for (long long w = blockIdx.x; w < total; w += gridDim.x) prefill_item<DT, G13>(a, w, cum, lds);
+  const long long total = (long long)total_mt * ((a.G + kPfGroups - 1) / kPfGroups);
+  for (long long w = xcd_logical_block(); w < total; w += gridDim.x) prefill_item<DT, G13>(a, w, cum, st);
 }
 
 template <int DT, bool G13>

@@ -1,159 +1,248 @@
 // The prefill-shaped grouped-GEMM work item, shared by the stage kernel
 // (moe_prefill.hip) and the fused single-launch kernel.
+//
+// Item = (expert, m-tile of 128 sorted rows, n-block of 4 weight row groups
+// = 256 weight rows).  The block's 4 waves each own one row group (its 4
+// packed 16-row tiles) and all 128 token rows: a 64 x 128 wave tile of
+// 16x16x32 MFMAs, accumulated over K in order.
+//
+//  * Weights stream from global memory straight into registers (each weight
+//    element is used by exactly one wave): a ring of kPfStages K steps.
+//  * Token rows are shared by the 4 waves through LDS, filled by the 16-byte
+//    direct global->LDS load (no register round trip) into a ring of
+//    kPfStages stages, each one 64-wide K step in the matrix instruction's
+//    lane order.
+//  * One barrier per K step.  Loads for step s+kPfStages-1 are issued when
+//    step s starts, so kPfStages-1 steps of MFMA work cover their latency;
+//    the wait before the barrier counts outstanding vector-memory operations
+//    explicitly.
 #pragma once
 
 #include "moe_gemm_item.h"
 
 namespace moe {
 
-constexpr int kPfRows = 128;          // routed rows per item
-constexpr int kPfSlots = 8 * 2 * 64;  // 16-byte slots per operand per stage: [8 tiles][2 chunks][64 lanes]
+constexpr int kPfRows = 128;                  // routed rows per item: 8 sub-tiles of 16
+constexpr int kPfGroups = 4;                  // weight row groups per item, one per wave
+constexpr int kPfBand = 8;                    // m-tiles per band of the item order
+constexpr int kPfStageSlots = 8 * 2 * 64;     // token stage: [sub-tile][chunk][lane] x 16 B = 16 KB
+constexpr int kPfStepOps = 12;                // vector-memory operations per wave per K step
+constexpr int kPfStages = 4;                  // pipeline depth: K steps in flight + the one computed
 
-// Staging registers and LDS slots use plain vector types: copies of HIP's
-// uint4 (a struct) keep the staging registers in private memory.
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
-// Global data of one K step held in registers between the load and the LDS store.
+// One K step (64 wide) of this wave's 4 weight tiles, as loaded.
 template <int DT>
-struct PfRegs {
-  u32x4_t a[DT == DT_BF16 ? 4 : 2];  // BF16: 4 slots of 16 B; MXFP8: 2 lane-slots of 16 fp8; NVFP4: 2 x 8 B in [0], [1]
-  uint32_t as[2][DT == DT_NVFP4 ? 2 : 1];
-  u32x4_t b[4];
+struct PfA;
+template <>
+struct PfA<DT_BF16> {
+  u32x4_t c[4][2];  // [tile][chunk]: 8 bf16 per lane
+};
+template <>
+struct PfA<DT_MXFP8> {
+  u32x4_t c[4];   // [tile]: chunk 0 in words 0-1, chunk 1 in words 2-3 (8 e4m3 each)
+  uint32_t s[4];  // [tile]: the row's 4 e8m0 scales of the kgroup
+};
+template <>
+struct PfA<DT_NVFP4> {
+  u32x2_t c[4];   // [tile]: 8 e2m1 of chunk 0, of chunk 1
+  uint32_t s[4];  // [tile]: the row's 4 e4m3 scales of this half kgroup
 };
 
-// One prefill work item (see the kernel file for the decomposition).  `w`
-// numbers items expert-major, then n-tile, m-tile fastest; `cum` holds the
-// per-expert 128-row m-tile prefix from build_schedule.  `lds` is the block's
-// two-stage operand buffer.  Returns the item's expert; ends with the block's
-// LDS free for reuse.
+// Blocks are dealt to the 8 XCDs (each with its own L2) round-robin by
+// block index.  Renumbering so that each XCD holds a contiguous range of
+// logical ids makes neighbouring items -- which share weight or token tiles
+// -- run on the same L2.
+__device__ __forceinline__ int xcd_logical_block() {
+  const int b = blockIdx.x, g = gridDim.x;
+  return g % 8 == 0 ? (b % 8) * (g / 8) + b / 8 : b;
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and all its LDS reads are done, then barrier.  No fence: the
+// direct-to-LDS loads of later stages stay in flight across it.
+template <int N>
+__device__ __forceinline__ void pf_wait_barrier() {
+  static_assert(N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Keep the uses of a K step's weight registers below the barrier that
+// follows their wait (otherwise the register-only conversions are hoisted
+// above it and the compiler inserts a full wait of its own).
+template <int DT>
+__device__ __forceinline__ void pf_pin(PfA<DT>& A) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (DT == DT_BF16) {
+      asm volatile("" : "+v"(A.c[t][0]), "+v"(A.c[t][1]));
+    } else {
+      asm volatile("" : "+v"(A.c[t]), "+v"(A.s[t]));
+    }
+  }
+}
+
+// The token stages of one block (separate LDS objects, so the compiler's
+// waits for the direct loads track each stage on its own).
+struct PfStages {
+  u32x4_t (*s[kPfStages])[kPfStageSlots];
+};
+
+// One prefill work item.  `w` numbers items expert-major; within an expert,
+// bands of up to kPfBand m-tiles, n-block-major inside a band, so kPfBand^2
+// consecutive items form a square of weight x token tiles.  `cum` holds the
+// per-expert 128-row m-tile prefix from build_schedule.  Returns the item's
+// expert; ends with every load landed and the block's LDS free for reuse.
 template <int DT, bool G13>
-__device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, const int* cum,
-                                            u32x4_t (*lds)[2][kPfSlots]) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
-  const int NB = a.G / 2;  // n-tiles of two row groups (G is even for supported shapes)
+__device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, const int* cum, const PfStages& st) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, i16 = lane & 15, q = lane >> 4;
+  const int NB = (a.G + kPfGroups - 1) / kPfGroups;
   const int KS = a.KG * 2;  // K steps of 64
-  const size_t tcode = tile_code_bytes(DT), tscale = tile_scale_bytes(DT);
   const int e = find_expert(cum, a.E, (int)(w / NB));
   const int mts = cum[e + 1] - cum[e];
   const long long local = w - (long long)cum[e] * NB;
-  const int nt = (int)(local / mts), mt = (int)(local % mts);
+  const int band = (int)(local / (kPfBand * NB)), full = mts / kPfBand;
+  const int bsize = band < full ? kPfBand : mts - full * kPfBand;
+  const int inner = (int)(local - (long long)band * kPfBand * NB);
+  const int nb = inner / bsize, mt = band * kPfBand + inner % bsize;
   const int r0 = a.offsets[e] + mt * kPfRows, r_end = a.offsets[e + 1];
+  // this wave's row group; a group past the end (G not a multiple of 4) reads group G-1 and discards it
+  const int g = kPfGroups * nb + wv, gl = min(g, a.G - 1);
 
-  // B slots of this thread: slot = tid + 256 i -> subtile s, chunk c, lane (j, q)
-  int brow[4];
+  // token rows of the two sub-tiles this wave loads (2wv, 2wv+1); rows past
+  // the expert's end load its last row, whose results are discarded
+  const uint8_t* bsrc[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int slot = tid + 256 * i, s = slot >> 7, l = slot & 63;
-    const int r = r0 + 16 * s + (l & 15);
-    brow[i] = r < r_end ? (G13 ? a.sorted_pairs[r] / a.k : r) : -1;
+  for (int j = 0; j < 2; ++j) {
+    const int r = min(r0 + 16 * (2 * wv + j) + i16, r_end - 1);
+    const int row = G13 ? a.sorted_pairs[r] / a.k : r;
+    bsrc[j] = a.act + ((size_t)row * a.K + 8 * q) * 2;
   }
-  // weight tile of slot-tile t (0..7): row group 2*nt + t/4, tile t%4
-  auto tile_index = [&](int t, int kg) -> size_t {
-    return ((size_t)(e * a.G + 2 * nt + (t >> 2)) * a.KG + kg) * 4 + (t & 3);
-  };
-
-  auto gload = [&](PfRegs<DT>& R, int step) {
-    const int kg = step >> 1, h = step & 1;
+  const size_t tile0 = (size_t)(e * a.G + gl) * a.KG * 4;  // tile index of (gl, kgroup 0, tile 0)
+  // Vector-memory operation k (0..11) of K step `step`: k < 4 the token
+  // rows of sub-tile 2wv + k/2, chunk k%2 into `stage`; k >= 4 a piece of
+  // weight tile (k-4)/2 into A.
+  auto issue_op = [&](int k, u32x4_t(&stage)[kPfStageSlots], PfA<DT>& A, int step) {
+    if (k < 4) {
+      const int j = k >> 1, c = k & 1;
+      __builtin_amdgcn_global_load_lds(bsrc[j] + step * 128 + c * 64, &stage[((2 * wv + j) * 2 + c) * 64], 16, 0, 0);
+      return;
+    }
+    const int t = (k - 4) >> 1, part = (k - 4) & 1, kg = step >> 1, h = step & 1;
+    const size_t ti = tile0 + (size_t)kg * 4 + t;
     if constexpr (DT == DT_BF16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int slot = tid + 256 * i, t = slot >> 7, within = slot & 127;
-        R.a[i] = *reinterpret_cast<const u32x4_t*>(a.wcodes + tile_index(t, kg) * tcode + h * 2048 + within * 16);
-      }
+      A.c[t][part] = *reinterpret_cast<const u32x4_t*>(a.wcodes + ti * 4096 + (2 * h + part) * 1024 + lane * 16);
+    } else if constexpr (DT == DT_MXFP8) {
+      if (part == 0) A.c[t] = *reinterpret_cast<const u32x4_t*>(a.wcodes + ti * 2048 + h * 1024 + lane * 16);
+      else A.s[t] = *reinterpret_cast<const uint32_t*>(a.wscales + ti * 64 + i16 * 4);
     } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int slot = tid + 256 * i, t = slot >> 6, l = slot & 63;
-        const size_t ti = tile_index(t, kg);
-        if constexpr (DT == DT_MXFP8) {
-          R.a[i] = *reinterpret_cast<const u32x4_t*>(a.wcodes + ti * tcode + h * 1024 + l * 16);
-          R.as[i][0] = *reinterpret_cast<const uint32_t*>(a.wscales + ti * tscale + (l & 15) * 4);
-        } else {
-          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(a.wcodes + ti * tcode + l * 16 + 8 * h);
-          R.a[i] = u32x4_t{v[0], v[1], 0u, 0u};
-          const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(a.wscales + ti * tscale + (l & 15) * 8);
-          R.as[i][0] = sv[0];
-          R.as[i][1] = sv[1];
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = tid + 256 * i, c = (slot >> 6) & 1, q = (slot & 63) >> 4;
-      R.b[i] = brow[i] >= 0 ? *reinterpret_cast<const u32x4_t*>(
-                                  a.act + ((size_t)brow[i] * a.K + step * 64 + 32 * c + 8 * q) * 2)
-                            : u32x4_t{0u, 0u, 0u, 0u};
+      if (part == 0) A.c[t] = *reinterpret_cast<const u32x2_t*>(a.wcodes + ti * 1024 + lane * 16 + 8 * h);
+      else A.s[t] = *reinterpret_cast<const uint32_t*>(a.wscales + ti * 128 + i16 * 8 + 4 * h);
     }
   };
-
-  auto sstore = [&](const PfRegs<DT>& R, int buf, int step) {
-    u32x4_t* A = lds[buf][0];
-    u32x4_t* B = lds[buf][1];
-    const int h = step & 1;
-    if constexpr (DT == DT_BF16) {
+  auto issue_all = [&](u32x4_t(&stage)[kPfStageSlots], PfA<DT>& A, int step) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) A[tid + 256 * i] = R.a[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int slot = tid + 256 * i, t = slot >> 6, l = slot & 63, q = l >> 4;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {  // chunk 2h + j of this kgroup -> LDS chunk j
-          const int c = 2 * h + j;
-          if constexpr (DT == DT_MXFP8) {
-            const uint32_t lo = R.a[i][2 * j], hi = R.a[i][2 * j + 1];
-            A[t * 128 + j * 64 + l] = (u32x4_t)mxfp8_dequant8(lo, hi, (R.as[i][0] >> (8 * c)) & 0xFF);
-          } else {
-            const int sb = 2 * c + (q >> 1);
-            const uint32_t sw = sb < 4 ? R.as[i][0] : R.as[i][1];
-            A[t * 128 + j * 64 + l] = (u32x4_t)nvfp4_dequant8(R.a[i][j], (sw >> (8 * (sb & 3))) & 0xFF);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) B[tid + 256 * i] = R.b[i];
+    for (int k = 0; k < kPfStepOps; ++k) issue_op(k, stage, A, step);
   };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[4][8];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc[t][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 8; ++s) acc[t][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  {
-    PfRegs<DT> R0;
-    gload(R0, 0);
-    sstore(R0, 0, 0);
-  }
-  __syncthreads();
-  for (int step = 0; step < KS; ++step) {
-    const int buf = step & 1;
-    PfRegs<DT> R{};  // the next step's data, live only within this iteration
-    if (step + 1 < KS) gload(R, step + 1);
-    const u32x4_t* A = lds[buf][0];
-    const u32x4_t* B = lds[buf][1];
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short op_t;
+  // matrix operands of chunk j (0, 1) of a step: the 4 weight tiles, converted
+  auto convert = [&](op_t(&af)[4], const PfA<DT>& A, int h, int j) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      u32x4_t af[4], bf[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) af[t] = A[(4 * wn + t) * 128 + c * 64 + lane];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) bf[s] = B[(4 * wm + s) * 128 + c * 64 + lane];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if constexpr (DT == DT_NVFP4)
-            acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16((f16x8_t)af[t], (f16x8_t)bf[s], acc[t][s], 0, 0, 0);
-          else
-            acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16((bf16x8_t)af[t], (bf16x8_t)bf[s], acc[t][s], 0, 0, 0);
-        }
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (DT == DT_BF16) {
+        af[t] = (op_t)A.c[t][j];
+      } else if constexpr (DT == DT_MXFP8) {
+        af[t] = (op_t)mxfp8_dequant8(A.c[t][2 * j], A.c[t][2 * j + 1], (A.s[t] >> (8 * (2 * h + j))) & 0xFF);
+      } else {
+        af[t] = (op_t)nvfp4_dequant8(A.c[t][j], (A.s[t] >> (8 * (2 * j + (q >> 1)))) & 0xFF);
+      }
     }
-    if (step + 1 < KS) sstore(R, buf ^ 1, step + 1);
-    __syncthreads();
+  };
+  // token operands of chunk j, sub-tiles 4sh .. 4sh+3
+  auto read_b = [&](u32x4_t(&bf)[4], const u32x4_t(&stage)[kPfStageSlots], int j, int sh) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) bf[s4] = stage[((4 * sh + s4) * 2 + j) * 64 + lane];
+  };
+
+  // One K step: 64 MFMAs on `stage` / A in four quarters (chunk j, sub-tile
+  // half sh), the next quarter's token fragments read ahead, and the 12
+  // loads of step `nstep` spread one per five MFMAs so the memory pipeline
+  // accepts them while the matrix unit is busy.
+  auto step_body = [&](const u32x4_t(&stage)[kPfStageSlots], const PfA<DT>& A, int step,
+                       u32x4_t(&nstage)[kPfStageSlots], PfA<DT>& nA, int nstep) {
+    const int h = step & 1;
+    op_t af[2][4];
+    u32x4_t bf[2][4];
+    convert(af[0], A, h, 0);
+    read_b(bf[0], stage, 0, 0);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int j = qq >> 1, sh = qq & 1;
+      if (qq < 3) read_b(bf[(qq + 1) & 1], stage, (qq + 1) >> 1, (qq + 1) & 1);
+      if (qq == 1) convert(af[1], A, h, 1);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const int s4 = m >> 2, t = m & 3, gm = qq * 16 + m;
+        f32x4_t& c = acc[t][4 * sh + s4];
+        if constexpr (DT == DT_NVFP4)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16((f16x8_t)af[j][t], (f16x8_t)bf[qq & 1][s4], c, 0, 0, 0);
+        else
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16((bf16x8_t)af[j][t], (bf16x8_t)bf[qq & 1][s4], c, 0, 0, 0);
+        if (gm % 5 == 4 && gm / 5 < kPfStepOps) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_op(gm / 5, nstage, nA, nstep);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  };
+
+  // prologue: steps 0 .. NS-2 in flight (every wave issues the same number
+  // of operations each step, clamped to the last step past the end)
+  PfA<DT> A[kPfStages];
+#pragma unroll
+  for (int i = 0; i < kPfStages - 1; ++i) {
+    issue_all(*st.s[i], A[i], min(i, KS - 1));
+    asm volatile("" ::: "memory");  // each step's operations issue after the previous step's
   }
-  gemm_epilogue<DT, 4, G13>(a, acc, r0 + 64 * wm, r_end, 2 * nt + wn, e, lane);
+  int s = 0;
+  for (; s + kPfStages <= KS; s += kPfStages) {
+#pragma unroll
+    for (int u = 0; u < kPfStages; ++u) {
+      // step s+u has landed once at most the NS-2 newer steps are in flight
+      pf_wait_barrier<kPfStepOps * (kPfStages - 2)>();
+      pf_pin(A[u]);
+      const int nxt = (u + kPfStages - 1) % kPfStages;
+      step_body(*st.s[u], A[u], s + u, *st.s[nxt], A[nxt], min(s + u + kPfStages - 1, KS - 1));
+    }
+  }
+  if (s < KS) {  // the last KS % NS steps; every body still issues its 12 (clamped) operations
+#pragma unroll
+    for (int u = 0; u < kPfStages - 1; ++u) {
+      pf_wait_barrier<kPfStepOps * (kPfStages - 2)>();
+      pf_pin(A[u]);
+      const int nxt = (u + kPfStages - 1) % kPfStages;
+      const int nstep = min(s + u + kPfStages - 1, KS - 1);
+      if (s + u < KS) step_body(*st.s[u], A[u], s + u, *st.s[nxt], A[nxt], nstep);
+      else issue_all(*st.s[nxt], A[nxt], nstep);
+    }
+  }
+  pf_wait_barrier<0>();
+  if (g < a.G) gemm_epilogue<DT, 8, G13>(a, acc, r0, r_end, g, e, lane);
+  // Drain the epilogue's stores: with stores and loads both pending, the
+  // shared vector-memory counter no longer counts loads in order, and the
+  // compiler would wait for everything at the next item's K-loop head.
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
   return e;
 }
 
