@@ -116,9 +116,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   const int per2 = V == 2 ? (a.g2.G + kPfGroups - 1) / kPfGroups : a.g2.G;
   auto item = [&](const GemmArgs& g, bool g13, long long w) -> int {
     if constexpr (V == 2) {
-      __shared__ u32x4_t s0[kPfStageSlots], s1[kPfStageSlots], s2[kPfStageSlots], s3[kPfStageSlots];
-      static_assert(kPfStages == 4, "stage objects");
-      const PfStages st{{&s0, &s1, &s2, &s3}};
+      const PfStages st = pf_make_stages<pf_stages<DT>()>();
       return g13 ? prefill_item<DT, true>(g, w, cum, st) : prefill_item<DT, false>(g, w, cum, st);
     } else {
       auto* red = reinterpret_cast<f32x4_t(*)[4 * NT][64]>(smem);

@@ -2,51 +2,68 @@
 // (moe_prefill.hip) and the fused single-launch kernel.
 //
 // Item = (expert, m-tile of 128 sorted rows, n-block of 4 weight row groups
-// = 256 weight rows).  The block's 4 waves each own one row group (its 4
-// packed 16-row tiles) and all 128 token rows: a 64 x 128 wave tile of
-// 16x16x32 MFMAs, accumulated over K in order.
+// = 256 weight rows).  The block's 4 waves each own one row group (64 rows:
+// for the gate/up GEMM 32 gate rows then the 32 matching up rows) and all
+// 128 token rows: a 64 x 128 wave tile of 32x32x16 MFMAs (2 x 4 of them per
+// 16-wide K slice), accumulated over K in order.  (From a single wave per
+// SIMD the 32x32x16 instruction keeps the matrix unit much busier than
+// 16x16x32: measured 2.1 vs 1.4 PFLOP/s on MI355X.)
 //
 //  * Weights stream from global memory straight into registers (each weight
 //    element is used by exactly one wave): a ring of kPfStages K steps.
+//    Fragments are gathered from the packed 16-row tiles: lane l of a
+//    32-row fragment reads tile 2f + ((l >> 4) & 1), the lane position
+//    (l & 15) + 16 * (2m + (l >> 5)) of the 16x16x32 layout.
 //  * Token rows are shared by the 4 waves through LDS, filled by the 16-byte
 //    direct global->LDS load (no register round trip) into a ring of
-//    kPfStages stages, each one 64-wide K step in the matrix instruction's
-//    lane order.
-//  * One barrier per K step.  Loads for step s+kPfStages-1 are issued when
-//    step s starts, so kPfStages-1 steps of MFMA work cover their latency;
-//    the wait before the barrier counts outstanding vector-memory operations
-//    explicitly.
+//    kPfStages stages of one 64-wide K step: per (32-row sub-tile, 32-wide
+//    chunk) block, row-major with 64 B per row, the four 16-byte pieces of a
+//    row XOR-swizzled so fragment reads are free of bank conflicts.
+//  * One barrier per K step.  Loads for step s+kPfStages-1 are issued while
+//    step s computes, spread between its MFMAs; the wait before the barrier
+//    counts outstanding vector-memory operations explicitly.
 #pragma once
 
 #include "moe_gemm_item.h"
 
 namespace moe {
 
-constexpr int kPfRows = 128;                  // routed rows per item: 8 sub-tiles of 16
+constexpr int kPfRows = 128;                  // routed rows per item: 4 sub-tiles of 32
 constexpr int kPfGroups = 4;                  // weight row groups per item, one per wave
 constexpr int kPfBand = 8;                    // m-tiles per band of the item order
-constexpr int kPfStageSlots = 8 * 2 * 64;     // token stage: [sub-tile][chunk][lane] x 16 B = 16 KB
-constexpr int kPfStepOps = 12;                // vector-memory operations per wave per K step
-constexpr int kPfStages = 4;                  // pipeline depth: K steps in flight + the one computed
+constexpr int kPfStageSlots = 8 * 2 * 64;     // token stage: 8 blocks of 32 rows x 32 K, 16-byte slots (16 KB)
+#ifndef MOE_PF_STAGES_Q
+#define MOE_PF_STAGES_Q 4  // pipeline depth for MXFP8 / NVFP4 weights
+#endif
+constexpr int kPfMaxStages = 8;
+// pipeline depth (K steps in flight + the one computed); 16-bit weights need
+// twice the registers per step
+template <int DT>
+constexpr int pf_stages() { return DT == DT_BF16 ? 4 : MOE_PF_STAGES_Q; }
+
+// vector-memory operations per wave per K step: 4 token loads + the weights
+template <int DT>
+constexpr int pf_step_ops() { return DT == DT_BF16 ? 12 : 10; }
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
-// One K step (64 wide) of this wave's 4 weight tiles, as loaded.
+// One K step (64 wide = chunks 2h, 2h+1 of kgroup kg) of this wave's two
+// 32-row weight fragments f, K slices m (16 wide) of each chunk, as loaded.
 template <int DT>
 struct PfA;
 template <>
 struct PfA<DT_BF16> {
-  u32x4_t c[4][2];  // [tile][chunk]: 8 bf16 per lane
+  u32x4_t c[2][2][2];  // [f][chunk][m]: 8 bf16
 };
 template <>
 struct PfA<DT_MXFP8> {
-  u32x4_t c[4];   // [tile]: chunk 0 in words 0-1, chunk 1 in words 2-3 (8 e4m3 each)
-  uint32_t s[4];  // [tile]: the row's 4 e8m0 scales of the kgroup
+  u32x4_t c[2][2];  // [f][m]: 8 e4m3 of chunk 2h (words 0-1), of chunk 2h+1 (words 2-3)
+  uint32_t s[2];    // [f]: the row's 4 e8m0 scales of the kgroup
 };
 template <>
 struct PfA<DT_NVFP4> {
-  u32x2_t c[4];   // [tile]: 8 e2m1 of chunk 0, of chunk 1
-  uint32_t s[4];  // [tile]: the row's 4 e4m3 scales of this half kgroup
+  u32x2_t c[2][2];  // [f][m]: 8 e2m1 of chunk 2h, of chunk 2h+1
+  uint32_t s[2];    // [f]: the row's e4m3 scales of chunks 2h, 2h+1 (16 wide each)
 };
 
 // Blocks are dealt to the 8 XCDs (each with its own L2) round-robin by
@@ -76,20 +93,151 @@ __device__ __forceinline__ void pf_wait_barrier() {
 template <int DT>
 __device__ __forceinline__ void pf_pin(PfA<DT>& A) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int f = 0; f < 2; ++f) {
     if constexpr (DT == DT_BF16) {
-      asm volatile("" : "+v"(A.c[t][0]), "+v"(A.c[t][1]));
+      asm volatile("" : "+v"(A.c[f][0][0]), "+v"(A.c[f][0][1]), "+v"(A.c[f][1][0]), "+v"(A.c[f][1][1]));
     } else {
-      asm volatile("" : "+v"(A.c[t]), "+v"(A.s[t]));
+      asm volatile("" : "+v"(A.c[f][0]), "+v"(A.c[f][1]), "+v"(A.s[f]));
     }
   }
 }
 
-// The token stages of one block (separate LDS objects, so the compiler's
-// waits for the direct loads track each stage on its own).
+// The token stages of one block: separate LDS objects, so the compiler's
+// waits for the direct loads track each stage on its own.  Each index is
+// one allocation per kernel, shared by every item the kernel runs.
 struct PfStages {
-  u32x4_t (*s[kPfStages])[kPfStageSlots];
+  u32x4_t (*s[kPfMaxStages])[kPfStageSlots];
 };
+template <int I>
+__device__ __forceinline__ u32x4_t (*pf_stage())[kPfStageSlots] {
+  __shared__ u32x4_t buf[kPfStageSlots];
+  return &buf;
+}
+template <int NS>
+__device__ __forceinline__ PfStages pf_make_stages() {
+  static_assert(NS >= 3 && NS <= kPfMaxStages, "stages");
+  PfStages st{};
+  st.s[0] = pf_stage<0>();
+  st.s[1] = pf_stage<1>();
+  st.s[2] = pf_stage<2>();
+  if constexpr (NS > 3) st.s[3] = pf_stage<3>();
+  if constexpr (NS > 4) st.s[4] = pf_stage<4>();
+  if constexpr (NS > 5) st.s[5] = pf_stage<5>();
+  if constexpr (NS > 6) st.s[6] = pf_stage<6>();
+  if constexpr (NS > 7) st.s[7] = pf_stage<7>();
+  return st;
+}
+
+// Swizzle of the 16-byte pieces of token row r (0..31) in a stage block:
+// piece p of the row sits in slot p ^ pf_swz(r).  Rows r, r+4, r+8, r+12
+// (which the 64-byte row pitch puts on the same banks) get distinct slots;
+// measured on MI355X, fragment reads with this swizzle are free of bank
+// conflicts.
+__device__ __forceinline__ int pf_swz(int r) { return (r >> 2) & 3; }
+
+// Epilogue of a 64 x 128 wave tile in the 32x32 accumulator layout: lane l,
+// element e of acc[f][S] is weight row 32f + (e & 3) + 8 (e >> 2) + 4 (l >> 5)
+// of row group g, routed row r0 + 32 S + (l & 31).  Gate/up GEMM: SwiGLU of
+// the f = 0 (gate) and f = 1 (up) values, requantised per token row; down
+// GEMM: bf16 y rows of the pair.
+template <int DT, bool G13>
+__device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2][4], int r0, int r_end, int g, int e,
+                                            int lane) {
+  const int hl = lane >> 5, l32 = lane & 31;
+  const float alpha = DT == DT_NVFP4 ? a.walpha[e] : 1.f;
+#pragma unroll
+  for (int S = 0; S < 4; ++S) {
+    const int r = r0 + 32 * S + l32;
+    const bool ok = r < r_end;
+    if constexpr (G13) {
+      const int I = a.n_out;
+      float h[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float gv = acc[0][S][i] * alpha, uv = acc[1][S][i] * alpha;
+        h[i] = gv / (1.0f + expf(-gv)) * uv;
+      }
+      // h[4b + j] is intermediate index 32g + 8b + 4hl + j
+      if constexpr (DT == DT_BF16) {
+        if (ok) {
+          uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * g + 4 * hl;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            *reinterpret_cast<uint2*>(o + 8 * b) =
+                make_uint2(f32_to_bf16(h[4 * b]) | ((uint32_t)f32_to_bf16(h[4 * b + 1]) << 16),
+                           f32_to_bf16(h[4 * b + 2]) | ((uint32_t)f32_to_bf16(h[4 * b + 3]) << 16));
+        }
+      } else if constexpr (DT == DT_MXFP8) {
+        // one block of 32 along I: this lane's 16 values and lane l ^ 32's
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(h[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+        const int sx = mx_scale_exp(amax);
+        if (ok) {
+          uint8_t* o = a.out + (size_t)r * I + 32 * g + 4 * hl;
+          uint16_t* od = a.out_deq + (size_t)r * I + 32 * g + 4 * hl;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            uint32_t v = 0, d[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t c = e4m3_from_f32(ldexpf(h[4 * b + j], -sx));
+              v |= c << (8 * j);
+              d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), sx)) >> 16;  // exact in bf16
+            }
+            *reinterpret_cast<uint32_t*>(o + 8 * b) = v;
+            *reinterpret_cast<uint2*>(od + 8 * b) = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+          }
+          if (hl == 0) a.out_scales[(size_t)r * (I / 32) + g] = (uint8_t)(sx + 127);
+        }
+      } else {
+        // two blocks of 16 along I: tp = 0 holds b = 0, 1; tp = 1 holds b = 2, 3
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 8 * tp; i < 8 * tp + 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
+          amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+          const uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
+          const float sc = e4m3_to_f32(sc_code);
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) {
+            const int b = 2 * tp + bb;
+            uint32_t v = 0, d[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float x = h[4 * b + j];
+              const uint32_t c = sc > 0.f ? e2m1_from_f32(x, sc) : ((__float_as_uint(x) >> 28) & 8u);
+              v |= c << (4 * j);
+              d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
+            }
+            if (ok) {
+              *reinterpret_cast<uint16_t*>(a.out + (size_t)r * (I / 2) + 16 * g + 4 * b + 2 * hl) = (uint16_t)v;
+              *reinterpret_cast<uint2*>(a.out_deq + (size_t)r * I + 32 * g + 8 * b + 4 * hl) =
+                  make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+            }
+          }
+          if (ok && hl == 0) a.out_scales[(size_t)r * (I / 16) + 2 * g + tp] = (uint8_t)sc_code;
+        }
+      }
+    } else {
+      if (ok) {
+        const int p = a.sorted_pairs[r];
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)p * a.n_out + 64 * g + 4 * hl;
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const f32x16_t& v = acc[f][S];
+            *reinterpret_cast<uint2*>(o + 32 * f + 8 * b) =
+                make_uint2(f32_to_bf16(v[4 * b] * alpha) | ((uint32_t)f32_to_bf16(v[4 * b + 1] * alpha) << 16),
+                           f32_to_bf16(v[4 * b + 2] * alpha) | ((uint32_t)f32_to_bf16(v[4 * b + 3] * alpha) << 16));
+          }
+      }
+    }
+  }
+}
 
 // One prefill work item.  `w` numbers items expert-major; within an expert,
 // bands of up to kPfBand m-tiles, n-block-major inside a band, so kPfBand^2
@@ -98,7 +246,10 @@ struct PfStages {
 // expert; ends with every load landed and the block's LDS free for reuse.
 template <int DT, bool G13>
 __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, const int* cum, const PfStages& st) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, i16 = lane & 15, q = lane >> 4;
+  constexpr int kOps = pf_step_ops<DT>();
+  constexpr int kPfStages = pf_stages<DT>();
+  const int tid = threadIdx.x, lane = tid & 63, i16 = lane & 15, hl = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NB = (a.G + kPfGroups - 1) / kPfGroups;
   const int KS = a.KG * 2;  // K steps of 64
   const int e = find_expert(cum, a.E, (int)(w / NB));
@@ -112,96 +263,120 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
   // this wave's row group; a group past the end (G not a multiple of 4) reads group G-1 and discards it
   const int g = kPfGroups * nb + wv, gl = min(g, a.G - 1);
 
-  // token rows of the two sub-tiles this wave loads (2wv, 2wv+1); rows past
-  // the expert's end load its last row, whose results are discarded
+  // Token loads of this wave: sub-tile S = wv, rows 16 half + lane / 4, the
+  // row's 16-byte piece (lane % 4) ^ swizzle.  Rows past the expert's end
+  // load its last row, whose results are discarded.
   const uint8_t* bsrc[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = min(r0 + 16 * (2 * wv + j) + i16, r_end - 1);
+  for (int half = 0; half < 2; ++half) {
+    const int rl = 16 * half + (lane >> 2);
+    const int r = min(r0 + 32 * wv + rl, r_end - 1);
     const int row = G13 ? a.sorted_pairs[r] / a.k : r;
-    bsrc[j] = a.act + ((size_t)row * a.K + 8 * q) * 2;
+    const int piece = (lane & 3) ^ pf_swz(rl);
+    bsrc[half] = a.act + ((size_t)row * a.K + 8 * piece) * 2;
   }
+  // fragment reads: row l32 of a block, piece 2m + hl
+  int boff[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) boff[m] = 4 * l32 + ((2 * m + hl) ^ pf_swz(l32));
+
+  // weights: lane part of the gathered fragment address
+  constexpr size_t tcode = DT == DT_BF16 ? 4096 : DT == DT_MXFP8 ? 2048 : 1024;
+  constexpr size_t tscale = DT == DT_MXFP8 ? 64 : 128;
+  const int ltile = (lane >> 4) & 1, lpos = i16 + 16 * hl;  // lane position (l & 15) + 16 (2m + (l >> 5)), less 32m
   const size_t tile0 = (size_t)(e * a.G + gl) * a.KG * 4;  // tile index of (gl, kgroup 0, tile 0)
-  // Vector-memory operation k (0..11) of K step `step`: k < 4 the token
-  // rows of sub-tile 2wv + k/2, chunk k%2 into `stage`; k >= 4 a piece of
-  // weight tile (k-4)/2 into A.
+  const uint8_t* wc = a.wcodes + (tile0 + ltile) * tcode + lpos * 16;
+  const uint8_t* ws = a.wscales + (tile0 + ltile) * tscale + i16 * (DT == DT_MXFP8 ? 4 : 8);
+
+  // Vector-memory operation k of K step `step`: k < 4 token rows of chunk
+  // k / 2, row half k % 2 into `stage`; k >= 4 a piece of the weights into A.
   auto issue_op = [&](int k, u32x4_t(&stage)[kPfStageSlots], PfA<DT>& A, int step) {
     if (k < 4) {
-      const int j = k >> 1, c = k & 1;
-      __builtin_amdgcn_global_load_lds(bsrc[j] + step * 128 + c * 64, &stage[((2 * wv + j) * 2 + c) * 64], 16, 0, 0);
+      const int cc = k >> 1, half = k & 1;
+      __builtin_amdgcn_global_load_lds(bsrc[half] + step * 128 + cc * 64, &stage[((2 * wv + cc) * 2 + half) * 64], 16,
+                                       0, 0);
       return;
     }
-    const int t = (k - 4) >> 1, part = (k - 4) & 1, kg = step >> 1, h = step & 1;
-    const size_t ti = tile0 + (size_t)kg * 4 + t;
+    const int kg = step >> 1, h = step & 1, idx = k - 4;
+    const size_t tk = (size_t)kg * 4;  // tile offset of the kgroup
     if constexpr (DT == DT_BF16) {
-      A.c[t][part] = *reinterpret_cast<const u32x4_t*>(a.wcodes + ti * 4096 + (2 * h + part) * 1024 + lane * 16);
-    } else if constexpr (DT == DT_MXFP8) {
-      if (part == 0) A.c[t] = *reinterpret_cast<const u32x4_t*>(a.wcodes + ti * 2048 + h * 1024 + lane * 16);
-      else A.s[t] = *reinterpret_cast<const uint32_t*>(a.wscales + ti * 64 + i16 * 4);
+      const int f = idx >> 2, cc = (idx >> 1) & 1, m = idx & 1;
+      A.c[f][cc][m] = *reinterpret_cast<const u32x4_t*>(wc + (tk + 2 * f) * tcode + (2 * h + cc) * 1024 + m * 512);
+    } else if (idx < 4) {
+      const int f = idx >> 1, m = idx & 1;
+      if constexpr (DT == DT_MXFP8)
+        A.c[f][m] = *reinterpret_cast<const u32x4_t*>(wc + (tk + 2 * f) * tcode + h * 1024 + m * 512);
+      else
+        A.c[f][m] = *reinterpret_cast<const u32x2_t*>(wc + (tk + 2 * f) * tcode + m * 512 + 8 * h);
     } else {
-      if (part == 0) A.c[t] = *reinterpret_cast<const u32x2_t*>(a.wcodes + ti * 1024 + lane * 16 + 8 * h);
-      else A.s[t] = *reinterpret_cast<const uint32_t*>(a.wscales + ti * 128 + i16 * 8 + 4 * h);
+      const int f = idx - 4;
+      A.s[f] = *reinterpret_cast<const uint32_t*>(ws + (tk + 2 * f) * tscale + (DT == DT_MXFP8 ? 0 : 4 * h));
     }
   };
   auto issue_all = [&](u32x4_t(&stage)[kPfStageSlots], PfA<DT>& A, int step) {
 #pragma unroll
-    for (int k = 0; k < kPfStepOps; ++k) issue_op(k, stage, A, step);
+    for (int k = 0; k < kOps; ++k) issue_op(k, stage, A, step);
   };
 
-  f32x4_t acc[4][8];
+  f32x16_t acc[2][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc[t][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int S = 0; S < 4; ++S)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[f][S][i] = 0.f;
 
   typedef __attribute__((__vector_size__(8 * sizeof(short)))) short op_t;
-  // matrix operands of chunk j (0, 1) of a step: the 4 weight tiles, converted
-  auto convert = [&](op_t(&af)[4], const PfA<DT>& A, int h, int j) {
+  // weight fragments f = 0, 1 of K slice (chunk cc, m), converted
+  auto convert = [&](op_t(&af)[2], const PfA<DT>& A, int h, int cc, int m) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int f = 0; f < 2; ++f) {
       if constexpr (DT == DT_BF16) {
-        af[t] = (op_t)A.c[t][j];
+        af[f] = (op_t)A.c[f][cc][m];
       } else if constexpr (DT == DT_MXFP8) {
-        af[t] = (op_t)mxfp8_dequant8(A.c[t][2 * j], A.c[t][2 * j + 1], (A.s[t] >> (8 * (2 * h + j))) & 0xFF);
+        af[f] = (op_t)mxfp8_dequant8(A.c[f][m][2 * cc], A.c[f][m][2 * cc + 1], (A.s[f] >> (8 * (2 * h + cc))) & 0xFF);
       } else {
-        af[t] = (op_t)nvfp4_dequant8(A.c[t][j], (A.s[t] >> (8 * (2 * j + (q >> 1)))) & 0xFF);
+        af[f] = (op_t)nvfp4_dequant8(A.c[f][m][cc], (A.s[f] >> (8 * (2 * cc + m))) & 0xFF);
       }
     }
   };
-  // token operands of chunk j, sub-tiles 4sh .. 4sh+3
-  auto read_b = [&](u32x4_t(&bf)[4], const u32x4_t(&stage)[kPfStageSlots], int j, int sh) {
+  // token fragments S = 0..3 of K slice (chunk cc, m)
+  auto read_b = [&](u32x4_t(&bf)[4], const u32x4_t(&stage)[kPfStageSlots], int cc, int m) {
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) bf[s4] = stage[((4 * sh + s4) * 2 + j) * 64 + lane];
+    for (int S = 0; S < 4; ++S) bf[S] = stage[(2 * S + cc) * 128 + boff[m]];
   };
 
-  // One K step: 64 MFMAs on `stage` / A in four quarters (chunk j, sub-tile
-  // half sh), the next quarter's token fragments read ahead, and the 12
-  // loads of step `nstep` spread one per five MFMAs so the memory pipeline
-  // accepts them while the matrix unit is busy.
+  // One K step: 4 K slices x 8 MFMAs on `stage` / A, the next slice's
+  // operands fetched ahead, and the loads of step `nstep` spread between the
+  // MFMAs so the memory pipeline accepts them while the matrix unit is busy.
   auto step_body = [&](const u32x4_t(&stage)[kPfStageSlots], const PfA<DT>& A, int step,
                        u32x4_t(&nstage)[kPfStageSlots], PfA<DT>& nA, int nstep) {
     const int h = step & 1;
-    op_t af[2][4];
+    op_t af[2][2];
     u32x4_t bf[2][4];
-    convert(af[0], A, h, 0);
+    convert(af[0], A, h, 0, 0);
     read_b(bf[0], stage, 0, 0);
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int j = qq >> 1, sh = qq & 1;
-      if (qq < 3) read_b(bf[(qq + 1) & 1], stage, (qq + 1) >> 1, (qq + 1) & 1);
-      if (qq == 1) convert(af[1], A, h, 1);
+    for (int sl = 0; sl < 4; ++sl) {
+      if (sl < 3) {
+        read_b(bf[(sl + 1) & 1], stage, (sl + 1) >> 1, (sl + 1) & 1);
+        convert(af[(sl + 1) & 1], A, h, (sl + 1) >> 1, (sl + 1) & 1);
+      }
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const int s4 = m >> 2, t = m & 3, gm = qq * 16 + m;
-        f32x4_t& c = acc[t][4 * sh + s4];
+      for (int mm = 0; mm < 8; ++mm) {
+        const int f = mm >> 2, S = mm & 3, gm = sl * 8 + mm;
+        f32x16_t& c = acc[f][S];
         if constexpr (DT == DT_NVFP4)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16((f16x8_t)af[j][t], (f16x8_t)bf[qq & 1][s4], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16((f16x8_t)af[sl & 1][f], (f16x8_t)bf[sl & 1][S], c, 0, 0, 0);
         else
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16((bf16x8_t)af[j][t], (bf16x8_t)bf[qq & 1][s4], c, 0, 0, 0);
-        if (gm % 5 == 4 && gm / 5 < kPfStepOps) {
-          __builtin_amdgcn_sched_barrier(0);
-          issue_op(gm / 5, nstage, nA, nstep);
-          __builtin_amdgcn_sched_barrier(0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16((bf16x8_t)af[sl & 1][f], (bf16x8_t)bf[sl & 1][S], c, 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < kOps; ++k) {
+          if (gm == (k * 32) / kOps + 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_op(k, nstage, nA, nstep);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     }
@@ -220,16 +395,16 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
 #pragma unroll
     for (int u = 0; u < kPfStages; ++u) {
       // step s+u has landed once at most the NS-2 newer steps are in flight
-      pf_wait_barrier<kPfStepOps * (kPfStages - 2)>();
+      pf_wait_barrier<kOps * (kPfStages - 2)>();
       pf_pin(A[u]);
       const int nxt = (u + kPfStages - 1) % kPfStages;
       step_body(*st.s[u], A[u], s + u, *st.s[nxt], A[nxt], min(s + u + kPfStages - 1, KS - 1));
     }
   }
-  if (s < KS) {  // the last KS % NS steps; every body still issues its 12 (clamped) operations
+  if (s < KS) {  // the last KS % NS steps; every body still issues its (clamped) operations
 #pragma unroll
     for (int u = 0; u < kPfStages - 1; ++u) {
-      pf_wait_barrier<kPfStepOps * (kPfStages - 2)>();
+      pf_wait_barrier<kOps * (kPfStages - 2)>();
       pf_pin(A[u]);
       const int nxt = (u + kPfStages - 1) % kPfStages;
       const int nstep = min(s + u + kPfStages - 1, KS - 1);
@@ -238,7 +413,7 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
     }
   }
   pf_wait_barrier<0>();
-  if (g < a.G) gemm_epilogue<DT, 8, G13>(a, acc, r0, r_end, g, e, lane);
+  if (g < a.G) pf_epilogue<DT, G13>(a, acc, r0, r_end, g, e, lane);
   // Drain the epilogue's stores: with stores and loads both pending, the
   // shared vector-memory counter no longer counts loads in order, and the
   // compiler would wait for everything at the next item's K-loop head.
