@@ -21,9 +21,16 @@ struct GemmArgs {
   int E, K, G, KG, k, n_out;
 };
 
-// cum[e] = m-tiles of experts < e (LDS), returns the total.
+// cum[e] = m-tiles of experts < e (LDS), returns the total.  The first
+// kGemmThreads threads do the scan; a larger block only waits for it.
+// wsum holds kGemmThreads / 64 ints.
 __device__ int build_schedule(const int* __restrict__ offsets, int E, int MT, int* cum, int* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid >= kGemmThreads) {
+    __syncthreads();
+    __syncthreads();
+    return cum[E];
+  }
   const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 4 (E <= 1024)
   const int e0 = tid * per;
   int cnt[4] = {0, 0, 0, 0}, local = 0;

@@ -9,14 +9,16 @@
 
 namespace moe {
 
+constexpr int kPfThreads = 2 * kGemmThreads;  // 8 waves: 4 row groups x 2 token halves
+
 template <int DT, bool G13>
-__global__ __launch_bounds__(kGemmThreads) void gemm_prefill_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmArgs a) {
   __shared__ int cum[1025];
   __shared__ int wsum[4];
   const PfStages st = pf_make_stages<pf_stages<DT>()>();
   const int total_mt = build_schedule(a.offsets, a.E, kPfRows, cum, wsum);
   const long long total = (long long)total_mt * ((a.G + kPfGroups - 1) / kPfGroups);
-  for (long long w = xcd_logical_block(); w < total; w += gridDim.x) prefill_item<DT, G13>(a, w, cum, st);
+  for (long long w = xcd_logical_block(); w < total; w += gridDim.x) prefill_item<DT, G13, 2>(a, w, cum, st);
 }
 
 template <int DT, bool G13>
@@ -32,14 +34,14 @@ static const void* prefill_ptr(int dt, bool g13) {
 
 int prefill_blocks_per_cu(int dt, bool g13) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_ptr(dt, g13), kGemmThreads, 0) != hipSuccess || n < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_ptr(dt, g13), kPfThreads, 0) != hipSuccess || n < 1)
     n = 1;
   return n;
 }
 
 hipError_t launch_prefill(int dt, bool g13, const GemmArgs& a, int grid, hipStream_t s) {
   void* args[] = {const_cast<GemmArgs*>(&a)};
-  return hipLaunchKernel(prefill_ptr(dt, g13), dim3(grid), dim3(kGemmThreads), args, 0, s);
+  return hipLaunchKernel(prefill_ptr(dt, g13), dim3(grid), dim3(kPfThreads), args, 0, s);
 }
 
 }  // namespace moe

@@ -24,6 +24,8 @@
 //    counts outstanding vector-memory operations explicitly.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_gemm_item.h"
 
 namespace moe {
@@ -37,13 +39,14 @@ constexpr int kPfStageSlots = 8 * 2 * 64;     // token stage: 8 blocks of 32 row
 #endif
 constexpr int kPfMaxStages = 8;
 // pipeline depth (K steps in flight + the one computed); 16-bit weights need
-// twice the registers per step
+// twice the registers per step (the depth barely matters once loads are
+// interleaved with the MFMAs: measured flat from 3 to 8 for MXFP8)
 template <int DT>
-constexpr int pf_stages() { return DT == DT_BF16 ? 4 : MOE_PF_STAGES_Q; }
+constexpr int pf_stages() { return DT == DT_BF16 ? 3 : MOE_PF_STAGES_Q; }
 
-// vector-memory operations per wave per K step: 4 token loads + the weights
+// weight loads per wave per K step
 template <int DT>
-constexpr int pf_step_ops() { return DT == DT_BF16 ? 12 : 10; }
+constexpr int pf_a_ops() { return DT == DT_BF16 ? 8 : 6; }
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -135,18 +138,18 @@ __device__ __forceinline__ PfStages pf_make_stages() {
 // conflicts.
 __device__ __forceinline__ int pf_swz(int r) { return (r >> 2) & 3; }
 
-// Epilogue of a 64 x 128 wave tile in the 32x32 accumulator layout: lane l,
+// Epilogue of a 64 x 32 NSA wave tile in the 32x32 accumulator layout: lane l,
 // element e of acc[f][S] is weight row 32f + (e & 3) + 8 (e >> 2) + 4 (l >> 5)
 // of row group g, routed row r0 + 32 S + (l & 31).  Gate/up GEMM: SwiGLU of
 // the f = 0 (gate) and f = 1 (up) values, requantised per token row; down
 // GEMM: bf16 y rows of the pair.
-template <int DT, bool G13>
-__device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2][4], int r0, int r_end, int g, int e,
+template <int DT, bool G13, int NSA, int SW>
+__device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2][SW], int r0, int r_end, int g, int e,
                                             int lane) {
   const int hl = lane >> 5, l32 = lane & 31;
   const float alpha = DT == DT_NVFP4 ? a.walpha[e] : 1.f;
 #pragma unroll
-  for (int S = 0; S < 4; ++S) {
+  for (int S = 0; S < NSA; ++S) {
     const int r = r0 + 32 * S + l32;
     const bool ok = r < r_end;
     if constexpr (G13) {
@@ -244,12 +247,21 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
 // consecutive items form a square of weight x token tiles.  `cum` holds the
 // per-expert 128-row m-tile prefix from build_schedule.  Returns the item's
 // expert; ends with every load landed and the block's LDS free for reuse.
-template <int DT, bool G13>
+//
+// TW (1 or 2) is the number of waves along the token dimension: the block
+// has 4 TW waves; wave wv owns row group wv % 4 and token sub-tiles
+// (wv / 4) * 4/TW .. + 4/TW.  With TW = 2 a wave's tile is 64 x 64 (64
+// accumulator registers), so two waves fit per SIMD and one wave's LDS
+// reads, loads and converts overlap the other's MFMAs.
+template <int DT, bool G13, int TW>
 __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, const int* cum, const PfStages& st) {
-  constexpr int kOps = pf_step_ops<DT>();
+  static_assert(TW == 1 || TW == 2, "waves along tokens");
+  constexpr int kSW = 4 / TW;                       // token sub-tiles per wave
+  constexpr int kDma = 4 / TW;                      // token loads per wave per K step (16 per block)
+  constexpr int kOps = pf_a_ops<DT>() + kDma;       // vector-memory operations per wave per K step
   constexpr int kPfStages = pf_stages<DT>();
   const int tid = threadIdx.x, lane = tid & 63, i16 = lane & 15, hl = lane >> 5, l32 = lane & 31;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wg = wv & 3, th = wv >> 2;
   const int NB = (a.G + kPfGroups - 1) / kPfGroups;
   const int KS = a.KG * 2;  // K steps of 64
   const int e = find_expert(cum, a.E, (int)(w / NB));
@@ -261,16 +273,19 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
   const int nb = inner / bsize, mt = band * kPfBand + inner % bsize;
   const int r0 = a.offsets[e] + mt * kPfRows, r_end = a.offsets[e + 1];
   // this wave's row group; a group past the end (G not a multiple of 4) reads group G-1 and discards it
-  const int g = kPfGroups * nb + wv, gl = min(g, a.G - 1);
+  const int g = kPfGroups * nb + wg, gl = min(g, a.G - 1);
 
-  // Token loads of this wave: sub-tile S = wv, rows 16 half + lane / 4, the
+  // Token loads: the block's 16 per K step are (sub-tile d / 4, chunk
+  // (d / 2) % 2, row half d % 2), d = 0..15; this wave issues d = wv kDma ..
+  // + kDma, all in sub-tile dS.  Load lane: row 16 half + lane / 4, the
   // row's 16-byte piece (lane % 4) ^ swizzle.  Rows past the expert's end
   // load its last row, whose results are discarded.
+  const int dS = (wv * kDma) >> 2;
   const uint8_t* bsrc[2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int rl = 16 * half + (lane >> 2);
-    const int r = min(r0 + 32 * wv + rl, r_end - 1);
+    const int r = min(r0 + 32 * dS + rl, r_end - 1);
     const int row = G13 ? a.sorted_pairs[r] / a.k : r;
     const int piece = (lane & 3) ^ pf_swz(rl);
     bsrc[half] = a.act + ((size_t)row * a.K + 8 * piece) * 2;
@@ -288,16 +303,16 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
   const uint8_t* wc = a.wcodes + (tile0 + ltile) * tcode + lpos * 16;
   const uint8_t* ws = a.wscales + (tile0 + ltile) * tscale + i16 * (DT == DT_MXFP8 ? 4 : 8);
 
-  // Vector-memory operation k of K step `step`: k < 4 token rows of chunk
-  // k / 2, row half k % 2 into `stage`; k >= 4 a piece of the weights into A.
+  // Vector-memory operation k of K step `step`: k < kDma a token load into
+  // `stage`; k >= kDma a piece of the weights into A.
   auto issue_op = [&](int k, u32x4_t(&stage)[kPfStageSlots], PfA<DT>& A, int step) {
-    if (k < 4) {
-      const int cc = k >> 1, half = k & 1;
-      __builtin_amdgcn_global_load_lds(bsrc[half] + step * 128 + cc * 64, &stage[((2 * wv + cc) * 2 + half) * 64], 16,
+    if (k < kDma) {
+      const int d = wv * kDma + k, cc = (d >> 1) & 1, half = k & 1;
+      __builtin_amdgcn_global_load_lds(bsrc[half] + step * 128 + cc * 64, &stage[((2 * dS + cc) * 2 + half) * 64], 16,
                                        0, 0);
       return;
     }
-    const int kg = step >> 1, h = step & 1, idx = k - 4;
+    const int kg = step >> 1, h = step & 1, idx = k - kDma;
     const size_t tk = (size_t)kg * 4;  // tile offset of the kgroup
     if constexpr (DT == DT_BF16) {
       const int f = idx >> 2, cc = (idx >> 1) & 1, m = idx & 1;
@@ -318,102 +333,131 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
     for (int k = 0; k < kOps; ++k) issue_op(k, stage, A, step);
   };
 
-  f32x16_t acc[2][4];
+  // The K loop with NSA of this wave's sub-tiles active (the rest of the
+  // m-tile lies past the expert's rows and is skipped; its loads still
+  // issue, clamped, so every wave keeps the same operation count per step).
+  auto run = [&](auto nsa_tag) {
+    constexpr int NSA = decltype(nsa_tag)::value;
+    constexpr int kMfma = 8 * NSA;  // MFMAs per K step
+    f32x16_t acc[2][kSW];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int S = 0; S < 4; ++S)
+      for (int S = 0; S < NSA; ++S)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[f][S][i] = 0.f;
+        for (int i = 0; i < 16; ++i) acc[f][S][i] = 0.f;
 
-  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short op_t;
-  // weight fragments f = 0, 1 of K slice (chunk cc, m), converted
-  auto convert = [&](op_t(&af)[2], const PfA<DT>& A, int h, int cc, int m) {
+    typedef __attribute__((__vector_size__(8 * sizeof(short)))) short op_t;
+    // weight fragments f = 0, 1 of K slice (chunk cc, m), converted
+    auto convert = [&](op_t(&af)[2], const PfA<DT>& A, int h, int cc, int m) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      if constexpr (DT == DT_BF16) {
-        af[f] = (op_t)A.c[f][cc][m];
-      } else if constexpr (DT == DT_MXFP8) {
-        af[f] = (op_t)mxfp8_dequant8(A.c[f][m][2 * cc], A.c[f][m][2 * cc + 1], (A.s[f] >> (8 * (2 * h + cc))) & 0xFF);
-      } else {
-        af[f] = (op_t)nvfp4_dequant8(A.c[f][m][cc], (A.s[f] >> (8 * (2 * cc + m))) & 0xFF);
+      for (int f = 0; f < 2; ++f) {
+        if constexpr (DT == DT_BF16) {
+          af[f] = (op_t)A.c[f][cc][m];
+        } else if constexpr (DT == DT_MXFP8) {
+          af[f] = (op_t)mxfp8_dequant8(A.c[f][m][2 * cc], A.c[f][m][2 * cc + 1], (A.s[f] >> (8 * (2 * h + cc))) & 0xFF);
+        } else {
+          af[f] = (op_t)nvfp4_dequant8(A.c[f][m][cc], (A.s[f] >> (8 * (2 * cc + m))) & 0xFF);
+        }
       }
-    }
-  };
-  // token fragments S = 0..3 of K slice (chunk cc, m)
-  auto read_b = [&](u32x4_t(&bf)[4], const u32x4_t(&stage)[kPfStageSlots], int cc, int m) {
+    };
+    // token fragments of the active sub-tiles, K slice (chunk cc, m)
+    auto read_b = [&](u32x4_t(&bf)[kSW], const u32x4_t(&stage)[kPfStageSlots], int cc, int m) {
 #pragma unroll
-    for (int S = 0; S < 4; ++S) bf[S] = stage[(2 * S + cc) * 128 + boff[m]];
-  };
+      for (int S = 0; S < NSA; ++S) bf[S] = stage[(2 * (th * kSW + S) + cc) * 128 + boff[m]];
+    };
 
-  // One K step: 4 K slices x 8 MFMAs on `stage` / A, the next slice's
-  // operands fetched ahead, and the loads of step `nstep` spread between the
-  // MFMAs so the memory pipeline accepts them while the matrix unit is busy.
-  auto step_body = [&](const u32x4_t(&stage)[kPfStageSlots], const PfA<DT>& A, int step,
-                       u32x4_t(&nstage)[kPfStageSlots], PfA<DT>& nA, int nstep) {
-    const int h = step & 1;
-    op_t af[2][2];
-    u32x4_t bf[2][4];
-    convert(af[0], A, h, 0, 0);
-    read_b(bf[0], stage, 0, 0);
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      if (sl < 3) {
-        read_b(bf[(sl + 1) & 1], stage, (sl + 1) >> 1, (sl + 1) & 1);
-        convert(af[(sl + 1) & 1], A, h, (sl + 1) >> 1, (sl + 1) & 1);
+    // One K step: 4 K slices x 2 NSA MFMAs on `stage` / A, the next slice's
+    // operands fetched ahead, and the loads of step `nstep` spread between
+    // the MFMAs so the memory pipeline accepts them while the matrix unit is
+    // busy.
+    auto step_body = [&](const u32x4_t(&stage)[kPfStageSlots], const PfA<DT>& A, int step,
+                         u32x4_t(&nstage)[kPfStageSlots], PfA<DT>& nA, int nstep) {
+      if constexpr (NSA == 0) {
+        issue_all(nstage, nA, nstep);
+        return;
       }
+      const int h = step & 1;
+      op_t af[2][2];
+      u32x4_t bf[2][kSW];
+      convert(af[0], A, h, 0, 0);
+      read_b(bf[0], stage, 0, 0);
 #pragma unroll
-      for (int mm = 0; mm < 8; ++mm) {
-        const int f = mm >> 2, S = mm & 3, gm = sl * 8 + mm;
-        f32x16_t& c = acc[f][S];
-        if constexpr (DT == DT_NVFP4)
-          c = __builtin_amdgcn_mfma_f32_32x32x16_f16((f16x8_t)af[sl & 1][f], (f16x8_t)bf[sl & 1][S], c, 0, 0, 0);
-        else
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16((bf16x8_t)af[sl & 1][f], (bf16x8_t)bf[sl & 1][S], c, 0, 0, 0);
+      for (int sl = 0; sl < 4; ++sl) {
+        if (sl < 3) {
+          read_b(bf[(sl + 1) & 1], stage, (sl + 1) >> 1, (sl + 1) & 1);
+          convert(af[(sl + 1) & 1], A, h, (sl + 1) >> 1, (sl + 1) & 1);
+        }
 #pragma unroll
-        for (int k = 0; k < kOps; ++k) {
-          if (gm == (k * 32) / kOps + 1) {
-            __builtin_amdgcn_sched_barrier(0);
-            issue_op(k, nstage, nA, nstep);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int mm = 0; mm < 2 * NSA; ++mm) {
+          const int f = mm / NSA, S = mm % NSA, gm = sl * 2 * NSA + mm;
+          f32x16_t& c = acc[f][S];
+          if constexpr (DT == DT_NVFP4)
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16((f16x8_t)af[sl & 1][f], (f16x8_t)bf[sl & 1][S], c, 0, 0, 0);
+          else
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16((bf16x8_t)af[sl & 1][f], (bf16x8_t)bf[sl & 1][S], c, 0, 0, 0);
+#pragma unroll
+          for (int k = 0; k < kOps; ++k) {
+            if (gm == (k * kMfma) / kOps) {
+              __builtin_amdgcn_sched_barrier(0);
+              issue_op(k, nstage, nA, nstep);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }
-    }
-  };
+    };
 
-  // prologue: steps 0 .. NS-2 in flight (every wave issues the same number
-  // of operations each step, clamped to the last step past the end)
-  PfA<DT> A[kPfStages];
+    // prologue: steps 0 .. NS-2 in flight (every wave issues the same number
+    // of operations each step, clamped to the last step past the end)
+    PfA<DT> A[kPfStages];
 #pragma unroll
-  for (int i = 0; i < kPfStages - 1; ++i) {
-    issue_all(*st.s[i], A[i], min(i, KS - 1));
-    asm volatile("" ::: "memory");  // each step's operations issue after the previous step's
-  }
-  int s = 0;
-  for (; s + kPfStages <= KS; s += kPfStages) {
+    for (int i = 0; i < kPfStages - 1; ++i) {
+      issue_all(*st.s[i], A[i], min(i, KS - 1));
+      asm volatile("" ::: "memory");  // each step's operations issue after the previous step's
+    }
+    int s = 0;
+    for (; s + kPfStages <= KS; s += kPfStages) {
 #pragma unroll
-    for (int u = 0; u < kPfStages; ++u) {
-      // step s+u has landed once at most the NS-2 newer steps are in flight
-      pf_wait_barrier<kOps * (kPfStages - 2)>();
-      pf_pin(A[u]);
-      const int nxt = (u + kPfStages - 1) % kPfStages;
-      step_body(*st.s[u], A[u], s + u, *st.s[nxt], A[nxt], min(s + u + kPfStages - 1, KS - 1));
+      for (int u = 0; u < kPfStages; ++u) {
+        // step s+u has landed once at most the NS-2 newer steps are in flight
+        pf_wait_barrier<kOps * (kPfStages - 2)>();
+        pf_pin(A[u]);
+        const int nxt = (u + kPfStages - 1) % kPfStages;
+        step_body(*st.s[u], A[u], s + u, *st.s[nxt], A[nxt], min(s + u + kPfStages - 1, KS - 1));
+      }
+    }
+    if (s < KS) {  // the last KS % NS steps; every body still issues its (clamped) operations
+#pragma unroll
+      for (int u = 0; u < kPfStages - 1; ++u) {
+        pf_wait_barrier<kOps * (kPfStages - 2)>();
+        pf_pin(A[u]);
+        const int nxt = (u + kPfStages - 1) % kPfStages;
+        const int nstep = min(s + u + kPfStages - 1, KS - 1);
+        if (s + u < KS) step_body(*st.s[u], A[u], s + u, *st.s[nxt], A[nxt], nstep);
+        else issue_all(*st.s[nxt], A[nxt], nstep);
+      }
+    }
+    pf_wait_barrier<0>();
+    if constexpr (NSA > 0)
+      if (g < a.G) pf_epilogue<DT, G13, NSA, kSW>(a, acc, r0 + 32 * th * kSW, r_end, g, e, lane);
+  };
+  // this wave's active 32-row sub-tiles (uniform across the wave)
+  const int nsa = min(kSW, max(0, ((r_end - r0 + 31) >> 5) - th * kSW));
+  if constexpr (TW == 1) {
+    switch (nsa) {
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      default: run(std::integral_constant<int, 4>{}); break;
+    }
+  } else {
+    switch (nsa) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      default: run(std::integral_constant<int, 2>{}); break;
     }
   }
-  if (s < KS) {  // the last KS % NS steps; every body still issues its (clamped) operations
-#pragma unroll
-    for (int u = 0; u < kPfStages - 1; ++u) {
-      pf_wait_barrier<kOps * (kPfStages - 2)>();
-      pf_pin(A[u]);
-      const int nxt = (u + kPfStages - 1) % kPfStages;
-      const int nstep = min(s + u + kPfStages - 1, KS - 1);
-      if (s + u < KS) step_body(*st.s[u], A[u], s + u, *st.s[nxt], A[nxt], nstep);
-      else issue_all(*st.s[nxt], A[nxt], nstep);
-    }
-  }
-  pf_wait_barrier<0>();
-  if (g < a.G) pf_epilogue<DT, G13>(a, acc, r0, r_end, g, e, lane);
   // Drain the epilogue's stores: with stores and loads both pending, the
   // shared vector-memory counter no longer counts loads in order, and the
   // compiler would wait for everything at the next item's K-loop head.
