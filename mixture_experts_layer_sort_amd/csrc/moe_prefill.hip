@@ -15,7 +15,7 @@ template <int DT, bool G13>
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmArgs a) {
   __shared__ int cum[1025];
   __shared__ int wsum[4];
-  const PfStages st = pf_make_stages<pf_stages<DT>()>();
+  const auto st = pf_make_stages<DT>();
   const int total_mt = build_schedule(a.offsets, a.E, kPfRows, cum, wsum);
   const long long total = (long long)total_mt * ((a.G + kPfGroups - 1) / kPfGroups);
   for (long long w = xcd_logical_block(); w < total; w += gridDim.x) prefill_item<DT, G13, 2>(a, w, cum, st);

@@ -33,7 +33,7 @@ namespace moe {
 constexpr int kPfRows = 128;                  // routed rows per item: 4 sub-tiles of 32
 constexpr int kPfGroups = 4;                  // weight row groups per item, one per wave
 constexpr int kPfBand = 8;                    // m-tiles per band of the item order
-constexpr int kPfStageSlots = 8 * 2 * 64;     // token stage: 8 blocks of 32 rows x 32 K, 16-byte slots (16 KB)
+constexpr int kPfTokSlots = 8 * 2 * 64;       // token part of a stage: 8 blocks of 32 rows x 32 K, 16-byte slots (16 KB)
 #ifndef MOE_PF_STAGES_Q
 #define MOE_PF_STAGES_Q 4  // pipeline depth for MXFP8 / NVFP4 weights
 #endif
@@ -44,7 +44,16 @@ constexpr int kPfMaxStages = 8;
 template <int DT>
 constexpr int pf_stages() { return DT == DT_BF16 ? 3 : MOE_PF_STAGES_Q; }
 
-// weight loads per wave per K step
+// Weights of MXFP8 items also go through LDS (direct loads in fragment
+// order, shared by the two waves of a row group): the per-instruction cost of
+// the address unit, not bytes, bounds the loads, and this halves their count.
+template <int DT>
+constexpr bool pf_alds() { return DT == DT_MXFP8; }
+// 16-byte slots of one stage: tokens, then for LDS weights the codes
+// [group 4][f 2][m 2][64 lanes] (16 KB) and per-wave scale copies [wave 8][64 words]
+template <int DT>
+constexpr int pf_stage_slots() { return pf_alds<DT>() ? kPfTokSlots + 1024 + 128 : kPfTokSlots; }
+// weight loads per wave per K step (register path)
 template <int DT>
 constexpr int pf_a_ops() { return DT == DT_BF16 ? 8 : 6; }
 
@@ -108,26 +117,28 @@ __device__ __forceinline__ void pf_pin(PfA<DT>& A) {
 // The token stages of one block: separate LDS objects, so the compiler's
 // waits for the direct loads track each stage on its own.  Each index is
 // one allocation per kernel, shared by every item the kernel runs.
+template <int SLOTS>
 struct PfStages {
-  u32x4_t (*s[kPfMaxStages])[kPfStageSlots];
+  u32x4_t (*s[kPfMaxStages])[SLOTS];
 };
-template <int I>
-__device__ __forceinline__ u32x4_t (*pf_stage())[kPfStageSlots] {
-  __shared__ u32x4_t buf[kPfStageSlots];
+template <int I, int SLOTS>
+__device__ __forceinline__ u32x4_t (*pf_stage())[SLOTS] {
+  __shared__ u32x4_t buf[SLOTS];
   return &buf;
 }
-template <int NS>
-__device__ __forceinline__ PfStages pf_make_stages() {
+template <int DT>
+__device__ __forceinline__ PfStages<pf_stage_slots<DT>()> pf_make_stages() {
+  constexpr int NS = pf_stages<DT>(), SL = pf_stage_slots<DT>();
   static_assert(NS >= 3 && NS <= kPfMaxStages, "stages");
-  PfStages st{};
-  st.s[0] = pf_stage<0>();
-  st.s[1] = pf_stage<1>();
-  st.s[2] = pf_stage<2>();
-  if constexpr (NS > 3) st.s[3] = pf_stage<3>();
-  if constexpr (NS > 4) st.s[4] = pf_stage<4>();
-  if constexpr (NS > 5) st.s[5] = pf_stage<5>();
-  if constexpr (NS > 6) st.s[6] = pf_stage<6>();
-  if constexpr (NS > 7) st.s[7] = pf_stage<7>();
+  PfStages<SL> st{};
+  st.s[0] = pf_stage<0, SL>();
+  st.s[1] = pf_stage<1, SL>();
+  st.s[2] = pf_stage<2, SL>();
+  if constexpr (NS > 3) st.s[3] = pf_stage<3, SL>();
+  if constexpr (NS > 4) st.s[4] = pf_stage<4, SL>();
+  if constexpr (NS > 5) st.s[5] = pf_stage<5, SL>();
+  if constexpr (NS > 6) st.s[6] = pf_stage<6, SL>();
+  if constexpr (NS > 7) st.s[7] = pf_stage<7, SL>();
   return st;
 }
 
@@ -254,11 +265,16 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
 // accumulator registers), so two waves fit per SIMD and one wave's LDS
 // reads, loads and converts overlap the other's MFMAs.
 template <int DT, bool G13, int TW>
-__device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, const int* cum, const PfStages& st) {
+__device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, const int* cum,
+                                            const PfStages<pf_stage_slots<DT>()>& st) {
   static_assert(TW == 1 || TW == 2, "waves along tokens");
+  constexpr bool kALds = pf_alds<DT>();
+  constexpr int kSlots = pf_stage_slots<DT>();
   constexpr int kSW = 4 / TW;                       // token sub-tiles per wave
   constexpr int kDma = 4 / TW;                      // token loads per wave per K step (16 per block)
-  constexpr int kOps = pf_a_ops<DT>() + kDma;       // vector-memory operations per wave per K step
+  constexpr int kADma = 4 / TW;                     // LDS weights: code loads per wave per K step (16 per block)
+  // vector-memory operations per wave per K step
+  constexpr int kOps = kDma + (kALds ? kADma + 1 : pf_a_ops<DT>());
   constexpr int kPfStages = pf_stages<DT>();
   const int tid = threadIdx.x, lane = tid & 63, i16 = lane & 15, hl = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wg = wv & 3, th = wv >> 2;
@@ -305,7 +321,7 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
 
   // Vector-memory operation k of K step `step`: k < kDma a token load into
   // `stage`; k >= kDma a piece of the weights into A.
-  auto issue_op = [&](int k, u32x4_t(&stage)[kPfStageSlots], PfA<DT>& A, int step) {
+  auto issue_op = [&](int k, u32x4_t(&stage)[kSlots], PfA<DT>& A, int step) {
     if (k < kDma) {
       const int d = wv * kDma + k, cc = (d >> 1) & 1, half = k & 1;
       __builtin_amdgcn_global_load_lds(bsrc[half] + step * 128 + cc * 64, &stage[((2 * dS + cc) * 2 + half) * 64], 16,
@@ -314,6 +330,19 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
     }
     const int kg = step >> 1, h = step & 1, idx = k - kDma;
     const size_t tk = (size_t)kg * 4;  // tile offset of the kgroup
+    if constexpr (kALds) {
+      if (idx < kADma) {
+        // codes of fragment pair (f, m) of this row group, in fragment-lane order
+        const int f = TW == 2 ? th : (idx >> 1), m = TW == 2 ? idx : (idx & 1);
+        __builtin_amdgcn_global_load_lds(wc + (tk + 2 * f) * tcode + h * 1024 + m * 512,
+                                         &stage[kPfTokSlots + ((wg * 2 + f) * 2 + m) * 64], 16, 0, 0);
+      } else {
+        // this wave's copy of the group's 4 tile scale blocks (256 contiguous bytes)
+        __builtin_amdgcn_global_load_lds(a.wscales + (tile0 + tk) * tscale + lane * 4,
+                                         &stage[kPfTokSlots + 1024 + wv * 16], 4, 0, 0);
+      }
+      return;
+    }
     if constexpr (DT == DT_BF16) {
       const int f = idx >> 2, cc = (idx >> 1) & 1, m = idx & 1;
       A.c[f][cc][m] = *reinterpret_cast<const u32x4_t*>(wc + (tk + 2 * f) * tcode + (2 * h + cc) * 1024 + m * 512);
@@ -328,7 +357,7 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
       A.s[f] = *reinterpret_cast<const uint32_t*>(ws + (tk + 2 * f) * tscale + (DT == DT_MXFP8 ? 0 : 4 * h));
     }
   };
-  auto issue_all = [&](u32x4_t(&stage)[kPfStageSlots], PfA<DT>& A, int step) {
+  auto issue_all = [&](u32x4_t(&stage)[kSlots], PfA<DT>& A, int step) {
 #pragma unroll
     for (int k = 0; k < kOps; ++k) issue_op(k, stage, A, step);
   };
@@ -362,31 +391,69 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
       }
     };
     // token fragments of the active sub-tiles, K slice (chunk cc, m)
-    auto read_b = [&](u32x4_t(&bf)[kSW], const u32x4_t(&stage)[kPfStageSlots], int cc, int m) {
+    auto read_b = [&](u32x4_t(&bf)[kSW], const u32x4_t(&stage)[kSlots], int cc, int m) {
 #pragma unroll
       for (int S = 0; S < NSA; ++S) bf[S] = stage[(2 * (th * kSW + S) + cc) * 128 + boff[m]];
     };
 
-    // One K step: 4 K slices x 2 NSA MFMAs on `stage` / A, the next slice's
-    // operands fetched ahead, and the loads of step `nstep` spread between
-    // the MFMAs so the memory pipeline accepts them while the matrix unit is
-    // busy.
-    auto step_body = [&](const u32x4_t(&stage)[kPfStageSlots], const PfA<DT>& A, int step,
-                         u32x4_t(&nstage)[kPfStageSlots], PfA<DT>& nA, int nstep) {
+    // Operands of slice 0 of a step, read ahead across the step boundary:
+    // the LDS weights (codes and scales) and the first token fragments.
+    struct Carry {
+      PfA<DT> AL;
+      u32x4_t bf0[kSW];
+    };
+    auto prefetch = [&](Carry& cr, const u32x4_t(&stage)[kSlots]) {
+      if constexpr (kALds) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) cr.AL.c[f][m] = stage[kPfTokSlots + ((wg * 2 + f) * 2 + m) * 64 + lane];
+          cr.AL.s[f] = reinterpret_cast<const uint32_t*>(&stage[kPfTokSlots + 1024 + wv * 16])[(2 * f + ltile) * 16 + i16];
+        }
+      }
+      read_b(cr.bf0, stage, 0, 0);
+    };
+    // loads issued before the mid-step barrier (interleave positions in slices 0..2)
+    constexpr int kMidOps = [] {
+      int n = 0;
+      for (int k = 0; k < kOps; ++k)
+        if (NSA == 0 || (k * kMfma) / kOps < 6 * NSA) ++n;
+      return n;
+    }();
+    // Step t needs step t+1 landed (for every wave) at its mid barrier: at
+    // most the NS-3 steps after t+1 and the part of step t+NS-1 issued so far
+    // may still be in flight.
+    constexpr int kMidWait = kOps * (kPfStages - 3) + kMidOps;
+
+    // One K step: 4 K slices x 2 NSA MFMAs on `stage` / A, each slice's
+    // operands fetched one slice ahead, the loads of step `nstep` spread
+    // between the MFMAs so the memory pipeline accepts them while the matrix
+    // unit is busy.  After slice 2: wait for step t+1, barrier, and read its
+    // slice-0 operands (from `next`) while slice 3 computes.
+    auto step_body = [&](const u32x4_t(&stage)[kSlots], const PfA<DT>& A, int step, Carry& cr,
+                         const u32x4_t(&next)[kSlots], PfA<DT>& nextA, u32x4_t(&nstage)[kSlots], PfA<DT>& nA,
+                         int nstep) {
       if constexpr (NSA == 0) {
         issue_all(nstage, nA, nstep);
+        pf_wait_barrier<kMidWait>();
         return;
       }
       const int h = step & 1;
       op_t af[2][2];
       u32x4_t bf[2][kSW];
-      convert(af[0], A, h, 0, 0);
-      read_b(bf[0], stage, 0, 0);
+      const PfA<DT>& Aop = kALds ? cr.AL : A;
+      convert(af[0], Aop, h, 0, 0);
+#pragma unroll
+      for (int S = 0; S < NSA; ++S) bf[0][S] = cr.bf0[S];
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
         if (sl < 3) {
           read_b(bf[(sl + 1) & 1], stage, (sl + 1) >> 1, (sl + 1) & 1);
-          convert(af[(sl + 1) & 1], A, h, (sl + 1) >> 1, (sl + 1) & 1);
+          convert(af[(sl + 1) & 1], Aop, h, (sl + 1) >> 1, (sl + 1) & 1);
+        } else {
+          pf_wait_barrier<kMidWait>();
+          if constexpr (!kALds) pf_pin(nextA);
+          prefetch(cr, next);
         }
 #pragma unroll
         for (int mm = 0; mm < 2 * NSA; ++mm) {
@@ -409,33 +476,39 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
     };
 
     // prologue: steps 0 .. NS-2 in flight (every wave issues the same number
-    // of operations each step, clamped to the last step past the end)
+    // of operations each step, clamped to the last step past the end), then
+    // wait for step 0 and read its slice-0 operands
     PfA<DT> A[kPfStages];
 #pragma unroll
     for (int i = 0; i < kPfStages - 1; ++i) {
       issue_all(*st.s[i], A[i], min(i, KS - 1));
       asm volatile("" ::: "memory");  // each step's operations issue after the previous step's
     }
+    Carry cr;
+    pf_wait_barrier<kOps * (kPfStages - 2)>();
+    if constexpr (!kALds) pf_pin(A[0]);
+    prefetch(cr, *st.s[0]);
     int s = 0;
     for (; s + kPfStages <= KS; s += kPfStages) {
 #pragma unroll
       for (int u = 0; u < kPfStages; ++u) {
-        // step s+u has landed once at most the NS-2 newer steps are in flight
-        pf_wait_barrier<kOps * (kPfStages - 2)>();
-        pf_pin(A[u]);
         const int nxt = (u + kPfStages - 1) % kPfStages;
-        step_body(*st.s[u], A[u], s + u, *st.s[nxt], A[nxt], min(s + u + kPfStages - 1, KS - 1));
+        step_body(*st.s[u], A[u], s + u, cr, *st.s[(u + 1) % kPfStages], A[(u + 1) % kPfStages], *st.s[nxt], A[nxt],
+                  min(s + u + kPfStages - 1, KS - 1));
       }
     }
-    if (s < KS) {  // the last KS % NS steps; every body still issues its (clamped) operations
+    if (s < KS) {  // the last KS % NS steps; every body still issues its (clamped) operations and barrier
 #pragma unroll
       for (int u = 0; u < kPfStages - 1; ++u) {
-        pf_wait_barrier<kOps * (kPfStages - 2)>();
-        pf_pin(A[u]);
         const int nxt = (u + kPfStages - 1) % kPfStages;
         const int nstep = min(s + u + kPfStages - 1, KS - 1);
-        if (s + u < KS) step_body(*st.s[u], A[u], s + u, *st.s[nxt], A[nxt], nstep);
-        else issue_all(*st.s[nxt], A[nxt], nstep);
+        if (s + u < KS) {
+          step_body(*st.s[u], A[u], s + u, cr, *st.s[(u + 1) % kPfStages], A[(u + 1) % kPfStages], *st.s[nxt], A[nxt],
+                    nstep);
+        } else {
+          issue_all(*st.s[nxt], A[nxt], nstep);
+          pf_wait_barrier<kMidWait>();
+        }
       }
     }
     pf_wait_barrier<0>();
