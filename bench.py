@@ -29,6 +29,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # dense MFMA peak of the arithmetic the contraction runs in: bf16 MFMA for bf16
 # and MXFP8 (exact fp8 -> bf16), fp16 MFMA for NVFP4 (exact e2m1 x e4m3 -> fp16)
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 2500.0, "nvfp4": 2500.0}
+# the arithmetic type of the contractions per weight format
+ARITH_DTYPE = {"bf16": "bf16", "mxfp8": "bf16", "nvfp4": "f16"}
 FP8_PEAK_TFLOPS = 5000.0
 DEFAULT_WORKLOAD = "bf16_decode"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -308,7 +310,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": ARITH_DTYPE[w.dtype],
         "data": "synthetic (seeded N(0,1) x and logits, N(0,0.02) weights; random init)",
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.k,
                    "weights": w.dtype, "routing_skew": w.bias, "active_experts": n_active},
