@@ -6,12 +6,16 @@ One step = one pass of the whole layer over one batch (route -> permute +
 activation quantisation -> gate/up GEMM + SwiGLU + requant -> down GEMM ->
 combine), i.e. one moe_forward call, with inputs and prepared weights already resident in HBM.  The default
 workload is the bf16 decode layer (T=64, H=4096, I=1408, E=64, top-6).
-Prints one JSON line with tokens/s (K steps of moe_forward: the five stage
-kernels back to back on torch's stream, no events between them), the
-roofline of the dominant kernel (the gate/up GEMM, timed with HIP events on
-its launch stream over a second region of K steps through the staged entry
-points), whole-layer HBM / MFMA fractions, the single-launch entry's step
-time, and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line with tokens/s (K steps of moe_forward, the five stage
+kernels back to back on torch's stream, each step between HIP events, with
+the L2 and the Infinity Cache flushed by reading 1 GiB before every step
+outside the timed intervals), the roofline of the dominant kernel (the
+gate/up GEMM, timed with HIP events on its launch stream over a second
+region of K steps through the staged entry points, flushed the same way),
+whole-layer HBM / MFMA fractions, the back-to-back (unflushed) step time,
+the single-launch entry's step time, measured achievable peaks (device copy
+GB/s, a register-only MFMA loop) and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -191,6 +195,46 @@ def cpu_baseline(w, device, ids, max_seconds=25.0):
                       f"{dt:.1f} s wall, weight quantisation excluded"}
 
 
+def measure_achievable(torch, device):
+    """Measured context for the peaks: a 1 GiB device-to-device copy (GB/s of
+    read + write traffic) and a register-only loop of 32x32x16 bf16 MFMAs
+    (the contraction the prefill GEMM uses) at one and two blocks per CU."""
+    import ctypes
+
+    res = {}
+    a = torch.empty(1 << 28, dtype=torch.float32, device=device)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    res["device_copy_gbs"] = 5 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    path = os.path.join(ROOT, "mixture_experts_layer_sort_amd", "libmoe_probe.so")
+    if os.path.exists(path):
+        probe = ctypes.CDLL(path)
+        cus = torch.cuda.get_device_properties(device).multi_processor_count
+        out = torch.empty(2 * cus * 256, dtype=torch.float32, device=device)
+        stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+        best, iters = 0.0, 4000
+        for bpc in (1, 2):
+            blocks = bpc * cus
+            probe.moe_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, 100, stream)
+            e0.record()
+            rc = probe.moe_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, iters, stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc == 0:
+                flops = blocks * 4 * iters * 8 * 32768.0
+                best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        res["mfma_bf16_32x32x16_loop_tflops"] = best
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +276,16 @@ def main():
     def forward():
         lib.moe_forward(layer.shape, w.T, layer.packed, logits, x, out, layer.ws, topk_ids=ids_t, topk_w=wts_t)
 
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=device)  # 1 GiB
+    flush_sink = torch.empty((), dtype=torch.float32, device=device)
+
+    def flush(i):
+        # Evict the L2s and the 256 MB Infinity Cache by reading 1 GiB, enqueued
+        # outside the timed intervals.  A read, not a write: a write leaves the
+        # memory-side cache full of dirty lines whose write-back then competes
+        # with the next step's reads (measured: -20 % on NVFP4 decode).
+        flush_sink.copy_(flush_buf.sum())
+
     for _ in range(args.warmup):
         forward()
     torch.cuda.synchronize()
@@ -239,29 +293,43 @@ def main():
     n_active = int(len(np.unique(ids)))
 
     # timed region: K steps of moe_forward (five kernels each) on torch's stream,
-    # one HIP event pair around the whole region; no events between kernels
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # each step between its own HIP event pair, caches flushed before every step
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    for i in range(args.steps):
+        flush(i)
+        starts[i].record()
+        forward()
+        ends[i].record()
+    torch.cuda.synchronize()
+    step_ms = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    ms_step = step_ms[len(step_ms) // 2]  # median
+    gpu_ms_step = ms_step
+
+    # back to back, unflushed (context): one event pair around K steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for _ in range(args.steps):
         forward()
     ev1.record()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = 1e3 * elapsed / args.steps
-    gpu_ms_step = ev0.elapsed_time(ev1) / args.steps
+    b2b_ms_step = ev0.elapsed_time(ev1) / args.steps
 
     # kernel timing region: K steps of the same kernels through the staged entry
-    # points, HIP events around every kernel (the events themselves add gaps)
+    # points, HIP events around every kernel (the events themselves add gaps),
+    # caches flushed before every step
     step = StagedStep(lib, layer, x, logits)
     for _ in range(3):
         step.run()
     torch.cuda.synchronize()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        flush(i)
         step.run(timed=True)
     torch.cuda.synchronize()
     kms = step.kernel_ms()
+    del flush_buf
+    achievable = measure_achievable(torch, device)
 
     # the single-launch entry, for comparison
     def fused():
@@ -320,7 +388,10 @@ def main():
                   "mfma_frac": tflops / MFMA_PEAK_TFLOPS[w.dtype],
                   "mfma_frac_of_fp8_peak": tflops / FP8_PEAK_TFLOPS if w.dtype == "mxfp8" else None,
                   "regime": "decode" if decode else "prefill", "staged_kernel_ms": kms,
+                  "step_ms_min_median_max": [step_ms[0], ms_step, step_ms[-1]],
+                  "back_to_back_unflushed_ms_per_step": b2b_ms_step,
                   "single_launch_ms_per_step": fused_ms},
+        "achievable": achievable,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, device, ids)

@@ -37,10 +37,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the MoE library)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source under csrc/ into LIB_PATH; returns its path."""
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB_PATH + ".tmp"
+PROBE_DIR = os.path.join(PKG_DIR, "probe")
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libmoe_probe.so")
+
+
+def _compile(srcs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", os.path.join(PKG_DIR, "..", "include"), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -48,7 +50,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed with status {r.returncode}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source under csrc/ into LIB_PATH (and the benchmark's
+    roofline probe into PROBE_LIB_PATH); returns LIB_PATH."""
+    _compile(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), LIB_PATH, verbose)
+    _compile(sorted(glob.glob(os.path.join(PROBE_DIR, "*.hip"))), PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 
