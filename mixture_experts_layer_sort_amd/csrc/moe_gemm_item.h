@@ -125,7 +125,12 @@ struct KW {  // words per lane per tile: codes (uint4) / scales (dwords)
 template <int DT, int NT>
 struct KFrag {
   uint4 ac[4][KW<DT>::A];
-  uint32_t as[4][KW<DT>::AS];
+  // the 4 tiles' scale rows of the kgroup, one per lane: lane L holds tile
+  // L / 16, row L % 16 (the tiles' scale blocks are contiguous); each lane
+  // takes its own rows from the right lanes when it converts (one load per
+  // kgroup instead of one per tile: the address unit's per-instruction cost
+  // bounds the decode loads)
+  uint32_t as[KW<DT>::AS];
   uint4 bc[NT][4];  // 16-bit activation operand, 4 chunks of 8
 };
 
@@ -154,13 +159,16 @@ __device__ __forceinline__ void load_kfrag(KFrag<DT, NT>& f, const GemmArgs& a, 
     } else if constexpr (DT == DT_MXFP8) {
       f.ac[t][0] = ld_w16<NTLD>(pc + lane * 16);
       f.ac[t][1] = ld_w16<NTLD>(pc + 1024 + lane * 16);
-      f.as[t][0] = *reinterpret_cast<const uint32_t*>(a.wscales + (tile0 + t) * tscale + i16 * 4);
     } else {
       f.ac[t][0] = ld_w16<NTLD>(pc + lane * 16);
-      const uint2 sv = *reinterpret_cast<const uint2*>(a.wscales + (tile0 + t) * tscale + i16 * 8);
-      f.as[t][0] = sv.x;
-      f.as[t][1] = sv.y;
     }
+  }
+  if constexpr (DT == DT_MXFP8) {
+    f.as[0] = *reinterpret_cast<const uint32_t*>(a.wscales + tile0 * tscale + lane * 4);
+  } else if constexpr (DT == DT_NVFP4) {
+    const uint2 sv = *reinterpret_cast<const uint2*>(a.wscales + tile0 * tscale + lane * 8);
+    f.as[0] = sv.x;
+    f.as[1] = sv.y;
   }
 #pragma unroll
   for (int s = 0; s < NT; ++s) {
@@ -177,13 +185,22 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
 
 template <int DT, int NT>
 __device__ __forceinline__ void mma_kfrag(f32x4_t (&acc)[4][NT], const KFrag<DT, NT>& f, int q) {
+  // this lane's scale words of tile t (row lane % 16) from lane 16 t + lane % 16
+  uint32_t st[4][KW<DT>::AS];
+  if constexpr (DT != DT_BF16) {
+    const int i16 = __lane_id() & 15;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int w = 0; w < KW<DT>::AS; ++w) st[t][w] = (uint32_t)__shfl((int)f.as[w], 16 * t + i16, 64);
+  }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if constexpr (DT == DT_NVFP4) {
         const int sb = 2 * c + (q >> 1);  // 16-block of this lane's 8 k's
-        const uint32_t sw = sb < 4 ? f.as[t][0] : f.as[t][1];
+        const uint32_t sw = sb < 4 ? st[t][0] : st[t][1];
         const f16x8_t A = nvfp4_dequant8(u4_word(f.ac[t][0], c), (sw >> (8 * (sb & 3))) & 0xFF);
 #pragma unroll
         for (int s = 0; s < NT; ++s) {
@@ -197,8 +214,8 @@ __device__ __forceinline__ void mma_kfrag(f32x4_t (&acc)[4][NT], const KFrag<DT,
           __builtin_memcpy(&A, &f.ac[t][c], 16);
         } else {
           const uint4& v = f.ac[t][c >> 1];
-          A = (c & 1) ? mxfp8_dequant8(v.z, v.w, (f.as[t][0] >> (8 * c)) & 0xFF)
-                      : mxfp8_dequant8(v.x, v.y, (f.as[t][0] >> (8 * c)) & 0xFF);
+          A = (c & 1) ? mxfp8_dequant8(v.z, v.w, (st[t][0] >> (8 * c)) & 0xFF)
+                      : mxfp8_dequant8(v.x, v.y, (st[t][0] >> (8 * c)) & 0xFF);
         }
 #pragma unroll
         for (int s = 0; s < NT; ++s) {
