@@ -21,6 +21,22 @@
 
 namespace moe {
 
+__device__ __forceinline__ void set_wave_priority(int p) {
+  switch (p) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
+// Every block gets the same number of items, so a compute unit finishes with
+// its slowest resident block.  Measured on MI355X, the blocks placed later on
+// a compute unit (higher block ids: the first 256 blocks take one unit each,
+// the next 256 a second slot, ...) stream ~25 % slower than the first, as the
+// older waves win the issue arbitration.  Each block therefore rotates its
+// waves' priority by item, starting from its slot, so the blocks of one unit
+// take turns at the top priority (3-4 % faster MXFP8 / NVFP4 decode GEMMs).
 template <int DT, int NT, bool G13>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
   __shared__ int cum[1025];
@@ -28,7 +44,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
   __shared__ f32x4_t red[3][4 * NT][64];
   const int total_mt = build_schedule(a.offsets, a.E, 16 * NT, cum, wsum);
   const long long total = (long long)total_mt * a.G;
-  for (long long w = blockIdx.x; w < total; w += gridDim.x) gemm_item<DT, NT, G13>(a, w, cum, red);
+  int turn = (int)(blockIdx.x >> 8);
+  for (long long w = blockIdx.x; w < total; w += gridDim.x, ++turn) {
+    set_wave_priority(turn & 3);
+    gemm_item<DT, NT, G13>(a, w, cum, red);
+  }
 }
 
 // ------------------------------------------------------------------ prepare (repack)
