@@ -13,6 +13,8 @@ outside the timed intervals), the roofline of the dominant kernel (the
 gate/up GEMM, timed with HIP events on its launch stream over a second
 region of K steps through the staged entry points, flushed the same way),
 whole-layer HBM / MFMA fractions, the back-to-back (unflushed) step time,
+the step time when the same moe_forward call is captured into a HIP graph
+and replayed,
 the single-launch entry's step time, measured achievable peaks (device copy
 GB/s, a register-only MFMA loop) and the CPU oracle timed on a bounded
 sample of the same workload.
@@ -311,6 +313,28 @@ def main():
     ms_step = step_ms[len(step_ms) // 2]  # median
     gpu_ms_step = ms_step
 
+    # the same step captured once into a HIP graph and replayed (context):
+    # flushed and timed like the eager steps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        forward()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        forward()
+    g_ms = []
+    for i in range(args.steps):
+        flush(i)
+        starts[i].record()
+        graph.replay()
+        ends[i].record()
+    torch.cuda.synchronize()
+    g_ms = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    graph_ms_step = g_ms[len(g_ms) // 2]
+    del graph
+
     # back to back, unflushed (context): one event pair around K steps
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
@@ -394,6 +418,7 @@ def main():
                   "regime": "decode" if decode else "prefill", "staged_kernel_ms": kms,
                   "step_ms_min_median_max": [step_ms[0], ms_step, step_ms[-1]],
                   "back_to_back_unflushed_ms_per_step": b2b_ms_step,
+                  "graph_replay_ms_per_step": graph_ms_step,
                   "single_launch_ms_per_step": fused_ms},
         "achievable": achievable,
     }

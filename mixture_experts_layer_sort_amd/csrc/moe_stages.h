@@ -81,8 +81,18 @@ __device__ void permute_block(const int* __restrict__ ids, int P, int E, int* __
   __syncthreads();
   const int S = ((P + kPermWaves * 64 - 1) / (kPermWaves * 64)) * 64;  // segment, multiple of 64
   const int seg0 = min(P, w * S), seg1 = min(P, (w + 1) * S);
-  // ids outside [0, E) are clamped: results are then unspecified but every access stays in bounds
-  for (int p = seg0 + lane; p < seg1; p += 64) atomicAdd(&hist[w][min(max(ids[p], 0), E - 1)], 1);
+  // ids outside [0, E) are clamped: results are then unspecified but every access stays in bounds.
+  // Loads go kAhead chunks of 64 at a time, so the wave waits for memory once per group, not per chunk.
+  // (Loads past the segment read a clamped in-bounds address and are discarded, so they need no branch.)
+  constexpr int kAhead = 16;
+  for (int p = seg0 + lane; p < seg1; p += 64 * kAhead) {
+    int v[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) v[u] = ids[min(p + 64 * u, P - 1)];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u)
+      if (p + 64 * u < seg1) atomicAdd(&hist[w][min(max(v[u], 0), E - 1)], 1);
+  }
   __syncthreads();
   // per-thread experts kPer*tid .. +kPer: totals, block exclusive scan
   int e0 = kPer * tid, local = 0;
@@ -120,24 +130,35 @@ __device__ void permute_block(const int* __restrict__ ids, int P, int E, int* __
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int p0 = seg0; p0 < seg1; p0 += 64) {
-    const int p = p0 + lane;
-    const bool valid = p < seg1;
-    const int id = valid ? min(max(ids[p], 0), E - 1) : 0;
-    unsigned long long m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      bool bit = (id >> b) & 1;
-      unsigned long long bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
+  // chunk c's ids are loaded while chunk c - kAhead is ranked (a ring of kAhead registers)
+  // (The wave's LDS operations complete in order, so each chunk sees the
+  // previous chunk's hist update without a fence.)
+  int ring[kAhead];
+  if (seg0 < seg1) {
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) ring[u] = ids[min(seg0 + 64 * u + lane, P - 1)];
+  }
+  for (int p0 = seg0; p0 < seg1; p0 += 64 * kAhead) {
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int p = p0 + 64 * u + lane;
+      if (p0 + 64 * u >= seg1) break;  // wave-uniform
+      const bool valid = p < seg1;
+      const int id = valid ? min(max(ring[u], 0), E - 1) : 0;
+      ring[u] = ids[min(p + 64 * kAhead, P - 1)];
+      unsigned long long m = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        bool bit = (id >> b) & 1;
+        unsigned long long bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      if (valid) {
+        int pos = hist[w][id] + __popcll(m & lt);
+        sorted_pairs[pos] = p;
+        pair_pos[p] = pos;
+        if (lane == 63 - __clzll(m)) hist[w][id] += __popcll(m);
+      }
     }
-    if (valid) {
-      int pos = hist[w][id] + __popcll(m & lt);
-      sorted_pairs[pos] = p;
-      pair_pos[p] = pos;
-      if (lane == 63 - __clzll(m)) hist[w][id] += __popcll(m);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
