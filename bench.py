@@ -34,22 +34,27 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # dense MFMA peak of the arithmetic the contraction runs in: bf16 MFMA for bf16
 # and MXFP8 (exact fp8 -> bf16), fp16 MFMA for NVFP4 (exact e2m1 x e4m3 -> fp16)
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 2500.0, "nvfp4": 2500.0}
-# the arithmetic type of the contractions per weight format
-ARITH_DTYPE = {"bf16": "bf16", "mxfp8": "bf16", "nvfp4": "f16"}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 2500.0, "nvfp4": 2500.0, "bf16_mxfp8": 2500.0}
+# the arithmetic type of the contractions per layer format ("bf16_mxfp8": bf16
+# activations over MXFP8 weights)
+ARITH_DTYPE = {"bf16": "bf16", "mxfp8": "bf16", "nvfp4": "f16", "bf16_mxfp8": "bf16"}
 FP8_PEAK_TFLOPS = 5000.0
 DEFAULT_WORKLOAD = "bf16_decode"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mixture_experts_layer_sort_amd", "csrc")
 
 
-def weight_bytes_per_elem(dtype):
+def _bytes_per_elem(fmt):
     # codes + block scales (MXFP8: 1 + 1/32, NVFP4: 1/2 + 1/16)
-    return {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32, "nvfp4": 0.5 + 1.0 / 16}[dtype]
+    return {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32, "nvfp4": 0.5 + 1.0 / 16}[fmt]
+
+
+def weight_bytes_per_elem(dtype):
+    return _bytes_per_elem("mxfp8" if dtype == "bf16_mxfp8" else dtype)
 
 
 def act_bytes_per_elem(dtype):
-    return weight_bytes_per_elem(dtype)
+    return _bytes_per_elem("bf16" if dtype == "bf16_mxfp8" else dtype)
 
 
 def kernel_source_hash():
@@ -113,7 +118,8 @@ class StagedStep:
         self.off = torch.empty(w.E + 1, dtype=torch.int32, device=d)
         self.sp = torch.empty(P, dtype=torch.int32, device=d)
         self.pp = torch.empty(P, dtype=torch.int32, device=d)
-        self.xq = x if w.dtype == "bf16" else torch.empty(lib.moe_xq_bytes(s, T), dtype=torch.uint8, device=d)
+        self.xq = x if w.dtype in ("bf16", "bf16_mxfp8") else torch.empty(lib.moe_xq_bytes(s, T), dtype=torch.uint8,
+                                                                          device=d)
         self.hq = torch.empty(lib.moe_hq_bytes(s, T), dtype=torch.uint8, device=d)
         self.y = torch.empty(P, w.H, dtype=torch.bfloat16, device=d)
         self.out = torch.empty(T, w.H, dtype=torch.bfloat16, device=d)
@@ -174,7 +180,7 @@ def cpu_baseline(w, device, ids, max_seconds=25.0):
     x = mi.device_x(w, device).view(torch.int16).cpu().numpy().view(np.uint16)
     logits = mi.device_logits(w, device).cpu().numpy()
     # sample size: tokens whose experts' dequantisation + products take ~10-25 s
-    per_expert_s = {"bf16": 0.25, "mxfp8": 2.0, "nvfp4": 2.5}[w.dtype] * (w.H * w.I) / (4096 * 1408)
+    per_expert_s = {"bf16": 0.25, "mxfp8": 2.0, "nvfp4": 2.5, "bf16_mxfp8": 2.0}[w.dtype] * (w.H * w.I) / (4096 * 1408)
     n = 0
     experts = set()
     while n < w.T:
@@ -414,7 +420,7 @@ def main():
         "layer": {"algorithmic_bytes": B, "flops": F, "gpu_ms_per_step": gpu_ms_step, "hbm_gbs": layer_gbs,
                   "hbm_frac": layer_gbs / HBM_PEAK_GBS, "mfma_tflops": tflops,
                   "mfma_frac": tflops / MFMA_PEAK_TFLOPS[w.dtype],
-                  "mfma_frac_of_fp8_peak": tflops / FP8_PEAK_TFLOPS if w.dtype == "mxfp8" else None,
+                  "mfma_frac_of_fp8_peak": tflops / FP8_PEAK_TFLOPS if w.dtype in ("mxfp8", "bf16_mxfp8") else None,
                   "regime": "decode" if decode else "prefill", "staged_kernel_ms": kms,
                   "step_ms_min_median_max": [step_ms[0], ms_step, step_ms[-1]],
                   "back_to_back_unflushed_ms_per_step": b2b_ms_step,

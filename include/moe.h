@@ -24,6 +24,13 @@
  *               global scale / fp4 max, alpha = 1 / global scale]:
  *               W13 u8 [E, 2I, H/2] + u8 [E, 2I, H/16] + f32 [E];
  *               W2  u8 [E, H, I/2]  + u8 [E, H, I/16]  + f32 [E].
+ *   MOE_BF16_MXFP8 : MXFP8 weights (as MOE_MXFP8) with bf16 activations: the
+ *               hidden states are not quantised and the intermediate is
+ *               rounded to bf16, as for MOE_BF16 (the pages list a bf16 x
+ *               MXFP8 MegaMoE entry, bf16_mxfp8_mega_moe, beside the three
+ *               formats [MegaMoE drop workflow, §1, the package exports]).
+ *               Weight buffers, moe_quantize_weights and moe_prepare_weights
+ *               are those of MOE_MXFP8; xq and hq are those of MOE_BF16.
  *   W13 rows [0, I) are the gate projection, rows [I, 2I) the up projection.
  *
  * Conventions of every entry point:
@@ -58,7 +65,7 @@ typedef struct ihipStream_t* hipStream_t;
 #define MOE_API
 #endif
 
-typedef enum { MOE_BF16 = 0, MOE_MXFP8 = 1, MOE_NVFP4 = 2 } moe_dtype;
+typedef enum { MOE_BF16 = 0, MOE_MXFP8 = 1, MOE_NVFP4 = 2, MOE_BF16_MXFP8 = 3 } moe_dtype;
 
 typedef enum {
   MOE_OK = 0,
@@ -95,14 +102,14 @@ MOE_API size_t moe_workspace_bytes(const moe_shape* shape);
  * (MXFP8, NVFP4) the exact dequantised values [T, H] as bf16 (MXFP8) or
  * fp16 (NVFP4) at moe_xq_dequant_offset(shape, T) — the operand the grouped
  * GEMM reads, produced once per token instead of once per expert tile.
- *   BF16: bf16 [T, H], no scales;  MXFP8: u8 [T, H] + e8m0 [T, H/32] + bf16;
+ *   BF16, BF16_MXFP8: bf16 [T, H], no scales;  MXFP8: u8 [T, H] + e8m0 [T, H/32] + bf16;
  *   NVFP4: packed e2m1 [T, H/2] + e4m3 [T, H/16] + fp16. */
 MOE_API size_t moe_xq_bytes(const moe_shape* shape, int32_t T);
 MOE_API size_t moe_xq_scale_offset(const moe_shape* shape, int32_t T);
 MOE_API size_t moe_xq_dequant_offset(const moe_shape* shape, int32_t T);
 /* Requantised intermediate of the T*k pairs in expert-sorted order
  * (moe_gemm13_swiglu_quant's hq), same scheme along I:
- *   BF16: bf16 [P, I];  MXFP8: u8 [P, I] + e8m0 [P, I/32] + bf16 [P, I];
+ *   BF16, BF16_MXFP8: bf16 [P, I];  MXFP8: u8 [P, I] + e8m0 [P, I/32] + bf16 [P, I];
  *   NVFP4: packed e2m1 [P, I/2] + e4m3 [P, I/16] + fp16 [P, I]  (P = T * k). */
 MOE_API size_t moe_hq_bytes(const moe_shape* shape, int32_t T);
 MOE_API size_t moe_hq_scale_offset(const moe_shape* shape, int32_t T);

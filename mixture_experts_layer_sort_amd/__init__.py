@@ -16,8 +16,9 @@ import os
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libmoe_mi355x.so")
 
-MOE_BF16, MOE_MXFP8, MOE_NVFP4 = 0, 1, 2
-DTYPES = {"bf16": MOE_BF16, "mxfp8": MOE_MXFP8, "nvfp4": MOE_NVFP4}
+MOE_BF16, MOE_MXFP8, MOE_NVFP4, MOE_BF16_MXFP8 = 0, 1, 2, 3
+# layer formats; "bf16_mxfp8" = bf16 activations over MXFP8 weights
+DTYPES = {"bf16": MOE_BF16, "mxfp8": MOE_MXFP8, "nvfp4": MOE_NVFP4, "bf16_mxfp8": MOE_BF16_MXFP8}
 
 EXPORTED = [
     "moe_status_string",

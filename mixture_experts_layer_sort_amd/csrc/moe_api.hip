@@ -31,6 +31,7 @@ int device_cu_count() {
 std::atomic<int> g_occ[kMaxDevices][3][2][3];
 
 int gemm_grid(int dt, bool g13, int T, int k, int E) {
+  dt = weight_dt(dt);  // the kernels are those of the weight format
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
   const int v = gemm_variant(T, k, E);
@@ -49,6 +50,7 @@ int gemm_grid(int dt, bool g13, int T, int k, int E) {
 std::atomic<int> g_fused_occ[kMaxDevices][3][3];
 
 int fused_grid(int dt, int T, int k, int E) {
+  dt = weight_dt(dt);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   const int v = gemm_variant(T, k, E);
@@ -62,7 +64,7 @@ int fused_grid(int dt, int T, int k, int E) {
 
 moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_INVALID_ARG;
-  if (s->dtype < MOE_BF16 || s->dtype > MOE_NVFP4) return MOE_ERR_UNSUPPORTED;
+  if (s->dtype < MOE_BF16 || s->dtype > MOE_BF16_MXFP8) return MOE_ERR_UNSUPPORTED;
   if (s->hidden <= 0 || s->inter <= 0 || s->hidden % 128 || s->inter % 128) return MOE_ERR_UNSUPPORTED;
   if (s->hidden > (1 << 20) || s->inter > (1 << 20)) return MOE_ERR_UNSUPPORTED;
   if (s->num_experts < 1 || s->num_experts > 1024) return MOE_ERR_UNSUPPORTED;
@@ -139,7 +141,8 @@ size_t moe_hq_scale_offset(const moe_shape* s, int32_t T) {
 
 moe_status moe_quantize_weights(int32_t dtype, int32_t count, int32_t rows, int32_t K, const float* w, void* codes,
                                 void* scales, float* alpha, hipStream_t stream) {
-  if (dtype < MOE_BF16 || dtype > MOE_NVFP4) return MOE_ERR_UNSUPPORTED;
+  if (dtype < MOE_BF16 || dtype > MOE_BF16_MXFP8) return MOE_ERR_UNSUPPORTED;
+  dtype = weight_dt(dtype);  // MOE_BF16_MXFP8 weights are MXFP8
   if (count < 0 || rows < 1 || K < 1) return MOE_ERR_INVALID_ARG;
   const int blk = dtype == MOE_MXFP8 ? 32 : (dtype == MOE_NVFP4 ? 16 : 8);
   if (K % blk) return MOE_ERR_UNSUPPORTED;
@@ -257,7 +260,7 @@ moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const 
   int32_t* offsets = (int32_t*)(base + W.offsets);
   int32_t* sorted_pairs = (int32_t*)(base + W.sorted_pairs);
   int32_t* pair_pos = (int32_t*)(base + W.pair_pos);
-  uint8_t* xq = dt == DT_BF16 ? (uint8_t*)x : base + W.xq;
+  uint8_t* xq = act_dt(dt) == DT_BF16 ? (uint8_t*)x : base + W.xq;  // bf16 activations are used in place
   uint8_t* hq = base + W.hq;
   uint16_t* y = (uint16_t*)(base + W.y);
   hipError_t e = launch_route(logits, T, E, k, ids, wts, stream);

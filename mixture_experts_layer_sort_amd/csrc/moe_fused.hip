@@ -200,14 +200,14 @@ hipError_t launch_fused(int dt, int E, int H, int I, int k, int T, const uint8_t
   f.offsets = reinterpret_cast<int*>(ws + W.offsets);
   f.sorted_pairs = reinterpret_cast<int*>(ws + W.sorted_pairs);
   f.pair_pos = reinterpret_cast<int*>(ws + W.pair_pos);
-  uint8_t* xq = dt == DT_BF16 ? const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(x)) : ws + W.xq;
+  uint8_t* xq = act_dt(dt) == DT_BF16 ? const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(x)) : ws + W.xq;
   uint8_t* hq = ws + W.hq;
   f.xq = xq;
   f.xq_scales = xq + act_scale_offset(dt, T, H);
   f.xq_deq = reinterpret_cast<uint16_t*>(xq + act_dequant_offset(dt, T, H));
   f.y = reinterpret_cast<uint16_t*>(ws + W.y);
   f.sync = reinterpret_cast<unsigned*>(ws + W.sync);
-  f.quant_x = dt != DT_BF16;
+  f.quant_x = act_dt(dt) != DT_BF16;
   f.T = T;
   f.E = E;
   f.H = H;
@@ -223,6 +223,7 @@ hipError_t launch_fused(int dt, int E, int H, int I, int k, int T, const uint8_t
   g.out = hq;
   g.out_scales = hq + act_scale_offset(dt, T * k, I);
   g.out_deq = reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
+  g.act_bf16 = dt == DT_BF16_MXFP8;
   g.E = E; g.K = H; g.G = L.G13; g.KG = L.KG13; g.k = k; g.n_out = I;
   GemmArgs& h = f.g2;
   h.wcodes = packed + L.w2_codes;
@@ -234,10 +235,11 @@ hipError_t launch_fused(int dt, int E, int H, int I, int k, int T, const uint8_t
   h.out = reinterpret_cast<uint8_t*>(f.y);
   h.out_scales = nullptr;
   h.out_deq = nullptr;
+  h.act_bf16 = dt == DT_BF16_MXFP8;
   h.E = E; h.K = I; h.G = L.G2; h.KG = L.KG2; h.k = k; h.n_out = H;
   (void)ws_bytes;
   void* args[] = {&f};
-  return hipLaunchCooperativeKernel(fused_ptr(dt, gemm_variant(T, k, E)), dim3(grid), dim3(kGemmThreads), args, 0,
+  return hipLaunchCooperativeKernel(fused_ptr(weight_dt(dt), gemm_variant(T, k, E)), dim3(grid), dim3(kGemmThreads), args, 0,
                                     s);
 }
 

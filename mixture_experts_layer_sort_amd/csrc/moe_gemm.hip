@@ -151,9 +151,10 @@ hipError_t launch_gemm13(int dt, int E, int H, int I, int k, int T, const uint8_
   a.out = hq;
   a.out_scales = hq + act_scale_offset(dt, T * k, I);
   a.out_deq = reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
+  a.act_bf16 = dt == DT_BF16_MXFP8;
   a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
-  if (gemm_prefill(T, k, E)) return launch_prefill(dt, true, a, grid, s);
-  return dispatch_gemm<true>(dt, gemm_nt(T, k, E), a, grid, s);
+  if (gemm_prefill(T, k, E)) return launch_prefill(weight_dt(dt), true, a, grid, s);
+  return dispatch_gemm<true>(weight_dt(dt), gemm_nt(T, k, E), a, grid, s);
 }
 
 hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const int* offsets,
@@ -169,9 +170,10 @@ hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t
   a.out = reinterpret_cast<uint8_t*>(y);
   a.out_scales = nullptr;
   a.out_deq = nullptr;
+  a.act_bf16 = dt == DT_BF16_MXFP8;
   a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
-  if (gemm_prefill(T, k, E)) return launch_prefill(dt, false, a, grid, s);
-  return dispatch_gemm<false>(dt, gemm_nt(T, k, E), a, grid, s);
+  if (gemm_prefill(T, k, E)) return launch_prefill(weight_dt(dt), false, a, grid, s);
+  return dispatch_gemm<false>(weight_dt(dt), gemm_nt(T, k, E), a, grid, s);
 }
 
 hipError_t launch_prepare(int dt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13s, const float* w13a,
@@ -185,6 +187,7 @@ hipError_t launch_prepare(int dt, int E, int H, int I, const uint8_t* w13, const
                      L.KG13, I, 1, packed + L.w13_codes, packed + L.w13_scales);                               \
   hipLaunchKernelGGL(prepare_kernel<D>, dim3(blocks(n2)), dim3(threads), 0, s, w2, w2s, E, H, I, L.G2, L.KG2, I, \
                      0, packed + L.w2_codes, packed + L.w2_scales);
+  dt = weight_dt(dt);
   if (dt == DT_BF16) { MOE_PREP(DT_BF16) }
   else if (dt == DT_MXFP8) { MOE_PREP(DT_MXFP8) }
   else {

@@ -18,6 +18,7 @@ struct GemmArgs {
   uint8_t* out;               // hq codes (gemm13) or y (gemm2)
   uint8_t* out_scales;        // hq scales (gemm13)
   uint16_t* out_deq;          // hq dequantised 16-bit copy (gemm13; MXFP8, NVFP4)
+  int act_bf16;               // MXFP8 weights with bf16 activations: the intermediate is rounded to bf16
   int E, K, G, KG, k, n_out;
 };
 
@@ -276,7 +277,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
           h[tp][j] = gv / (1.0f + expf(-gv)) * uv;
         }
       const int I = a.n_out;
-      if constexpr (DT == DT_BF16) {
+      if (DT == DT_BF16 || (DT == DT_MXFP8 && a.act_bf16)) {  // bf16 intermediate
         if (ok) {
           uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * g + 4 * q;
 #pragma unroll
@@ -313,7 +314,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
           }
           if (q == 0) a.out_scales[(size_t)r * (I / 32) + g] = (uint8_t)(sx + 127);
         }
-      } else {
+      } else if constexpr (DT == DT_NVFP4) {
         // two blocks of 16 along I: [32g + 16tp, +16)
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {

@@ -33,7 +33,12 @@
 
 namespace moe {
 
-enum { DT_BF16 = 0, DT_MXFP8 = 1, DT_NVFP4 = 2 };
+// Layer formats (moe_dtype).  DT_BF16_MXFP8 keeps activations in bf16 (no
+// quantisation of x, intermediate rounded to bf16) over MXFP8 weights.
+enum { DT_BF16 = 0, DT_MXFP8 = 1, DT_NVFP4 = 2, DT_BF16_MXFP8 = 3 };
+// the format of the weights / of the activations (x, the intermediate) of a layer format
+MOE_HD int weight_dt(int dt) { return dt == DT_BF16_MXFP8 ? DT_MXFP8 : dt; }
+MOE_HD int act_dt(int dt) { return dt == DT_BF16_MXFP8 ? DT_BF16 : dt; }
 
 constexpr int kKGroup = 128;   // K slice of one tile
 constexpr int kTileRows = 16;  // rows of one tile
@@ -41,14 +46,26 @@ constexpr int kTilesPerGroup = 4;
 
 MOE_HD size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// bytes of one tile's codes / scales
-MOE_HD size_t tile_code_bytes(int dt) { return dt == DT_BF16 ? 4096 : (dt == DT_MXFP8 ? 2048 : 1024); }
-MOE_HD size_t tile_scale_bytes(int dt) { return dt == DT_BF16 ? 0 : (dt == DT_MXFP8 ? 64 : 128); }
+// bytes of one weight tile's codes / scales (dt: a layer format)
+MOE_HD size_t tile_code_bytes(int dt) {
+  dt = weight_dt(dt);
+  return dt == DT_BF16 ? 4096 : (dt == DT_MXFP8 ? 2048 : 1024);
+}
+MOE_HD size_t tile_scale_bytes(int dt) {
+  dt = weight_dt(dt);
+  return dt == DT_BF16 ? 0 : (dt == DT_MXFP8 ? 64 : 128);
+}
 
-// element bytes (x2 for nvfp4: half a byte) and scale block of a format
-MOE_HD size_t row_code_bytes(int dt, int K) { return dt == DT_BF16 ? (size_t)K * 2 : (dt == DT_MXFP8 ? (size_t)K : (size_t)K / 2); }
+// activation row bytes (x2 for nvfp4: half a byte) and scale block (dt: a layer format)
+MOE_HD size_t row_code_bytes(int dt, int K) {
+  dt = act_dt(dt);
+  return dt == DT_BF16 ? (size_t)K * 2 : (dt == DT_MXFP8 ? (size_t)K : (size_t)K / 2);
+}
 MOE_HD int scale_block(int dt) { return dt == DT_MXFP8 ? 32 : (dt == DT_NVFP4 ? 16 : 0); }
-MOE_HD size_t row_scale_bytes(int dt, int K) { return dt == DT_BF16 ? 0 : (size_t)K / scale_block(dt); }
+MOE_HD size_t row_scale_bytes(int dt, int K) {
+  dt = act_dt(dt);
+  return dt == DT_BF16 ? 0 : (size_t)K / scale_block(dt);
+}
 
 struct PackedLayout {
   int G13, KG13, G2, KG2;
@@ -68,8 +85,8 @@ MOE_HD PackedLayout packed_layout(int dt, int E, int H, int I) {
   L.w13_scales = off; off = align256(off + n13 * tile_scale_bytes(dt));
   L.w2_codes = off; off = align256(off + n2 * tile_code_bytes(dt));
   L.w2_scales = off; off = align256(off + n2 * tile_scale_bytes(dt));
-  L.w13_alpha = off; off = align256(off + (dt == DT_NVFP4 ? (size_t)E * 4 : 0));
-  L.w2_alpha = off; off = align256(off + (dt == DT_NVFP4 ? (size_t)E * 4 : 0));
+  L.w13_alpha = off; off = align256(off + (weight_dt(dt) == DT_NVFP4 ? (size_t)E * 4 : 0));
+  L.w2_alpha = off; off = align256(off + (weight_dt(dt) == DT_NVFP4 ? (size_t)E * 4 : 0));
   L.total = off;
   return L;
 }
@@ -83,10 +100,12 @@ MOE_HD size_t act_dequant_offset(int dt, int rows, int K) {
   return act_scale_offset(dt, rows, K) + align256((size_t)rows * row_scale_bytes(dt, K));
 }
 MOE_HD size_t act_bytes(int dt, int rows, int K) {
-  return act_dequant_offset(dt, rows, K) + (dt == DT_BF16 ? 0 : align256((size_t)rows * K * 2));
+  return act_dequant_offset(dt, rows, K) + (act_dt(dt) == DT_BF16 ? 0 : align256((size_t)rows * K * 2));
 }
 // 16-bit operand rows of an activation buffer: the codes for BF16, else the dequantised copy
-MOE_HD size_t act_operand_offset(int dt, int rows, int K) { return dt == DT_BF16 ? 0 : act_dequant_offset(dt, rows, K); }
+MOE_HD size_t act_operand_offset(int dt, int rows, int K) {
+  return act_dt(dt) == DT_BF16 ? 0 : act_dequant_offset(dt, rows, K);
+}
 
 // moe_forward workspace, sized for max_tokens.  It opens with the fused
 // kernel's synchronisation words (kSyncHeader words, then one per expert),
@@ -108,7 +127,7 @@ MOE_HD WorkspaceLayout workspace_layout(int dt, int E, int H, int I, int k, int 
   W.offsets = off; off = align256(off + (size_t)(E + 1) * 4);
   W.sorted_pairs = off; off = align256(off + P * 4);
   W.pair_pos = off; off = align256(off + P * 4);
-  W.xq = off; off = align256(off + (dt == DT_BF16 ? 0 : act_bytes(dt, max_tokens, H)));
+  W.xq = off; off = align256(off + (act_dt(dt) == DT_BF16 ? 0 : act_bytes(dt, max_tokens, H)));
   W.hq = off; off = align256(off + act_bytes(dt, (int)P, I));
   W.y = off; off = align256(off + P * (size_t)H * 2);
   W.total = off;

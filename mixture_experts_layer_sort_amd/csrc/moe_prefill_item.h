@@ -172,7 +172,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
         h[i] = gv / (1.0f + expf(-gv)) * uv;
       }
       // h[4b + j] is intermediate index 32g + 8b + 4hl + j
-      if constexpr (DT == DT_BF16) {
+      if (DT == DT_BF16 || (DT == DT_MXFP8 && a.act_bf16)) {  // bf16 intermediate
         if (ok) {
           uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * g + 4 * hl;
 #pragma unroll
@@ -205,7 +205,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
           }
           if (hl == 0) a.out_scales[(size_t)r * (I / 32) + g] = (uint8_t)(sx + 127);
         }
-      } else {
+      } else if constexpr (DT == DT_NVFP4) {
         // two blocks of 16 along I: tp = 0 holds b = 0, 1; tp = 1 holds b = 2, 3
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {

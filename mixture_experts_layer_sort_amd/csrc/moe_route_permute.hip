@@ -135,6 +135,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, floa
 
 hipError_t launch_permute(int dt, const int* ids, int T, int k, int E, int H, int* offsets, int* sorted_pairs,
                           int* pair_pos, const uint16_t* x, uint8_t* xq, hipStream_t s) {
+  dt = act_dt(dt);  // only the activation format matters here
   const int P = T * k;
   const long long n_elem = (long long)T * H;
   const int do_quant = !(dt == DT_BF16 && (const void*)xq == (const void*)x);
@@ -161,6 +162,7 @@ hipError_t launch_permute(int dt, const int* ids, int T, int k, int E, int H, in
 
 hipError_t launch_quantize_weights(int dt, int count, int rows, int K, const float* w, void* codes, void* scales,
                                    float* alpha, hipStream_t s) {
+  dt = weight_dt(dt);
   const long long n = (long long)count * rows * K;
   const int threads = 256;
   if (dt == DT_BF16) {

@@ -49,7 +49,7 @@ class Workload:
     I: int          # expert intermediate size
     E: int          # experts
     k: int          # experts per token
-    dtype: str      # "bf16" | "mxfp8" | "nvfp4"
+    dtype: str      # "bf16" | "mxfp8" | "nvfp4" | "bf16_mxfp8" (bf16 activations, MXFP8 weights)
     bias: str       # "none" | "normal2" | "zipf1.1"
     cid: int        # seed id of the workload
 
@@ -75,6 +75,9 @@ WORKLOADS = {
         Workload("nvfp4_decode_t8", 8, 7168, 2048, 384, 8, "nvfp4", "none", 4),
         Workload("nvfp4_decode_t128", 128, 7168, 2048, 384, 8, "nvfp4", "none", 4),
         Workload("mxfp8_prefill", 8192, 7168, 2048, 256, 8, "mxfp8", "zipf1.1", 5),
+        # bf16 activations over the MXFP8 layers' weights (same seeds, same weights)
+        Workload("bf16_mxfp8_decode", 32, 7168, 2048, 256, 8, "bf16_mxfp8", "normal2", 3),
+        Workload("bf16_mxfp8_prefill", 8192, 7168, 2048, 256, 8, "bf16_mxfp8", "zipf1.1", 5),
     ]
 }
 

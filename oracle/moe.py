@@ -22,6 +22,10 @@ Readings where the pages are silent (all documented with the design):
    with global scale 1), the decision taken on fp32 h (kernel precision).
 6. Combine: out_t = bf16( sum_j w_tj * y_tj ), summed in slot order; no shared
    expert, no linear biases, no token dropping.
+7. Layer format "bf16_mxfp8" (the pages list a bf16 x MXFP8 MegaMoE entry
+   beside the three formats [MegaMoE drop workflow, §1, the package exports]
+   and say nothing more): MXFP8 weights with the activation path of the BF16
+   layer -- x is used as given and the intermediate is rounded to bf16.
 
 Arithmetic: dequantised operands are exact in float64, dot products and the
 SwiGLU are evaluated in float64, and rounding to fp32 happens only where the
@@ -82,6 +86,19 @@ def permute(ids: np.ndarray, E: int):
     return offsets.astype(np.int32), sorted_pairs.astype(np.int32), pair_pos.astype(np.int32)
 
 
+# ------------------------------------------------------------------ formats
+
+
+def weight_format(fmt: str) -> str:
+    """The format of a layer format's weights."""
+    return "mxfp8" if fmt == "bf16_mxfp8" else fmt
+
+
+def act_format(fmt: str) -> str:
+    """The format of a layer format's activations (x and the intermediate)."""
+    return "bf16" if fmt == "bf16_mxfp8" else fmt
+
+
 # ------------------------------------------------------------------ weights
 
 
@@ -93,6 +110,7 @@ class Weights:
     dtype mxfp8: w13 e4m3 [E, 2I, H] + w13_s e8m0 [E, 2I, H/32]; same for w2
     dtype nvfp4: w13 packed e2m1 [E, 2I, H/2] + w13_s e4m3 [E, 2I, H/16]
                  + w13_a fp32 [E]; same for w2
+    dtype bf16_mxfp8: as mxfp8 (the layer format's weights)
     Any of the per-expert arrays may be a mapping {expert: array} holding only
     the experts a computation needs.
     """
@@ -110,21 +128,23 @@ class Weights:
         def g(x):
             return None if x is None else x[e]
 
-        w13 = quant.dequantize_weight(g(self.w13), g(self.w13_s), g(self.w13_a), self.dtype)
-        w2 = quant.dequantize_weight(g(self.w2), g(self.w2_s), g(self.w2_a), self.dtype)
+        wf = weight_format(self.dtype)
+        w13 = quant.dequantize_weight(g(self.w13), g(self.w13_s), g(self.w13_a), wf)
+        w2 = quant.dequantize_weight(g(self.w2), g(self.w2_s), g(self.w2_a), wf)
         return w13, w2
 
 
 def quantize_weights(w13_f32: dict, w2_f32: dict, dtype: str) -> Weights:
     """Quantise fp32 master weights {e: array} into canonical form (harness)."""
     out = {k: {} for k in ("w13", "w13_s", "w13_a", "w2", "w2_s", "w2_a")}
+    wf = weight_format(dtype)
     for e in w13_f32:
-        out["w13"][e], out["w13_s"][e], out["w13_a"][e] = quant.quantize_weight(w13_f32[e], dtype)
-        out["w2"][e], out["w2_s"][e], out["w2_a"][e] = quant.quantize_weight(w2_f32[e], dtype)
-    if dtype == "bf16":
+        out["w13"][e], out["w13_s"][e], out["w13_a"][e] = quant.quantize_weight(w13_f32[e], wf)
+        out["w2"][e], out["w2_s"][e], out["w2_a"][e] = quant.quantize_weight(w2_f32[e], wf)
+    if wf == "bf16":
         for n in ("w13_s", "w13_a", "w2_s", "w2_a"):
             out[n] = None
-    if dtype == "mxfp8":
+    if wf == "mxfp8":
         out["w13_a"] = out["w2_a"] = None
     return Weights(dtype=dtype, **out)
 
@@ -140,16 +160,19 @@ def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
 
 
 def requant_h(h64: np.ndarray, dtype: str):
-    """Requantise the intermediate (decision on fp32 h); returns
-    (codes, scales, dequantised float64)."""
+    """Requantise the intermediate in the layer format's activation format
+    (decision on fp32 h); returns (codes, scales, dequantised float64)."""
+    dtype = act_format(dtype)
     h32 = np.asarray(h64, np.float64).astype(np.float32)
     c, s = quant.quantize_act(h32, dtype)
     return c, s, quant.dequantize_act(c, s, dtype)
 
 
 def quantize_x(x_bits: np.ndarray, dtype: str):
-    """In-kernel activation quantisation of bf16 hidden states; returns
-    (codes, scales, dequantised float64).  bf16 passes through."""
+    """In-kernel activation quantisation of bf16 hidden states in the layer
+    format's activation format; returns (codes, scales, dequantised float64).
+    bf16 passes through."""
+    dtype = act_format(dtype)
     x32 = codecs.bf16_decode(x_bits).astype(np.float32)
     c, s = quant.quantize_act(x32, dtype)
     if dtype == "bf16":

@@ -19,12 +19,22 @@ def dev():
     return torch.device("cuda:0")
 
 
+# the weight / activation formats of a layer format ("bf16_mxfp8": bf16
+# activations over MXFP8 weights)
+def weight_format(dtype):
+    return "mxfp8" if dtype == "bf16_mxfp8" else dtype
+
+
+def act_format(dtype):
+    return "bf16" if dtype == "bf16_mxfp8" else dtype
+
+
 def row_code_bytes(dtype, K):
-    return {"bf16": 2 * K, "mxfp8": K, "nvfp4": K // 2}[dtype]
+    return {"bf16": 2 * K, "mxfp8": K, "nvfp4": K // 2}[act_format(dtype)]
 
 
 def row_scale_bytes(dtype, K):
-    return {"bf16": 0, "mxfp8": K // 32, "nvfp4": K // 16}[dtype]
+    return {"bf16": 0, "mxfp8": K // 32, "nvfp4": K // 16}[act_format(dtype)]
 
 
 @dataclasses.dataclass
@@ -42,10 +52,11 @@ class CanonicalWeights:
 def alloc_canonical(w: mi.Workload) -> CanonicalWeights:
     d, E, H, I = dev(), w.E, w.H, w.I
     u8 = torch.uint8
-    if w.dtype == "bf16":
+    wf = weight_format(w.dtype)
+    if wf == "bf16":
         return CanonicalWeights(torch.empty(E, 2 * I, H, dtype=torch.bfloat16, device=d),
                                 torch.empty(E, H, I, dtype=torch.bfloat16, device=d), None, None, None, None)
-    if w.dtype == "mxfp8":
+    if wf == "mxfp8":
         return CanonicalWeights(torch.empty(E, 2 * I, H, dtype=u8, device=d), torch.empty(E, H, I, dtype=u8, device=d),
                                 torch.empty(E, 2 * I, H // 32, dtype=u8, device=d),
                                 torch.empty(E, H, I // 32, dtype=u8, device=d), None, None)
@@ -156,7 +167,7 @@ class DeviceLayer:
         dt = self.w.dtype
         a = buf.cpu().numpy()
         codes = a[: rows * row_code_bytes(dt, K)].reshape(rows, row_code_bytes(dt, K))
-        if dt == "bf16":
+        if act_format(dt) == "bf16":
             return codes.view(np.uint16), None
         scales = a[scale_off: scale_off + rows * row_scale_bytes(dt, K)].reshape(rows, row_scale_bytes(dt, K))
         return codes, scales
@@ -171,7 +182,7 @@ class DeviceLayer:
         """The 16-bit dequantised copy of an MXFP8 (bf16) / NVFP4 (fp16) activation
         buffer, widened to float64."""
         a = buf[off: off + rows * K * 2].cpu().numpy().view(np.uint16).reshape(rows, K)
-        if self.w.dtype == "mxfp8":
+        if act_format(self.w.dtype) == "mxfp8":
             return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         return a.view(np.float16).astype(np.float64)
 

@@ -43,7 +43,8 @@ def S(H=256, I=512, E=8, k=2, T=16, dt="bf16"):
     ({"H": 200}, UNSUPPORTED), ({"I": 100}, UNSUPPORTED), ({"H": 0}, UNSUPPORTED),
     ({"E": 0}, UNSUPPORTED), ({"E": 1025}, UNSUPPORTED), ({"E": 1024, "k": 32}, OK),
     ({"k": 0}, UNSUPPORTED), ({"k": 33, "E": 64}, UNSUPPORTED), ({"k": 9, "E": 8}, UNSUPPORTED),
-    ({"T": 0}, UNSUPPORTED), ({"T": 1 << 22, "k": 8}, UNSUPPORTED), ({"dt": 3}, UNSUPPORTED),
+    ({"T": 0}, UNSUPPORTED), ({"T": 1 << 22, "k": 8}, UNSUPPORTED), ({"dt": "bf16_mxfp8"}, OK),
+    ({"dt": 4}, UNSUPPORTED), ({"dt": -1}, UNSUPPORTED),
 ])
 def test_shape_validation(kw, status):
     args = dict(H=256, I=512, E=8, k=2, T=16, dt="bf16")
@@ -71,6 +72,13 @@ def test_sizes_match_layouts():
     s = S(512, 256, 8, 4, 64, "nvfp4")
     assert lib.moe_xq_scale_offset(s, T) == ((T * 256 + 255) // 256) * 256
     assert lib.moe_xq_bytes(s, 65) == 0  # T beyond max_tokens
+    # bf16 activations over MXFP8 weights: the weights of MXFP8, the activations of BF16
+    for shape in [(7168, 2048, 256, 8, 8192), (512, 256, 8, 4, 64)]:
+        a, m, b = S(*shape, "bf16_mxfp8"), S(*shape, "mxfp8"), S(*shape, "bf16")
+        assert lib.moe_packed_weight_bytes(a) == lib.moe_packed_weight_bytes(m)
+        for f in (lib.moe_xq_bytes, lib.moe_xq_scale_offset, lib.moe_hq_bytes, lib.moe_hq_scale_offset):
+            assert f(a, T) == f(b, T), f
+        assert lib.moe_workspace_bytes(a) == lib.moe_workspace_bytes(b)
 
 
 FAKE = 0x1000  # never dereferenced: every call below fails validation first

@@ -43,7 +43,7 @@ def pool():
 
 def _quantize_pair(args):
     w13, w2, dtype = args
-    return oquant.quantize_weight(w13, dtype), oquant.quantize_weight(w2, dtype)
+    return oquant.quantize_weight(w13, gh.weight_format(dtype)), oquant.quantize_weight(w2, gh.weight_format(dtype))
 
 
 def _pick_tokens(ids, k, limit):
@@ -62,7 +62,7 @@ def _pick_tokens(ids, k, limit):
 
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "bf16_decode", "mxfp8_decode", "nvfp4_decode_t8",
-                                  "nvfp4_decode_t128", "mxfp8_prefill"])
+                                  "nvfp4_decode_t128", "bf16_mxfp8_decode", "mxfp8_prefill"])
 def test_fullsize_parity(name, pool):
     w = W[name]
     dev = gh.dev()
@@ -127,8 +127,8 @@ def test_fullsize_parity(name, pool):
     _log(f"{name}: library weight codes of {len(experts)} experts equal the oracle's")
     if w.dtype == "bf16":
         Wo = omoe.Weights("bf16", ow["w13"], ow["w2"])
-    elif w.dtype == "mxfp8":
-        Wo = omoe.Weights("mxfp8", ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"])
+    elif gh.weight_format(w.dtype) == "mxfp8":
+        Wo = omoe.Weights(w.dtype, ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"])
     else:
         Wo = omoe.Weights("nvfp4", ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"], ow["w13_a"], ow["w2_a"])
     ref = omoe.moe_layer(x_bits, l_host, Wo, w.k, tokens=toks, keep=True)
@@ -139,7 +139,8 @@ def test_fullsize_parity(name, pool):
         for j in range(w.k):
             p = t * w.k + j
             row = int(pp[p])
-            h_got = oquant.dequantize_act(hc[row:row + 1], None if hs is None else hs[row:row + 1], w.dtype)[0]
+            h_got = oquant.dequantize_act(hc[row:row + 1], None if hs is None else hs[row:row + 1],
+                                          gh.act_format(w.dtype))[0]
             assert gh.rel_l2(h_got, ref.h[(t, j)][2]) <= tol, (t, j)
             y_got = (y[p].astype(np.uint32) << 16).view(np.float32)
             assert gh.rel_l2(y_got, ref.y[(t, j)]) <= tol, (t, j)

@@ -34,6 +34,9 @@ SMALL = {
     "nvfp4_singleton": W["nvfp4_decode_t8"].scaled(E=1, k=1, T=3, H=256, I=128),
     "bf16_k_equals_E": W["tiny_bf16"].scaled(E=4, k=4, T=9, H=128, I=128),
     "mxfp8_min": W["mxfp8_decode"].scaled(T=1, H=128, I=128, E=3, k=2),
+    # bf16 activations over MXFP8 weights: decode and prefill-shaped GEMMs
+    "bf16_mxfp8_decode_small": W["bf16_mxfp8_decode"].scaled(T=40, H=640, I=256, E=32),
+    "bf16_mxfp8_prefill_small": W["bf16_mxfp8_prefill"].scaled(T=520, H=256, I=384, E=8, k=2),
 }
 
 
@@ -84,7 +87,7 @@ def test_layer_parity_small(name):
         assert np.array_equal(layer.xq_dequant(r, w.T), xh)
     # requantised intermediate, expert-sorted: compare dequantised values
     hc, hs = layer.hq_numpy(r, w.T)
-    h_got = oquant.dequantize_act(hc, hs, w.dtype)
+    h_got = oquant.dequantize_act(hc, hs, gh.act_format(w.dtype))
     if hs is not None:
         assert np.array_equal(layer.hq_dequant(r, w.T), h_got)
     h_ref = np.stack([ref.h[(int(p) // w.k, int(p) % w.k)][2] for p in sp])

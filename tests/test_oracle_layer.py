@@ -11,7 +11,12 @@ import torch.nn.functional as F
 import moe_inputs as mi
 from oracle import codecs, moe, quant
 
-DTYPES = ["bf16", "mxfp8", "nvfp4"]
+DTYPES = ["bf16", "mxfp8", "nvfp4", "bf16_mxfp8"]
+
+
+def _act(dtype):
+    """Activation format of a layer format (bf16_mxfp8: bf16 activations)."""
+    return "bf16" if dtype == "bf16_mxfp8" else dtype
 
 
 def _small(dtype, T=6, H=64, I=64, E=5, k=2, bias="none", cid=91):
@@ -32,8 +37,8 @@ def _mlp_torch(x_hat, W13, W2, dtype):
     g = F.linear(xt, torch.from_numpy(W13[:I]))
     u = F.linear(xt, torch.from_numpy(W13[I:]))
     h = (F.silu(g) * u).numpy()
-    c, s = quant.quantize_act(h.astype(np.float32), dtype)
-    hh = quant.dequantize_act(c, s, dtype)
+    c, s = quant.quantize_act(h.astype(np.float32), _act(dtype))
+    hh = quant.dequantize_act(c, s, _act(dtype))
     return F.linear(torch.from_numpy(hh), torch.from_numpy(W2)).numpy()
 
 
@@ -118,6 +123,30 @@ def test_fp32_accumulation_headroom(dtype):
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     tol = 3e-2 if dtype == "nvfp4" else 1e-2
     assert rel < tol / 5, rel
+
+
+def test_bf16_mxfp8_is_the_bf16_layer_on_widened_mxfp8_weights():
+    """Reading of the bf16 x MXFP8 format: MXFP8 weights, the BF16 layer's
+    activation path.  e4m3 x 2^s is exact in bf16, so the layer must equal,
+    bit for bit, the BF16 layer run on the MXFP8 weights widened to bf16 --
+    and differ from the MXFP8 layer, which quantises x and h."""
+    w = _small("bf16_mxfp8", T=10, E=6, k=3, bias="normal2")
+    W = _weights(w)
+    assert W.w13[0].dtype == np.uint8 and W.w13_s is not None  # stored as MXFP8
+    wide13, wide2 = {}, {}
+    for e in range(w.E):
+        a, b = W.dequant(e)
+        wide13[e] = codecs.bf16_encode(a.astype(np.float32))
+        wide2[e] = codecs.bf16_encode(b.astype(np.float32))
+        assert np.array_equal(codecs.bf16_decode(wide13[e]), a)  # exact widening
+        assert np.array_equal(codecs.bf16_decode(wide2[e]), b)
+    x, l = mi.host_x(w), mi.host_logits(w)
+    got = moe.moe_layer(x, l, W, w.k)
+    ref = moe.moe_layer(x, l, moe.Weights("bf16", wide13, wide2), w.k)
+    assert np.array_equal(got.out_f64, ref.out_f64)
+    assert np.array_equal(got.out, ref.out)
+    mx = moe.moe_layer(x, l, moe.Weights("mxfp8", W.w13, W.w2, W.w13_s, W.w2_s), w.k)
+    assert not np.array_equal(mx.out_f64, got.out_f64)
 
 
 def test_token_subset_matches_full():
