@@ -32,6 +32,8 @@
  *               Weight buffers, moe_quantize_weights and moe_prepare_weights
  *               are those of MOE_MXFP8; xq and hq are those of MOE_BF16.
  *   W13 rows [0, I) are the gate projection, rows [I, 2I) the up projection.
+ *   With MOE_RELU2 experts W13 holds I rows (W1) instead of 2I: [E, I, H]
+ *   codes (and [E, I, H/32] / [E, I, H/16] scales); W2 is unchanged.
  *
  * Conventions of every entry point:
  *   - Buffers are device pointers owned by the caller; the library never
@@ -67,6 +69,14 @@ typedef struct ihipStream_t* hipStream_t;
 
 typedef enum { MOE_BF16 = 0, MOE_MXFP8 = 1, MOE_NVFP4 = 2, MOE_BF16_MXFP8 = 3 } moe_dtype;
 
+/* Expert activation.  MOE_SWIGLU: gated, h = silu(gate) * up with W13 rows
+ * [0, I) gate and [I, 2I) up.  MOE_RELU2: non-gated, h = relu(W1 x)^2 with
+ * W1 = W13 of I rows (the squared-ReLU experts of Nemotron-style models,
+ * which the pages note the b12x backend rejects [vLLM PR 40082 report,
+ * "Risks" item 4]).  Everything else -- formats, requantisation of h, the
+ * down GEMM and the combine -- is the same. */
+typedef enum { MOE_SWIGLU = 0, MOE_RELU2 = 1 } moe_activation;
+
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* null pointer, T out of range, bad size */
@@ -77,7 +87,8 @@ typedef enum {
 
 /* Layer shape.  Supported: hidden % 128 == 0, inter % 128 == 0,
  * 1 <= num_experts <= 1024, 1 <= top_k <= min(num_experts, 32),
- * 1 <= max_tokens and max_tokens * top_k <= 2^24, dtype a moe_dtype. */
+ * 1 <= max_tokens and max_tokens * top_k <= 2^24, dtype a moe_dtype,
+ * activation a moe_activation. */
 typedef struct {
   int32_t hidden;      /* H */
   int32_t inter;       /* I, per expert */
@@ -85,6 +96,7 @@ typedef struct {
   int32_t top_k;       /* k */
   int32_t max_tokens;  /* workspace capacity in tokens */
   int32_t dtype;       /* moe_dtype of weights and activations */
+  int32_t activation;  /* moe_activation of the experts */
 } moe_shape;
 
 /* Text of a status code (static storage). */
@@ -133,7 +145,8 @@ MOE_API moe_status moe_quantize_weights(int32_t dtype, int32_t count, int32_t ro
 
 /* Repack canonical weights into the MFMA-ready tile layout in `packed`
  * (moe_packed_weight_bytes bytes): per expert, W13 is cut into groups of 32
- * gate rows + the matching 32 up rows, W2 into groups of 64 rows; each
+ * gate rows + the matching 32 up rows (MOE_RELU2: W1 into groups of 64
+ * rows), W2 into groups of 64 rows; each
  * (row group, 128-wide K slice) is one contiguous block laid out in the
  * per-lane operand order of the CDNA4 MFMA that consumes it, with scales in
  * the matching per-lane order.  A pure byte permutation; done once at load
@@ -176,7 +189,7 @@ MOE_API moe_status moe_permute(const moe_shape* shape, int32_t T, const int32_t*
  * For each expert e and sorted row r in [offsets[e], offsets[e+1]):
  *   g, u = W13[e] . xq[sorted_pairs[r] / k]  (fp32 accumulation; NVFP4 scaled
  *   by the W13 alpha), h = silu(g) * u, hq[r] = requant(h) (layout of
- *   moe_hq_bytes).  ws / ws_bytes: unused, may be NULL / 0. */
+ *   moe_hq_bytes).  MOE_RELU2: g = W1[e] . xq[...], h = relu(g)^2.  ws / ws_bytes: unused, may be NULL / 0. */
 MOE_API moe_status moe_gemm13_swiglu_quant(const moe_shape* shape, int32_t T, const void* packed,
                                    const int32_t* offsets, const int32_t* sorted_pairs, const void* xq,
                                    void* hq, void* ws, size_t ws_bytes, hipStream_t stream);

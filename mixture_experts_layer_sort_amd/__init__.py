@@ -19,6 +19,9 @@ LIB_PATH = os.path.join(_PKG_DIR, "libmoe_mi355x.so")
 MOE_BF16, MOE_MXFP8, MOE_NVFP4, MOE_BF16_MXFP8 = 0, 1, 2, 3
 # layer formats; "bf16_mxfp8" = bf16 activations over MXFP8 weights
 DTYPES = {"bf16": MOE_BF16, "mxfp8": MOE_MXFP8, "nvfp4": MOE_NVFP4, "bf16_mxfp8": MOE_BF16_MXFP8}
+# expert activations: gated SwiGLU (W13 of 2I rows) or non-gated squared ReLU (W1 of I rows)
+MOE_SWIGLU, MOE_RELU2 = 0, 1
+ACTIVATIONS = {"swiglu": MOE_SWIGLU, "relu2": MOE_RELU2}
 
 EXPORTED = [
     "moe_status_string",
@@ -56,16 +59,18 @@ class moe_shape(ctypes.Structure):
         ("top_k", ctypes.c_int32),
         ("max_tokens", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("activation", ctypes.c_int32),
     ]
 
     def __repr__(self):
         return (f"moe_shape(H={self.hidden}, I={self.inter}, E={self.num_experts}, k={self.top_k}, "
-                f"max_tokens={self.max_tokens}, dtype={self.dtype})")
+                f"max_tokens={self.max_tokens}, dtype={self.dtype}, activation={self.activation})")
 
 
-def make_shape(hidden, inter, num_experts, top_k, max_tokens, dtype) -> moe_shape:
+def make_shape(hidden, inter, num_experts, top_k, max_tokens, dtype, activation="swiglu") -> moe_shape:
     d = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
-    return moe_shape(hidden, inter, num_experts, top_k, max_tokens, d)
+    a = ACTIVATIONS[activation] if isinstance(activation, str) else int(activation)
+    return moe_shape(hidden, inter, num_experts, top_k, max_tokens, d, a)
 
 
 def _load():

@@ -62,6 +62,8 @@ int fused_grid(int dt, int T, int k, int E) {
   return occ > 0 ? occ * device_cu_count() : 0;
 }
 
+static bool gated(const moe_shape* s) { return s->activation == MOE_SWIGLU; }
+
 moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_INVALID_ARG;
   if (s->dtype < MOE_BF16 || s->dtype > MOE_BF16_MXFP8) return MOE_ERR_UNSUPPORTED;
@@ -70,6 +72,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->num_experts < 1 || s->num_experts > 1024) return MOE_ERR_UNSUPPORTED;
   if (s->top_k < 1 || s->top_k > 32 || s->top_k > s->num_experts) return MOE_ERR_UNSUPPORTED;
   if (s->max_tokens < 1 || (long long)s->max_tokens * s->top_k > (1LL << 24)) return MOE_ERR_UNSUPPORTED;
+  if (s->activation != MOE_SWIGLU && s->activation != MOE_RELU2) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -101,7 +104,7 @@ moe_status moe_check_shape(const moe_shape* shape) { return check_shape(shape); 
 
 size_t moe_packed_weight_bytes(const moe_shape* s) {
   if (check_shape(s) != MOE_OK) return 0;
-  return packed_layout(s->dtype, s->num_experts, s->hidden, s->inter).total;
+  return packed_layout(s->dtype, s->num_experts, s->hidden, s->inter, gated(s)).total;
 }
 
 size_t moe_workspace_bytes(const moe_shape* s) {
@@ -163,7 +166,7 @@ moe_status moe_prepare_weights(const moe_shape* s, const void* w13_codes, const 
   if (s->dtype != MOE_BF16 && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
   if (s->dtype == MOE_NVFP4 && (!w13_alpha || !w2_alpha)) return MOE_ERR_INVALID_ARG;
   if (packed_bytes < moe_packed_weight_bytes(s)) return MOE_ERR_WORKSPACE;
-  return launched(launch_prepare(s->dtype, s->num_experts, s->hidden, s->inter, (const uint8_t*)w13_codes,
+  return launched(launch_prepare(s->dtype, gated(s), s->num_experts, s->hidden, s->inter, (const uint8_t*)w13_codes,
                                  (const uint8_t*)w13_scales, w13_alpha, (const uint8_t*)w2_codes,
                                  (const uint8_t*)w2_scales, w2_alpha, (uint8_t*)packed, stream));
 }
@@ -208,7 +211,7 @@ moe_status moe_gemm13_swiglu_quant(const moe_shape* s, int32_t T, const void* pa
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!packed || !offsets || !sorted_pairs || !xq || !hq) return MOE_ERR_INVALID_ARG;
-  return launched(launch_gemm13(s->dtype, s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
+  return launched(launch_gemm13(s->dtype, gated(s), s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
                                 offsets, sorted_pairs, (const uint8_t*)xq, (uint8_t*)hq,
                                 gemm_grid(s->dtype, true, T, s->top_k, s->num_experts), stream));
 }
@@ -222,7 +225,7 @@ moe_status moe_gemm2(const moe_shape* s, int32_t T, const void* packed, const in
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!packed || !offsets || !sorted_pairs || !hq || !y) return MOE_ERR_INVALID_ARG;
-  return launched(launch_gemm2(s->dtype, s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
+  return launched(launch_gemm2(s->dtype, gated(s), s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
                                offsets, sorted_pairs, (const uint8_t*)hq, y,
                                gemm_grid(s->dtype, false, T, s->top_k, s->num_experts), stream));
 }
@@ -267,10 +270,10 @@ moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const 
   if (e == hipSuccess)
     e = launch_permute(dt, ids, T, k, E, H, offsets, sorted_pairs, pair_pos, x, xq, stream);
   if (e == hipSuccess)
-    e = launch_gemm13(dt, E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, xq, hq,
+    e = launch_gemm13(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, xq, hq,
                       gemm_grid(dt, true, T, k, E), stream);
   if (e == hipSuccess)
-    e = launch_gemm2(dt, E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, hq, y,
+    e = launch_gemm2(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, hq, y,
                      gemm_grid(dt, false, T, k, E), stream);
   if (e == hipSuccess) e = launch_combine(T, H, k, y, wts, out, stream);
   return launched(e);
@@ -288,7 +291,7 @@ moe_status moe_forward_fused(const moe_shape* s, int32_t T, const void* packed, 
   float* wts = topk_w ? topk_w : (float*)(base + W.wts);
   const int grid = fused_grid(dt, T, k, E);
   if (grid <= 0) return MOE_ERR_UNSUPPORTED;
-  return launched(launch_fused(dt, E, H, I, k, T, (const uint8_t*)packed, logits, x, out, ids, wts, base, ws_bytes,
+  return launched(launch_fused(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, logits, x, out, ids, wts, base, ws_bytes,
                                s->max_tokens, grid, stream));
 }
 

@@ -186,11 +186,11 @@ int fused_blocks_per_cu(int dt, int v) {
   return n;
 }
 
-hipError_t launch_fused(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const float* logits,
-                        const uint16_t* x, uint16_t* out, int* ids, float* wts, uint8_t* ws, size_t ws_bytes,
-                        int max_tokens, int grid, hipStream_t s) {
+hipError_t launch_fused(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
+                        const float* logits, const uint16_t* x, uint16_t* out, int* ids, float* wts, uint8_t* ws,
+                        size_t ws_bytes, int max_tokens, int grid, hipStream_t s) {
   const WorkspaceLayout W = workspace_layout(dt, E, H, I, k, max_tokens);
-  const PackedLayout L = packed_layout(dt, E, H, I);
+  const PackedLayout L = packed_layout(dt, E, H, I, gated);
   FusedArgs f;
   f.logits = logits;
   f.x = x;
@@ -224,6 +224,7 @@ hipError_t launch_fused(int dt, int E, int H, int I, int k, int T, const uint8_t
   g.out_scales = hq + act_scale_offset(dt, T * k, I);
   g.out_deq = reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
   g.act_bf16 = dt == DT_BF16_MXFP8;
+  g.gated = gated;
   g.E = E; g.K = H; g.G = L.G13; g.KG = L.KG13; g.k = k; g.n_out = I;
   GemmArgs& h = f.g2;
   h.wcodes = packed + L.w2_codes;
@@ -236,6 +237,7 @@ hipError_t launch_fused(int dt, int E, int H, int I, int k, int T, const uint8_t
   h.out_scales = nullptr;
   h.out_deq = nullptr;
   h.act_bf16 = dt == DT_BF16_MXFP8;
+  h.gated = gated;
   h.E = E; h.K = I; h.G = L.G2; h.KG = L.KG2; h.k = k; h.n_out = H;
   (void)ws_bytes;
   void* args[] = {&f};

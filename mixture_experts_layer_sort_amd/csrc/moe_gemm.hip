@@ -138,9 +138,10 @@ int gemm_blocks_per_cu(int dt, bool g13, int nt) {
   return n;
 }
 
-hipError_t launch_gemm13(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const int* offsets,
-                         const int* sorted_pairs, const uint8_t* xq, uint8_t* hq, int grid, hipStream_t s) {
-  const PackedLayout L = packed_layout(dt, E, H, I);
+hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
+                         const int* offsets, const int* sorted_pairs, const uint8_t* xq, uint8_t* hq, int grid,
+                         hipStream_t s) {
+  const PackedLayout L = packed_layout(dt, E, H, I, gated);
   GemmArgs a;
   a.wcodes = packed + L.w13_codes;
   a.wscales = packed + L.w13_scales;
@@ -152,14 +153,16 @@ hipError_t launch_gemm13(int dt, int E, int H, int I, int k, int T, const uint8_
   a.out_scales = hq + act_scale_offset(dt, T * k, I);
   a.out_deq = reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
   a.act_bf16 = dt == DT_BF16_MXFP8;
+  a.gated = gated;
   a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
   if (gemm_prefill(T, k, E)) return launch_prefill(weight_dt(dt), true, a, grid, s);
   return dispatch_gemm<true>(weight_dt(dt), gemm_nt(T, k, E), a, grid, s);
 }
 
-hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const int* offsets,
-                        const int* sorted_pairs, const uint8_t* hq, uint16_t* y, int grid, hipStream_t s) {
-  const PackedLayout L = packed_layout(dt, E, H, I);
+hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
+                        const int* offsets, const int* sorted_pairs, const uint8_t* hq, uint16_t* y, int grid,
+                        hipStream_t s) {
+  const PackedLayout L = packed_layout(dt, E, H, I, gated);
   GemmArgs a;
   a.wcodes = packed + L.w2_codes;
   a.wscales = packed + L.w2_scales;
@@ -171,20 +174,22 @@ hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t
   a.out_scales = nullptr;
   a.out_deq = nullptr;
   a.act_bf16 = dt == DT_BF16_MXFP8;
+  a.gated = gated;
   a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
   if (gemm_prefill(T, k, E)) return launch_prefill(weight_dt(dt), false, a, grid, s);
   return dispatch_gemm<false>(weight_dt(dt), gemm_nt(T, k, E), a, grid, s);
 }
 
-hipError_t launch_prepare(int dt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13s, const float* w13a,
-                          const uint8_t* w2, const uint8_t* w2s, const float* w2a, uint8_t* packed, hipStream_t s) {
-  const PackedLayout L = packed_layout(dt, E, H, I);
+hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t* w13, const uint8_t* w13s,
+                          const float* w13a, const uint8_t* w2, const uint8_t* w2s, const float* w2a, uint8_t* packed,
+                          hipStream_t s) {
+  const PackedLayout L = packed_layout(dt, E, H, I, gated);
   const int threads = 256;
   auto blocks = [&](long long n) { return (int)std::min((n + threads - 1) / threads, 1LL << 20); };
   long long n13 = (long long)E * L.G13 * L.KG13 * 4 * 64, n2 = (long long)E * L.G2 * L.KG2 * 4 * 64;
 #define MOE_PREP(D)                                                                                              \
-  hipLaunchKernelGGL(prepare_kernel<D>, dim3(blocks(n13)), dim3(threads), 0, s, w13, w13s, E, 2 * I, H, L.G13,   \
-                     L.KG13, I, 1, packed + L.w13_codes, packed + L.w13_scales);                               \
+  hipLaunchKernelGGL(prepare_kernel<D>, dim3(blocks(n13)), dim3(threads), 0, s, w13, w13s, E, gated ? 2 * I : I, \
+                     H, L.G13, L.KG13, I, gated ? 1 : 0, packed + L.w13_codes, packed + L.w13_scales);         \
   hipLaunchKernelGGL(prepare_kernel<D>, dim3(blocks(n2)), dim3(threads), 0, s, w2, w2s, E, H, I, L.G2, L.KG2, I, \
                      0, packed + L.w2_codes, packed + L.w2_scales);
   dt = weight_dt(dt);

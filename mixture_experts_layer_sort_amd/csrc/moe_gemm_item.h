@@ -19,6 +19,7 @@ struct GemmArgs {
   uint8_t* out_scales;        // hq scales (gemm13)
   uint16_t* out_deq;          // hq dequantised 16-bit copy (gemm13; MXFP8, NVFP4)
   int act_bf16;               // MXFP8 weights with bf16 activations: the intermediate is rounded to bf16
+  int gated;                  // gate/up GEMM: 1 SwiGLU (gate/up row pairs), 0 ReLU^2 (64 W1 rows per group)
   int E, K, G, KG, k, n_out;
 };
 
@@ -255,7 +256,8 @@ struct StepK {
 // Epilogue of one wave's accumulators acc[4 tiles][NT token sub-tiles] for
 // sorted rows r0 + 16s + (lane % 16) (valid below r_end) and weight row group
 // g of expert e.  Gate/up GEMM: tiles 0,1 = gate rows 32g + 16tp + 4q + j,
-// tiles 2,3 = the matching up rows; h = silu(g) * u is requantised into hq
+// tiles 2,3 = the matching up rows; h = silu(g) * u (ReLU^2 experts: h =
+// relu(v)^2 of all four tiles, 64 intermediates) is requantised into hq
 // (codes, scales, exact 16-bit copy).  Down GEMM: y rows at the pair index.
 template <int DT, int NT, bool G13>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[4][NT], int r0, int r_end, int g,
@@ -267,75 +269,91 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
     const int r = r0 + 16 * s + i16;
     const bool ok = r < r_end;
     if constexpr (G13) {
-      // tiles 0,1 = gate rows 32g + 16tp + 4q + j; tiles 2,3 = the matching up rows
-      float h[2][4];
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float gv = acc[tp][s][j] * alpha, uv = acc[2 + tp][s][j] * alpha;
-          h[tp][j] = gv / (1.0f + expf(-gv)) * uv;
-        }
       const int I = a.n_out;
-      if (DT == DT_BF16 || (DT == DT_MXFP8 && a.act_bf16)) {  // bf16 intermediate
-        if (ok) {
-          uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * g + 4 * q;
+      // requantise and store 32 intermediates: h[tp][j] is index 32gg + 16tp + 4q + j
+      auto store_h = [&](const float(&h)[2][4], int gg) __attribute__((always_inline)) {
+        if (DT == DT_BF16 || (DT == DT_MXFP8 && a.act_bf16)) {  // bf16 intermediate
+          if (ok) {
+            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * gg + 4 * q;
 #pragma unroll
-          for (int tp = 0; tp < 2; ++tp) {
-            uint2 v;
-            v.x = f32_to_bf16(h[tp][0]) | ((uint32_t)f32_to_bf16(h[tp][1]) << 16);
-            v.y = f32_to_bf16(h[tp][2]) | ((uint32_t)f32_to_bf16(h[tp][3]) << 16);
-            *reinterpret_cast<uint2*>(o + 16 * tp) = v;
+            for (int tp = 0; tp < 2; ++tp) {
+              uint2 v;
+              v.x = f32_to_bf16(h[tp][0]) | ((uint32_t)f32_to_bf16(h[tp][1]) << 16);
+              v.y = f32_to_bf16(h[tp][2]) | ((uint32_t)f32_to_bf16(h[tp][3]) << 16);
+              *reinterpret_cast<uint2*>(o + 16 * tp) = v;
+            }
           }
-        }
-      } else if constexpr (DT == DT_MXFP8) {
-        // one block of 32 along I: [32g, 32g+32), spread over the 4 lanes sharing i16
-        float amax = 0.f;
+        } else if constexpr (DT == DT_MXFP8) {
+          // one block of 32 along I: [32g, 32g+32), spread over the 4 lanes sharing i16
+          float amax = 0.f;
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
+          for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(h[tp][j]));
-        amax = wave_max_xor(amax, 16, 32);
-        const int sx = mx_scale_exp(amax);
-        if (ok) {
-          uint8_t* o = a.out + (size_t)r * I + 32 * g + 4 * q;
-          uint16_t* od = a.out_deq + (size_t)r * I + 32 * g + 4 * q;
+            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(h[tp][j]));
+          amax = wave_max_xor(amax, 16, 32);
+          const int sx = mx_scale_exp(amax);
+          if (ok) {
+            uint8_t* o = a.out + (size_t)r * I + 32 * gg + 4 * q;
+            uint16_t* od = a.out_deq + (size_t)r * I + 32 * gg + 4 * q;
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+              uint32_t v = 0, d[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const uint32_t c = e4m3_from_f32(ldexpf(h[tp][j], -sx));
+                v |= c << (8 * j);
+                d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), sx)) >> 16;  // exact in bf16
+              }
+              *reinterpret_cast<uint32_t*>(o + 16 * tp) = v;
+              *reinterpret_cast<uint2*>(od + 16 * tp) = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+            }
+            if (q == 0) a.out_scales[(size_t)r * (I / 32) + gg] = (uint8_t)(sx + 127);
+          }
+        } else if constexpr (DT == DT_NVFP4) {
+          // two blocks of 16 along I: [32g + 16tp, +16)
 #pragma unroll
           for (int tp = 0; tp < 2; ++tp) {
+            float amax = fmaxf(fmaxf(fabsf(h[tp][0]), fabsf(h[tp][1])), fmaxf(fabsf(h[tp][2]), fabsf(h[tp][3])));
+            amax = wave_max_xor(amax, 16, 32);
+            const uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
+            const float sc = e4m3_to_f32(sc_code);
             uint32_t v = 0, d[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const uint32_t c = e4m3_from_f32(ldexpf(h[tp][j], -sx));
-              v |= c << (8 * j);
-              d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), sx)) >> 16;  // exact in bf16
+              uint32_t c = sc > 0.f ? e2m1_from_f32(h[tp][j], sc) : ((__float_as_uint(h[tp][j]) >> 28) & 8u);
+              v |= c << (4 * j);
+              d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
             }
-            *reinterpret_cast<uint32_t*>(o + 16 * tp) = v;
-            *reinterpret_cast<uint2*>(od + 16 * tp) = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+            if (ok) {
+              *reinterpret_cast<uint16_t*>(a.out + (size_t)r * (I / 2) + 16 * gg + 8 * tp + 2 * q) = (uint16_t)v;
+              if (q == 0) a.out_scales[(size_t)r * (I / 16) + 2 * gg + tp] = (uint8_t)sc_code;
+              *reinterpret_cast<uint2*>(a.out_deq + (size_t)r * I + 32 * gg + 16 * tp + 4 * q) =
+                  make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+            }
           }
-          if (q == 0) a.out_scales[(size_t)r * (I / 32) + g] = (uint8_t)(sx + 127);
         }
-      } else if constexpr (DT == DT_NVFP4) {
-        // two blocks of 16 along I: [32g + 16tp, +16)
+      };
+      // SwiGLU: tiles 0,1 = gate rows 32g + 16tp + 4q + j, tiles 2,3 = the
+      // matching up rows.  ReLU^2: the group's 64 W1 rows 64g + 16t + 4q + j
+      // are the intermediates of half groups 2g + t / 2.  One copy of the
+      // store code serves both (tiles are selected, not indexed).
+      const int halves = a.gated ? 1 : 2;
+#pragma unroll 1
+      for (int hh = 0; hh < halves; ++hh) {
+        float h[2][4];
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-          float amax = fmaxf(fmaxf(fabsf(h[tp][0]), fabsf(h[tp][1])), fmaxf(fabsf(h[tp][2]), fabsf(h[tp][3])));
-          amax = wave_max_xor(amax, 16, 32);
-          const uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
-          const float sc = e4m3_to_f32(sc_code);
-          uint32_t v = 0, d[4];
+        for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            uint32_t c = sc > 0.f ? e2m1_from_f32(h[tp][j], sc) : ((__float_as_uint(h[tp][j]) >> 28) & 8u);
-            v |= c << (4 * j);
-            d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
+            if (a.gated) {
+              const float gv = acc[tp][s][j] * alpha, uv = acc[2 + tp][s][j] * alpha;
+              h[tp][j] = gv / (1.0f + expf(-gv)) * uv;
+            } else {
+              const float v = fmaxf((hh ? acc[2 + tp][s][j] : acc[tp][s][j]) * alpha, 0.f);
+              h[tp][j] = v * v;
+            }
           }
-          if (ok) {
-            *reinterpret_cast<uint16_t*>(a.out + (size_t)r * (I / 2) + 16 * g + 8 * tp + 2 * q) = (uint16_t)v;
-            if (q == 0) a.out_scales[(size_t)r * (I / 16) + 2 * g + tp] = (uint8_t)sc_code;
-            *reinterpret_cast<uint2*>(a.out_deq + (size_t)r * I + 32 * g + 16 * tp + 4 * q) =
-                make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
-          }
-        }
+        store_h(h, a.gated ? g : 2 * g + hh);
       }
     } else {
       if (ok) {

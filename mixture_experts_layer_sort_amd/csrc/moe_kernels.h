@@ -18,15 +18,19 @@ hipError_t launch_permute(int dt, const int* ids, int T, int k, int E, int H, in
 hipError_t launch_quantize_weights(int dt, int count, int rows, int K, const float* w, void* codes, void* scales,
                                    float* alpha, hipStream_t s);
 
-hipError_t launch_prepare(int dt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13s, const float* w13a,
-                          const uint8_t* w2, const uint8_t* w2s, const float* w2a, uint8_t* packed, hipStream_t s);
+// gated: SwiGLU experts (W13 of 2I rows); otherwise ReLU^2 (W1 of I rows)
+hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t* w13, const uint8_t* w13s,
+                          const float* w13a, const uint8_t* w2, const uint8_t* w2s, const float* w2a, uint8_t* packed,
+                          hipStream_t s);
 
 // Grouped GEMMs.  `grid` is the persistent grid size (blocks).
-hipError_t launch_gemm13(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const int* offsets,
-                         const int* sorted_pairs, const uint8_t* xq, uint8_t* hq, int grid, hipStream_t s);
+hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
+                         const int* offsets, const int* sorted_pairs, const uint8_t* xq, uint8_t* hq, int grid,
+                         hipStream_t s);
 
-hipError_t launch_gemm2(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const int* offsets,
-                        const int* sorted_pairs, const uint8_t* hq, uint16_t* y, int grid, hipStream_t s);
+hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
+                        const int* offsets, const int* sorted_pairs, const uint8_t* hq, uint16_t* y, int grid,
+                        hipStream_t s);
 
 hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* wts, uint16_t* out, hipStream_t s);
 
@@ -45,7 +49,8 @@ int prefill_blocks_per_cu(int dt, bool g13);
 
 // The whole layer in one cooperative launch; `grid` must not exceed the
 // co-resident capacity (fused_blocks_per_cu * compute units).
-hipError_t launch_fused(int dt, int E, int H, int I, int k, int T, const uint8_t* packed, const float* logits,
+hipError_t launch_fused(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
+                        const float* logits,
                         const uint16_t* x, uint16_t* out, int* ids, float* wts, uint8_t* ws, size_t ws_bytes,
                         int max_tokens, int grid, hipStream_t s);
 int fused_blocks_per_cu(int dt, int variant);  // variant as gemm_variant

@@ -72,9 +72,11 @@ struct PackedLayout {
   size_t w13_codes, w13_scales, w2_codes, w2_scales, w13_alpha, w2_alpha, total;
 };
 
-MOE_HD PackedLayout packed_layout(int dt, int E, int H, int I) {
+// gated: SwiGLU experts, W13 row group g = 32 gate rows + the matching 32 up
+// rows; otherwise (ReLU^2) W1 of I rows in groups of 64.
+MOE_HD PackedLayout packed_layout(int dt, int E, int H, int I, bool gated = true) {
   PackedLayout L;
-  L.G13 = I / 32;
+  L.G13 = gated ? I / 32 : I / 64;
   L.KG13 = H / kKGroup;
   L.G2 = H / 64;
   L.KG2 = I / kKGroup;

@@ -152,8 +152,9 @@ __device__ __forceinline__ int pf_swz(int r) { return (r >> 2) & 3; }
 // Epilogue of a 64 x 32 NSA wave tile in the 32x32 accumulator layout: lane l,
 // element e of acc[f][S] is weight row 32f + (e & 3) + 8 (e >> 2) + 4 (l >> 5)
 // of row group g, routed row r0 + 32 S + (l & 31).  Gate/up GEMM: SwiGLU of
-// the f = 0 (gate) and f = 1 (up) values, requantised per token row; down
-// GEMM: bf16 y rows of the pair.
+// the f = 0 (gate) and f = 1 (up) values (ReLU^2 experts: relu(v)^2 of both
+// fragments, 64 intermediates), requantised per token row; down GEMM: bf16 y
+// rows of the pair.
 template <int DT, bool G13, int NSA, int SW>
 __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2][SW], int r0, int r_end, int g, int e,
                                             int lane) {
@@ -165,75 +166,95 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
     const bool ok = r < r_end;
     if constexpr (G13) {
       const int I = a.n_out;
-      float h[16];
+      // requantise and store 32 intermediates of this token row
+      auto store_h = [&](const float(&h)[16], int gg) __attribute__((always_inline)) {
+        // h[4b + j] is intermediate index 32gg + 8b + 4hl + j
+        if (DT == DT_BF16 || (DT == DT_MXFP8 && a.act_bf16)) {  // bf16 intermediate
+          if (ok) {
+            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * gg + 4 * hl;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float gv = acc[0][S][i] * alpha, uv = acc[1][S][i] * alpha;
-        h[i] = gv / (1.0f + expf(-gv)) * uv;
-      }
-      // h[4b + j] is intermediate index 32g + 8b + 4hl + j
-      if (DT == DT_BF16 || (DT == DT_MXFP8 && a.act_bf16)) {  // bf16 intermediate
-        if (ok) {
-          uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)r * I + 32 * g + 4 * hl;
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            *reinterpret_cast<uint2*>(o + 8 * b) =
-                make_uint2(f32_to_bf16(h[4 * b]) | ((uint32_t)f32_to_bf16(h[4 * b + 1]) << 16),
-                           f32_to_bf16(h[4 * b + 2]) | ((uint32_t)f32_to_bf16(h[4 * b + 3]) << 16));
-        }
-      } else if constexpr (DT == DT_MXFP8) {
-        // one block of 32 along I: this lane's 16 values and lane l ^ 32's
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(h[i]));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-        const int sx = mx_scale_exp(amax);
-        if (ok) {
-          uint8_t* o = a.out + (size_t)r * I + 32 * g + 4 * hl;
-          uint16_t* od = a.out_deq + (size_t)r * I + 32 * g + 4 * hl;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            uint32_t v = 0, d[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t c = e4m3_from_f32(ldexpf(h[4 * b + j], -sx));
-              v |= c << (8 * j);
-              d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), sx)) >> 16;  // exact in bf16
-            }
-            *reinterpret_cast<uint32_t*>(o + 8 * b) = v;
-            *reinterpret_cast<uint2*>(od + 8 * b) = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+            for (int b = 0; b < 4; ++b)
+              *reinterpret_cast<uint2*>(o + 8 * b) =
+                  make_uint2(f32_to_bf16(h[4 * b]) | ((uint32_t)f32_to_bf16(h[4 * b + 1]) << 16),
+                             f32_to_bf16(h[4 * b + 2]) | ((uint32_t)f32_to_bf16(h[4 * b + 3]) << 16));
           }
-          if (hl == 0) a.out_scales[(size_t)r * (I / 32) + g] = (uint8_t)(sx + 127);
-        }
-      } else if constexpr (DT == DT_NVFP4) {
-        // two blocks of 16 along I: tp = 0 holds b = 0, 1; tp = 1 holds b = 2, 3
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
+        } else if constexpr (DT == DT_MXFP8) {
+          // one block of 32 along I: this lane's 16 values and lane l ^ 32's
           float amax = 0.f;
 #pragma unroll
-          for (int i = 8 * tp; i < 8 * tp + 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
+          for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(h[i]));
           amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-          const uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
-          const float sc = e4m3_to_f32(sc_code);
+          const int sx = mx_scale_exp(amax);
+          if (ok) {
+            uint8_t* o = a.out + (size_t)r * I + 32 * gg + 4 * hl;
+            uint16_t* od = a.out_deq + (size_t)r * I + 32 * gg + 4 * hl;
 #pragma unroll
-          for (int bb = 0; bb < 2; ++bb) {
-            const int b = 2 * tp + bb;
-            uint32_t v = 0, d[4];
+            for (int b = 0; b < 4; ++b) {
+              uint32_t v = 0, d[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float x = h[4 * b + j];
-              const uint32_t c = sc > 0.f ? e2m1_from_f32(x, sc) : ((__float_as_uint(x) >> 28) & 8u);
-              v |= c << (4 * j);
-              d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
+              for (int j = 0; j < 4; ++j) {
+                const uint32_t c = e4m3_from_f32(ldexpf(h[4 * b + j], -sx));
+                v |= c << (8 * j);
+                d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), sx)) >> 16;  // exact in bf16
+              }
+              *reinterpret_cast<uint32_t*>(o + 8 * b) = v;
+              *reinterpret_cast<uint2*>(od + 8 * b) = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
             }
-            if (ok) {
-              *reinterpret_cast<uint16_t*>(a.out + (size_t)r * (I / 2) + 16 * g + 4 * b + 2 * hl) = (uint16_t)v;
-              *reinterpret_cast<uint2*>(a.out_deq + (size_t)r * I + 32 * g + 8 * b + 4 * hl) =
-                  make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
-            }
+            if (hl == 0) a.out_scales[(size_t)r * (I / 32) + gg] = (uint8_t)(sx + 127);
           }
-          if (ok && hl == 0) a.out_scales[(size_t)r * (I / 16) + 2 * g + tp] = (uint8_t)sc_code;
+        } else if constexpr (DT == DT_NVFP4) {
+          // two blocks of 16 along I: tp = 0 holds b = 0, 1; tp = 1 holds b = 2, 3
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp) {
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 8 * tp; i < 8 * tp + 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+            const uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
+            const float sc = e4m3_to_f32(sc_code);
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+              const int b = 2 * tp + bb;
+              uint32_t v = 0, d[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float x = h[4 * b + j];
+                const uint32_t c = sc > 0.f ? e2m1_from_f32(x, sc) : ((__float_as_uint(x) >> 28) & 8u);
+                v |= c << (4 * j);
+                d[j] = f32_to_f16_bits(e2m1_to_f32(c) * sc);  // exact in fp16
+              }
+              if (ok) {
+                *reinterpret_cast<uint16_t*>(a.out + (size_t)r * (I / 2) + 16 * gg + 4 * b + 2 * hl) = (uint16_t)v;
+                *reinterpret_cast<uint2*>(a.out_deq + (size_t)r * I + 32 * gg + 8 * b + 4 * hl) =
+                    make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+              }
+            }
+            if (ok && hl == 0) a.out_scales[(size_t)r * (I / 16) + 2 * gg + tp] = (uint8_t)sc_code;
+          }
         }
+      };
+      // SwiGLU: one set of 32 intermediates (group g) from the gate (f = 0)
+      // and up (f = 1) fragments.  ReLU^2: fragment f holds W1 rows 64g + 32f
+      // + ..., the intermediates of half group 2g + f.  One copy of the store
+      // code serves both (the fragment is selected, not indexed).
+      const int halves = a.gated ? 1 : 2;
+#pragma unroll 1
+      for (int f = 0; f < halves; ++f) {
+        float h[16];
+        if (a.gated) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float gv = acc[0][S][i] * alpha, uv = acc[1][S][i] * alpha;
+            h[i] = gv / (1.0f + expf(-gv)) * uv;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float t = fmaxf((f ? acc[1][S][i] : acc[0][S][i]) * alpha, 0.f);
+            h[i] = t * t;
+          }
+        }
+        store_h(h, a.gated ? g : 2 * g + f);
       }
     } else {
       if (ok) {

@@ -52,6 +52,12 @@ class Workload:
     dtype: str      # "bf16" | "mxfp8" | "nvfp4" | "bf16_mxfp8" (bf16 activations, MXFP8 weights)
     bias: str       # "none" | "normal2" | "zipf1.1"
     cid: int        # seed id of the workload
+    act: str = "swiglu"  # "swiglu" (gated, W13 of 2I rows) | "relu2" (non-gated, W1 of I rows)
+
+    @property
+    def R13(self) -> int:
+        """Rows of W13: 2I (gate and up) for SwiGLU, I (W1) for ReLU^2."""
+        return 2 * self.I if self.act == "swiglu" else self.I
 
     @property
     def P(self) -> int:
@@ -78,6 +84,8 @@ WORKLOADS = {
         # bf16 activations over the MXFP8 layers' weights (same seeds, same weights)
         Workload("bf16_mxfp8_decode", 32, 7168, 2048, 256, 8, "bf16_mxfp8", "normal2", 3),
         Workload("bf16_mxfp8_prefill", 8192, 7168, 2048, 256, 8, "bf16_mxfp8", "zipf1.1", 5),
+        # non-gated squared-ReLU experts (W1 of I rows) at the NVFP4 decode shape
+        Workload("relu2_nvfp4_decode_t128", 128, 7168, 2048, 384, 8, "nvfp4", "none", 4, "relu2"),
     ]
 }
 
@@ -136,15 +144,15 @@ def host_logits(w: Workload) -> np.ndarray:
 
 
 def host_master_weights(w: Workload, e: int) -> tuple[np.ndarray, np.ndarray]:
-    """fp32 master weights of expert e: W13 [2I, H], W2 [H, I], ~ N(0, 0.02)."""
-    w13 = _rng(w.cid, W13_STREAM, e).standard_normal((2 * w.I, w.H), dtype=np.float32)
+    """fp32 master weights of expert e: W13 [R13, H], W2 [H, I], ~ N(0, 0.02)."""
+    w13 = _rng(w.cid, W13_STREAM, e).standard_normal((w.R13, w.H), dtype=np.float32)
     w2 = _rng(w.cid, W2_STREAM, e).standard_normal((w.H, w.I), dtype=np.float32)
     return w13 * np.float32(WEIGHT_STD), w2 * np.float32(WEIGHT_STD)
 
 
 def host_all_master_weights(w: Workload) -> tuple[np.ndarray, np.ndarray]:
     """All experts' fp32 master weights (small workloads only)."""
-    w13 = np.empty((w.E, 2 * w.I, w.H), np.float32)
+    w13 = np.empty((w.E, w.R13, w.H), np.float32)
     w2 = np.empty((w.E, w.H, w.I), np.float32)
     for e in range(w.E):
         w13[e], w2[e] = host_master_weights(w, e)
@@ -176,11 +184,11 @@ def device_logits(w: Workload, device="cuda"):
 
 
 def device_master_weights(w: Workload, e: int, device="cuda"):
-    """fp32 master weights of expert e on `device`: W13 [2I, H], W2 [H, I]."""
+    """fp32 master weights of expert e on `device`: W13 [R13, H], W2 [H, I]."""
     import torch
 
     g = torch.Generator(device=device).manual_seed(device_seed(w.cid, W13_STREAM, e))
-    w13 = torch.randn(2 * w.I, w.H, generator=g, device=device, dtype=torch.float32)
+    w13 = torch.randn(w.R13, w.H, generator=g, device=device, dtype=torch.float32)
     g = torch.Generator(device=device).manual_seed(device_seed(w.cid, W2_STREAM, e))
     w2 = torch.randn(w.H, w.I, generator=g, device=device, dtype=torch.float32)
     return w13 * WEIGHT_STD, w2 * WEIGHT_STD

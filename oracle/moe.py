@@ -26,6 +26,10 @@ Readings where the pages are silent (all documented with the design):
    beside the three formats [MegaMoE drop workflow, §1, the package exports]
    and say nothing more): MXFP8 weights with the activation path of the BF16
    layer -- x is used as given and the intermediate is rounded to bf16.
+8. ReLU^2 experts (the pages note that models with squared-ReLU, non-gated
+   experts, such as Nemotron, are rejected by the b12x backend [vLLM PR 40082
+   report, "Risks" item 4]): W1 = W13 holds I rows and h = relu(W1 x)^2,
+   requantised like the SwiGLU intermediate; the rest of the layer is the same.
 
 Arithmetic: dequantised operands are exact in float64, dot products and the
 SwiGLU are evaluated in float64, and rounding to fp32 happens only where the
@@ -112,7 +116,8 @@ class Weights:
                  + w13_a fp32 [E]; same for w2
     dtype bf16_mxfp8: as mxfp8 (the layer format's weights)
     Any of the per-expert arrays may be a mapping {expert: array} holding only
-    the experts a computation needs.
+    the experts a computation needs.  act "swiglu": W13 rows [0, I) gate,
+    [I, 2I) up; act "relu2": W13 is W1 of I rows.
     """
 
     dtype: str
@@ -122,6 +127,7 @@ class Weights:
     w2_s: object = None
     w13_a: object = None
     w2_a: object = None
+    act: str = "swiglu"
 
     def dequant(self, e: int):
         """Exact float64 dequantised (W13 [2I, H], W2 [H, I]) of expert e."""
@@ -134,7 +140,7 @@ class Weights:
         return w13, w2
 
 
-def quantize_weights(w13_f32: dict, w2_f32: dict, dtype: str) -> Weights:
+def quantize_weights(w13_f32: dict, w2_f32: dict, dtype: str, act: str = "swiglu") -> Weights:
     """Quantise fp32 master weights {e: array} into canonical form (harness)."""
     out = {k: {} for k in ("w13", "w13_s", "w13_a", "w2", "w2_s", "w2_a")}
     wf = weight_format(dtype)
@@ -146,7 +152,7 @@ def quantize_weights(w13_f32: dict, w2_f32: dict, dtype: str) -> Weights:
             out[n] = None
     if wf == "mxfp8":
         out["w13_a"] = out["w2_a"] = None
-    return Weights(dtype=dtype, **out)
+    return Weights(dtype=dtype, act=act, **out)
 
 
 # ------------------------------------------------------------------ the layer
@@ -157,6 +163,12 @@ def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     "Implementation" item 1; "Risks" item 4: only gated act-and-mul MLPs]."""
     with np.errstate(over="ignore"):
         return g / (1.0 + np.exp(-g)) * u
+
+
+def relu2(g: np.ndarray) -> np.ndarray:
+    """Squared ReLU activation of non-gated experts: max(g, 0)^2."""
+    r = np.maximum(g, 0.0)
+    return r * r
 
 
 def requant_h(h64: np.ndarray, dtype: str):
@@ -213,10 +225,12 @@ def moe_layer(x_bits, logits, W: Weights, k: int, tokens=None, keep=False) -> La
             if e not in cache:
                 cache[e] = W.dequant(e)
             w13, w2 = cache[e]
-            I = w13.shape[0] // 2
-            g = w13[:I] @ xh
-            u = w13[I:] @ xh
-            hc, hsc, hh = requant_h(silu_mul(g, u)[None, :], W.dtype)
+            if W.act == "relu2":
+                h = relu2(w13 @ xh)
+            else:
+                I = w13.shape[0] // 2
+                h = silu_mul(w13[:I] @ xh, w13[I:] @ xh)
+            hc, hsc, hh = requant_h(h[None, :], W.dtype)
             y = w2 @ hh[0]
             acc += wts[t, j] * y
             if keep:
@@ -248,11 +262,15 @@ def moe_layer_grouped(x_bits, logits, W: Weights, k: int, acc_dtype=np.float64):
             continue
         pairs = sorted_pairs[lo:hi]
         w13, w2 = W.dequant(e)
-        I = w13.shape[0] // 2
         X = xh[pairs // k]
-        G = X @ w13[:I].T.astype(acc_dtype)
-        U = X @ w13[I:].T.astype(acc_dtype)
-        _, _, hh = requant_h(silu_mul(G.astype(np.float64), U.astype(np.float64)), W.dtype)
+        if W.act == "relu2":
+            Hm = relu2((X @ w13.T.astype(acc_dtype)).astype(np.float64))
+        else:
+            I = w13.shape[0] // 2
+            G = X @ w13[:I].T.astype(acc_dtype)
+            U = X @ w13[I:].T.astype(acc_dtype)
+            Hm = silu_mul(G.astype(np.float64), U.astype(np.float64))
+        _, _, hh = requant_h(Hm, W.dtype)
         y[pairs] = hh.astype(acc_dtype) @ w2.T.astype(acc_dtype)
     y = y.reshape(T, k, H)
     out64 = np.zeros((T, H), np.float64)

@@ -50,19 +50,19 @@ class CanonicalWeights:
 
 
 def alloc_canonical(w: mi.Workload) -> CanonicalWeights:
-    d, E, H, I = dev(), w.E, w.H, w.I
+    d, E, H, I, R = dev(), w.E, w.H, w.I, w.R13
     u8 = torch.uint8
     wf = weight_format(w.dtype)
     if wf == "bf16":
-        return CanonicalWeights(torch.empty(E, 2 * I, H, dtype=torch.bfloat16, device=d),
+        return CanonicalWeights(torch.empty(E, R, H, dtype=torch.bfloat16, device=d),
                                 torch.empty(E, H, I, dtype=torch.bfloat16, device=d), None, None, None, None)
     if wf == "mxfp8":
-        return CanonicalWeights(torch.empty(E, 2 * I, H, dtype=u8, device=d), torch.empty(E, H, I, dtype=u8, device=d),
-                                torch.empty(E, 2 * I, H // 32, dtype=u8, device=d),
+        return CanonicalWeights(torch.empty(E, R, H, dtype=u8, device=d), torch.empty(E, H, I, dtype=u8, device=d),
+                                torch.empty(E, R, H // 32, dtype=u8, device=d),
                                 torch.empty(E, H, I // 32, dtype=u8, device=d), None, None)
-    return CanonicalWeights(torch.empty(E, 2 * I, H // 2, dtype=u8, device=d),
+    return CanonicalWeights(torch.empty(E, R, H // 2, dtype=u8, device=d),
                             torch.empty(E, H, I // 2, dtype=u8, device=d),
-                            torch.empty(E, 2 * I, H // 16, dtype=u8, device=d),
+                            torch.empty(E, R, H // 16, dtype=u8, device=d),
                             torch.empty(E, H, I // 16, dtype=u8, device=d),
                             torch.empty(E, dtype=torch.float32, device=d),
                             torch.empty(E, dtype=torch.float32, device=d))
@@ -74,7 +74,7 @@ def _sub(t, e):
 
 def quantize_expert(w: mi.Workload, cw: CanonicalWeights, e: int, w13_f32: torch.Tensor, w2_f32: torch.Tensor):
     """Quantise expert e's fp32 master weights (device tensors) with the library."""
-    lib.moe_quantize_weights(w.dtype, 1, 2 * w.I, w.H, w13_f32, cw.w13[e:e + 1], _sub(cw.w13_s, e), _sub(cw.w13_a, e))
+    lib.moe_quantize_weights(w.dtype, 1, w.R13, w.H, w13_f32, cw.w13[e:e + 1], _sub(cw.w13_s, e), _sub(cw.w13_a, e))
     lib.moe_quantize_weights(w.dtype, 1, w.H, w.I, w2_f32, cw.w2[e:e + 1], _sub(cw.w2_s, e), _sub(cw.w2_a, e))
 
 
@@ -85,7 +85,7 @@ def canonical_from_host_master(w: mi.Workload):
     cw = alloc_canonical(w)
     t13 = torch.from_numpy(w13f).to(dev())
     t2 = torch.from_numpy(w2f).to(dev())
-    lib.moe_quantize_weights(w.dtype, w.E, 2 * w.I, w.H, t13, cw.w13, cw.w13_s, cw.w13_a)
+    lib.moe_quantize_weights(w.dtype, w.E, w.R13, w.H, t13, cw.w13, cw.w13_s, cw.w13_a)
     lib.moe_quantize_weights(w.dtype, w.E, w.H, w.I, t2, cw.w2, cw.w2_s, cw.w2_a)
     return cw, w13f, w2f
 
@@ -116,7 +116,7 @@ class DeviceLayer:
 
     def __init__(self, w: mi.Workload, cw: CanonicalWeights, max_tokens: int | None = None):
         self.w = w
-        self.shape = lib.make_shape(w.H, w.I, w.E, w.k, max_tokens or w.T, w.dtype)
+        self.shape = lib.make_shape(w.H, w.I, w.E, w.k, max_tokens or w.T, w.dtype, w.act)
         assert lib.moe_check_shape(self.shape) == 0, self.shape
         nbytes = lib.moe_packed_weight_bytes(self.shape)
         self.packed = torch.empty(nbytes, dtype=torch.uint8, device=dev())

@@ -34,8 +34,8 @@ def test_library_exports_every_declared_symbol():
     assert set(_declared()) <= exported
 
 
-def S(H=256, I=512, E=8, k=2, T=16, dt="bf16"):
-    return lib.make_shape(H, I, E, k, T, dt)
+def S(H=256, I=512, E=8, k=2, T=16, dt="bf16", act="swiglu"):
+    return lib.make_shape(H, I, E, k, T, dt, act)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -45,6 +45,7 @@ def S(H=256, I=512, E=8, k=2, T=16, dt="bf16"):
     ({"k": 0}, UNSUPPORTED), ({"k": 33, "E": 64}, UNSUPPORTED), ({"k": 9, "E": 8}, UNSUPPORTED),
     ({"T": 0}, UNSUPPORTED), ({"T": 1 << 22, "k": 8}, UNSUPPORTED), ({"dt": "bf16_mxfp8"}, OK),
     ({"dt": 4}, UNSUPPORTED), ({"dt": -1}, UNSUPPORTED),
+    ({"act": "relu2"}, OK), ({"act": "relu2", "dt": "nvfp4"}, OK), ({"act": 2}, UNSUPPORTED), ({"act": -1}, UNSUPPORTED),
 ])
 def test_shape_validation(kw, status):
     args = dict(H=256, I=512, E=8, k=2, T=16, dt="bf16")
@@ -72,6 +73,13 @@ def test_sizes_match_layouts():
     s = S(512, 256, 8, 4, 64, "nvfp4")
     assert lib.moe_xq_scale_offset(s, T) == ((T * 256 + 255) // 256) * 256
     assert lib.moe_xq_bytes(s, 65) == 0  # T beyond max_tokens
+    # squared-ReLU experts: W1 holds I rows instead of 2I
+    s = S(4096, 1408, 64, 6, 64, "bf16", "relu2")
+    assert lib.moe_packed_weight_bytes(s) == 64 * 2 * 4096 * 1408 * 2
+    s = S(7168, 2048, 256, 8, 8192, "mxfp8", "relu2")
+    canon = 256 * 2 * 7168 * 2048
+    assert lib.moe_packed_weight_bytes(s) == canon + canon // 32
+    assert lib.moe_workspace_bytes(s) == lib.moe_workspace_bytes(S(7168, 2048, 256, 8, 8192, "mxfp8"))
     # bf16 activations over MXFP8 weights: the weights of MXFP8, the activations of BF16
     for shape in [(7168, 2048, 256, 8, 8192), (512, 256, 8, 4, 64)]:
         a, m, b = S(*shape, "bf16_mxfp8"), S(*shape, "mxfp8"), S(*shape, "bf16")

@@ -62,7 +62,8 @@ def _pick_tokens(ids, k, limit):
 
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "bf16_decode", "mxfp8_decode", "nvfp4_decode_t8",
-                                  "nvfp4_decode_t128", "bf16_mxfp8_decode", "mxfp8_prefill"])
+                                  "nvfp4_decode_t128", "bf16_mxfp8_decode", "relu2_nvfp4_decode_t128",
+                                  "mxfp8_prefill"])
 def test_fullsize_parity(name, pool):
     w = W[name]
     dev = gh.dev()
@@ -126,11 +127,11 @@ def test_fullsize_parity(name, pool):
             assert float(got["w13_a"][e]) == float(a13) and float(got["w2_a"][e]) == float(a2), e
     _log(f"{name}: library weight codes of {len(experts)} experts equal the oracle's")
     if w.dtype == "bf16":
-        Wo = omoe.Weights("bf16", ow["w13"], ow["w2"])
+        Wo = omoe.Weights("bf16", ow["w13"], ow["w2"], act=w.act)
     elif gh.weight_format(w.dtype) == "mxfp8":
-        Wo = omoe.Weights(w.dtype, ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"])
+        Wo = omoe.Weights(w.dtype, ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"], act=w.act)
     else:
-        Wo = omoe.Weights("nvfp4", ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"], ow["w13_a"], ow["w2_a"])
+        Wo = omoe.Weights("nvfp4", ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"], ow["w13_a"], ow["w2_a"], act=w.act)
     ref = omoe.moe_layer(x_bits, l_host, Wo, w.k, tokens=toks, keep=True)
     hc, hs = layer.hq_numpy(r, w.T)
     y = gh.bf16_numpy(r["y"])

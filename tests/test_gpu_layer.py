@@ -37,12 +37,19 @@ SMALL = {
     # bf16 activations over MXFP8 weights: decode and prefill-shaped GEMMs
     "bf16_mxfp8_decode_small": W["bf16_mxfp8_decode"].scaled(T=40, H=640, I=256, E=32),
     "bf16_mxfp8_prefill_small": W["bf16_mxfp8_prefill"].scaled(T=520, H=256, I=384, E=8, k=2),
+    # non-gated squared-ReLU experts, every format, decode- and prefill-shaped GEMMs
+    "relu2_bf16_small": W["bf16_decode"].scaled(T=33, H=512, I=384, E=16, act="relu2"),
+    "relu2_mxfp8_decode_small": W["mxfp8_decode"].scaled(T=40, H=640, I=256, E=32, act="relu2"),
+    "relu2_nvfp4_decode_small": W["nvfp4_decode_t8"].scaled(T=13, H=512, I=256, E=48, act="relu2"),
+    "relu2_mxfp8_prefill_skewed": W["mxfp8_prefill"].scaled(T=520, H=256, I=384, E=8, k=2, act="relu2"),
+    "relu2_nvfp4_prefill_tiles": W["nvfp4_decode_t128"].scaled(T=200, H=384, I=256, E=4, k=2, act="relu2"),
+    "relu2_bf16_mxfp8_prefill": W["bf16_mxfp8_prefill"].scaled(T=300, H=256, I=256, E=4, k=2, act="relu2"),
 }
 
 
 def _setup(w):
     cw, w13f, w2f = gh.canonical_from_host_master(w)
-    Wo = omoe.quantize_weights({e: w13f[e] for e in range(w.E)}, {e: w2f[e] for e in range(w.E)}, w.dtype)
+    Wo = omoe.quantize_weights({e: w13f[e] for e in range(w.E)}, {e: w2f[e] for e in range(w.E)}, w.dtype, w.act)
     return cw, Wo
 
 

@@ -19,48 +19,55 @@ def _act(dtype):
     return "bf16" if dtype == "bf16_mxfp8" else dtype
 
 
-def _small(dtype, T=6, H=64, I=64, E=5, k=2, bias="none", cid=91):
-    return mi.Workload(f"small_{dtype}", T, H, I, E, k, dtype, bias, cid)
+def _small(dtype, T=6, H=64, I=64, E=5, k=2, bias="none", cid=91, act="swiglu"):
+    return mi.Workload(f"small_{dtype}_{act}", T, H, I, E, k, dtype, bias, cid, act)
 
 
 def _weights(w):
     w13, w2 = mi.host_all_master_weights(w)
-    return moe.quantize_weights({e: w13[e] for e in range(w.E)}, {e: w2[e] for e in range(w.E)}, w.dtype)
+    return moe.quantize_weights({e: w13[e] for e in range(w.E)}, {e: w2[e] for e in range(w.E)}, w.dtype, w.act)
 
 
-def _mlp_torch(x_hat, W13, W2, dtype):
-    """Dense SwiGLU MLP written with torch.nn.functional in fp64, with the
-    layer's requantisation of the intermediate (the quantiser is pinned in
+def _mlp_torch(x_hat, W13, W2, dtype, act="swiglu"):
+    """Dense expert MLP written with torch.nn.functional in fp64 -- SwiGLU
+    (gate rows, then up rows) or squared ReLU of W1 -- with the layer's
+    requantisation of the intermediate (the quantiser is pinned in
     test_oracle_quant)."""
-    I = W13.shape[0] // 2
     xt = torch.from_numpy(x_hat)
-    g = F.linear(xt, torch.from_numpy(W13[:I]))
-    u = F.linear(xt, torch.from_numpy(W13[I:]))
-    h = (F.silu(g) * u).numpy()
+    if act == "relu2":
+        h = (F.relu(F.linear(xt, torch.from_numpy(W13))) ** 2).numpy()
+    else:
+        I = W13.shape[0] // 2
+        g = F.linear(xt, torch.from_numpy(W13[:I]))
+        u = F.linear(xt, torch.from_numpy(W13[I:]))
+        h = (F.silu(g) * u).numpy()
     c, s = quant.quantize_act(h.astype(np.float32), _act(dtype))
     hh = quant.dequantize_act(c, s, _act(dtype))
     return F.linear(torch.from_numpy(hh), torch.from_numpy(W2)).numpy()
 
 
+@pytest.mark.parametrize("act", ["swiglu", "relu2"])
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_e1_top1_is_dense_swiglu_mlp(dtype):
-    w = _small(dtype, T=9, E=1, k=1)
+def test_e1_top1_is_dense_mlp(dtype, act):
+    w = _small(dtype, T=9, E=1, k=1, act=act)
     W = _weights(w)
+    assert W.dequant(0)[0].shape == (w.R13, w.H)
     x = mi.host_x(w)
     l = mi.host_logits(w)
     r = moe.moe_layer(x, l, W, 1)
     xc, xs, xh = moe.quantize_x(x, dtype)
     W13, W2 = W.dequant(0)
-    ref = _mlp_torch(xh, W13, W2, dtype)
+    ref = _mlp_torch(xh, W13, W2, dtype, act)
     assert np.allclose(r.out_f64, ref, rtol=1e-12, atol=1e-12)
     assert np.array_equal(r.out, codecs.bf16_encode(ref.astype(np.float32)))
 
 
+@pytest.mark.parametrize("act", ["swiglu", "relu2"])
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_dense_masked_brute_force(dtype):
+def test_dense_masked_brute_force(dtype, act):
     """out_t = sum_e G[t, e] * MLP_e(x_hat_t) with G the renormalised top-k
     gate matrix built from scipy's full softmax."""
-    w = _small(dtype, T=7, E=6, k=3)
+    w = _small(dtype, T=7, E=6, k=3, act=act)
     W = _weights(w)
     x = mi.host_x(w)
     l = mi.host_logits(w)
@@ -74,13 +81,13 @@ def test_dense_masked_brute_force(dtype):
     ref = np.zeros((w.T, w.H))
     for e in range(w.E):
         W13, W2 = W.dequant(e)
-        ref += G[:, e:e + 1] * _mlp_torch(xh, W13, W2, dtype)
+        ref += G[:, e:e + 1] * _mlp_torch(xh, W13, W2, dtype, act)
     assert np.allclose(r.out_f64, ref, rtol=1e-11, atol=1e-13)
 
 
-@pytest.mark.parametrize("dtype", DTYPES)
-def test_relabelling_invariance(dtype):
-    w = _small(dtype, T=8, E=7, k=3)
+@pytest.mark.parametrize("dtype,act", [(d, "swiglu") for d in DTYPES] + [("mxfp8", "relu2"), ("nvfp4", "relu2")])
+def test_relabelling_invariance(dtype, act):
+    w = _small(dtype, T=8, E=7, k=3, act=act)
     W = _weights(w)
     x = mi.host_x(w)
     l = mi.host_logits(w)
@@ -89,7 +96,8 @@ def test_relabelling_invariance(dtype):
     inv = np.argsort(pi)
     def perm(a):
         return None if a is None else {pi[e]: a[e] for e in range(w.E)}
-    Wp = moe.Weights(dtype, perm(W.w13), perm(W.w2), perm(W.w13_s), perm(W.w2_s), perm(W.w13_a), perm(W.w2_a))
+    Wp = moe.Weights(dtype, perm(W.w13), perm(W.w2), perm(W.w13_s), perm(W.w2_s), perm(W.w13_a), perm(W.w2_a),
+                     act=W.act)
     lp = l[:, inv]  # column pi[e] holds old column e
     got = moe.moe_layer(x, lp, Wp, w.k)
     assert np.array_equal(got.out, base.out)
@@ -97,9 +105,9 @@ def test_relabelling_invariance(dtype):
     assert np.array_equal(got.ids, pi[base.ids])
 
 
-@pytest.mark.parametrize("dtype", DTYPES)
-def test_loop_and_grouped_forms_agree(dtype):
-    w = _small(dtype, T=20, H=128, I=96, E=8, k=3, bias="normal2")
+@pytest.mark.parametrize("dtype,act", [(d, "swiglu") for d in DTYPES] + [("bf16", "relu2"), ("nvfp4", "relu2")])
+def test_loop_and_grouped_forms_agree(dtype, act):
+    w = _small(dtype, T=20, H=128, I=96, E=8, k=3, bias="normal2", act=act)
     W = _weights(w)
     x = mi.host_x(w)
     l = mi.host_logits(w)
