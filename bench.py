@@ -153,17 +153,18 @@ class StagedStep:
 
 def layer_bytes_flops(w, n_active):
     """Algorithmic bytes and flops of one step: weights (with scales) of the
-    active experts, x in, out, logits; flops 6*H*I per routed pair."""
-    wb = n_active * 3 * w.H * w.I * weight_bytes_per_elem(w.dtype)
+    active experts, x in, out, logits; flops 2*H*(R13 + I) per routed pair
+    (R13 = 2I rows of W13 for SwiGLU experts, I for ReLU^2)."""
+    wb = n_active * (w.R13 + w.I) * w.H * weight_bytes_per_elem(w.dtype)
     B = wb + 2 * w.T * w.H * 2 + 4 * w.T * w.E
-    F = w.T * w.k * 6.0 * w.H * w.I
+    F = w.T * w.k * 2.0 * w.H * (w.R13 + w.I)
     return B, F
 
 
 def gemm13_bytes(w, n_active):
     """Algorithmic bytes of one gate/up GEMM launch: W13 of the active experts
     (with scales), the quantised activations read, the intermediate written."""
-    return (n_active * 2 * w.I * w.H * weight_bytes_per_elem(w.dtype) + w.T * w.H * act_bytes_per_elem(w.dtype)
+    return (n_active * w.R13 * w.H * weight_bytes_per_elem(w.dtype) + w.T * w.H * act_bytes_per_elem(w.dtype)
             + w.T * w.k * w.I * act_bytes_per_elem(w.dtype))
 
 
@@ -192,7 +193,7 @@ def cpu_baseline(w, device, ids, max_seconds=25.0):
     for e in sorted(experts):
         a, b = mi.device_master_weights(w, e, device)
         w13[e], w2[e] = a.cpu().numpy(), b.cpu().numpy()
-    Wo = omoe.quantize_weights(w13, w2, w.dtype)  # weight quantisation: not timed
+    Wo = omoe.quantize_weights(w13, w2, w.dtype, w.act)  # weight quantisation: not timed
     del w13, w2
     threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     # repeat a short sample until about 10 s of CPU work have been timed
@@ -389,7 +390,7 @@ def main():
     tflops = F / (gpu_ms_step * 1e-3) / 1e12
     g13b = gemm13_bytes(w, n_active)
     g13_gbs = g13b / (kms["gemm13"] * 1e-3) / 1e9
-    g13_tflops = w.T * w.k * 4.0 * w.H * w.I / (kms["gemm13"] * 1e-3) / 1e12
+    g13_tflops = w.T * w.k * 2.0 * w.H * w.R13 / (kms["gemm13"] * 1e-3) / 1e12
     traffic = load_traffic(w.name)
     decode = w.T * w.k <= 16 * w.E
     if decode:
@@ -399,7 +400,7 @@ def main():
     else:
         roof = {"bound": "mfma", "kernel": "gemm13_swiglu_quant", "achieved": g13_tflops,
                 "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s", "frac": g13_tflops / MFMA_PEAK_TFLOPS[w.dtype],
-                "traffic": traffic, "algorithmic_flops_per_launch": w.T * w.k * 4.0 * w.H * w.I,
+                "traffic": traffic, "algorithmic_flops_per_launch": w.T * w.k * 2.0 * w.H * w.R13,
                 "avg_launch_ms": kms["gemm13"]}
     rec = {
         "metric": "MoE layer tokens/s; % HBM BW (decode) / % MFMA peak (prefill)",
@@ -415,7 +416,7 @@ def main():
         "dtype": ARITH_DTYPE[w.dtype],
         "data": "synthetic (seeded N(0,1) x and logits, N(0,0.02) weights; random init)",
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.k,
-                   "weights": w.dtype, "routing_skew": w.bias, "active_experts": n_active},
+                   "weights": w.dtype, "activation": w.act, "routing_skew": w.bias, "active_experts": n_active},
         "roofline": roof,
         "layer": {"algorithmic_bytes": B, "flops": F, "gpu_ms_per_step": gpu_ms_step, "hbm_gbs": layer_gbs,
                   "hbm_frac": layer_gbs / HBM_PEAK_GBS, "mfma_tflops": tflops,
