@@ -126,10 +126,20 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   const int total_mt = build_schedule(a.offsets, a.E, MT, cum, wsum);
   const long long n13 = (long long)total_mt * per13, n2 = (long long)total_mt * per2;
   const int lb = V == 2 ? xcd_logical_block() : (int)blockIdx.x;
+  // decode items: the blocks of a compute unit take turns at the top issue
+  // priority, as in the stage kernels (later-placed blocks otherwise lag)
+  int turn = (int)(blockIdx.x >> 8);
   if constexpr (MOE_FUSED_GEMM_BARRIER) {
-    for (long long w = lb; w < n13; w += G) item(a.g13, true, w);
+    for (long long w = lb; w < n13; w += G, ++turn) {
+      if constexpr (V != 2) set_wave_priority(turn & 3);
+      item(a.g13, true, w);
+    }
     grid_barrier(a.sync, 3 * G);
-    for (long long w = lb; w < n2; w += G) item(a.g2, false, w);
+    for (long long w = lb; w < n2; w += G, ++turn) {
+      if constexpr (V != 2) set_wave_priority(turn & 3);
+      item(a.g2, false, w);
+    }
+    set_wave_priority(0);
     grid_barrier(a.sync, 4 * G);
   } else {
     for (long long w = lb; w < n13 + n2; w += G) {

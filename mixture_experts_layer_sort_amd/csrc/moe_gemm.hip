@@ -21,15 +21,6 @@
 
 namespace moe {
 
-__device__ __forceinline__ void set_wave_priority(int p) {
-  switch (p) {
-    case 0: __builtin_amdgcn_s_setprio(0); break;
-    case 1: __builtin_amdgcn_s_setprio(1); break;
-    case 2: __builtin_amdgcn_s_setprio(2); break;
-    default: __builtin_amdgcn_s_setprio(3); break;
-  }
-}
-
 // Every block gets the same number of items, so a compute unit finishes with
 // its slowest resident block.  Measured on MI355X, the blocks placed later on
 // a compute unit (higher block ids: the first 256 blocks take one unit each,

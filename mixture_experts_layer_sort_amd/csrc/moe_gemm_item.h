@@ -23,6 +23,16 @@ struct GemmArgs {
   int E, K, G, KG, k, n_out;
 };
 
+// This wave's issue priority (0..3; s_setprio takes an immediate).
+__device__ __forceinline__ void set_wave_priority(int p) {
+  switch (p) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
 // cum[e] = m-tiles of experts < e (LDS), returns the total.  The first
 // kGemmThreads threads do the scan; a larger block only waits for it.
 // wsum holds kGemmThreads / 64 ints.

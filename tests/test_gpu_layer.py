@@ -44,6 +44,9 @@ SMALL = {
     "relu2_mxfp8_prefill_skewed": W["mxfp8_prefill"].scaled(T=520, H=256, I=384, E=8, k=2, act="relu2"),
     "relu2_nvfp4_prefill_tiles": W["nvfp4_decode_t128"].scaled(T=200, H=384, I=256, E=4, k=2, act="relu2"),
     "relu2_bf16_mxfp8_prefill": W["bf16_mxfp8_prefill"].scaled(T=300, H=256, I=256, E=4, k=2, act="relu2"),
+    # the largest expert count and top-k the library accepts
+    "max_experts_topk32": W["tiny_bf16"].scaled(E=1024, k=32, T=40, H=128, I=128),
+    "max_experts_topk32_nvfp4": W["nvfp4_decode_t8"].scaled(E=1024, k=32, T=24, H=128, I=128),
 }
 
 
@@ -147,7 +150,10 @@ def test_route_parity(T, E, k):
 
 
 @pytest.mark.parametrize("T,E,k,mode", [(8192, 256, 8, "zipf"), (1, 1, 1, "one"), (100, 64, 6, "all_one_expert"),
-                                        (3000, 1024, 4, "uniform"), (513, 7, 7, "uniform")])
+                                        (3000, 1024, 4, "uniform"), (513, 7, 7, "uniform"),
+                                        # the largest accepted shapes: E = 1024 with k = 32, and
+                                        # max_tokens * k = 2^24 pairs through the one-block sort
+                                        (32768, 1024, 32, "uniform"), (524288, 256, 32, "zipf")])
 def test_permute_parity(T, E, k, mode):
     rng = np.random.default_rng(T + E)
     if mode == "all_one_expert":
