@@ -193,7 +193,7 @@ def cpu_baseline(w, device, ids, max_seconds=25.0):
     for e in sorted(experts):
         a, b = mi.device_master_weights(w, e, device)
         w13[e], w2[e] = a.cpu().numpy(), b.cpu().numpy()
-    Wo = omoe.quantize_weights(w13, w2, w.dtype, w.act)  # weight quantisation: not timed
+    Wo = omoe.quantize_weights(w13, w2, w.dtype, w.act, w.fold)  # weight quantisation: not timed
     del w13, w2
     threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     # repeat a short sample until about 10 s of CPU work have been timed
@@ -416,7 +416,8 @@ def main():
         "dtype": ARITH_DTYPE[w.dtype],
         "data": "synthetic (seeded N(0,1) x and logits, N(0,0.02) weights; random init)",
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.k,
-                   "weights": w.dtype, "activation": w.act, "routing_skew": w.bias, "active_experts": n_active},
+                   "weights": w.dtype, "activation": w.act, "weight_alpha_folded": w.fold, "routing_skew": w.bias,
+                   "active_experts": n_active},
         "roofline": roof,
         "layer": {"algorithmic_bytes": B, "flops": F, "gpu_ms_per_step": gpu_ms_step, "hbm_gbs": layer_gbs,
                   "hbm_frac": layer_gbs / HBM_PEAK_GBS, "mfma_tflops": tflops,

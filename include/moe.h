@@ -143,6 +143,22 @@ MOE_API moe_status moe_quantize_weights(int32_t dtype, int32_t count, int32_t ro
                                 const float* w, void* codes, void* scales, float* alpha,
                                 hipStream_t stream);
 
+/* Fold the NVFP4 per-tensor weight alpha into the block scales, as the pages'
+ * weight preprocessing does [vLLM PR 40082 report, "Key source excerpts",
+ * process_weights_after_loading: the weight global scale is baked into the
+ * block scales and the weight alpha becomes 1]: for `count` matrices of
+ * `rows` x `K` NVFP4 weights,
+ *   scales_out[e, r, b] = e4m3_rne_satfinite( fp32(e4m3(scales_in[e, r, b]) * alpha_in[e]) ),
+ *   alpha_out[e] = 1.
+ * The codes are unchanged.  Every block scale is re-rounded in e4m3, and
+ * products below 2^-6 land in e4m3's subnormal range (quantum 2^-9), so
+ * the folded weights are a coarser quantisation of the same masters; the
+ * layer then runs with alpha = 1.  Buffers: scales u8 [count, rows, K/16],
+ * alpha f32 [count]; out may equal in (in place).  K % 16 == 0. */
+MOE_API moe_status moe_nvfp4_fold_global_scale(int32_t count, int32_t rows, int32_t K, const void* scales_in,
+                                               const float* alpha_in, void* scales_out, float* alpha_out,
+                                               hipStream_t stream);
+
 /* Repack canonical weights into the MFMA-ready tile layout in `packed`
  * (moe_packed_weight_bytes bytes): per expert, W13 is cut into groups of 32
  * gate rows + the matching 32 up rows (MOE_RELU2: W1 into groups of 64

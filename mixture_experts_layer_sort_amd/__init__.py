@@ -35,6 +35,7 @@ EXPORTED = [
     "moe_hq_scale_offset",
     "moe_hq_dequant_offset",
     "moe_quantize_weights",
+    "moe_nvfp4_fold_global_scale",
     "moe_prepare_weights",
     "moe_route",
     "moe_permute",
@@ -90,6 +91,7 @@ def _load():
         "moe_xq_dequant_offset": (SZ, [S, I32]),
         "moe_hq_dequant_offset": (SZ, [S, I32]),
         "moe_quantize_weights": (I32, [I32, I32, I32, I32, P, P, P, P, P]),
+        "moe_nvfp4_fold_global_scale": (I32, [I32, I32, I32, P, P, P, P, P]),
         "moe_prepare_weights": (I32, [S, P, P, P, P, P, P, P, SZ, P]),
         "moe_route": (I32, [S, I32, P, P, P, P]),
         "moe_permute": (I32, [S, I32, P, P, P, P, P, P, P, SZ, P]),
@@ -200,6 +202,14 @@ def moe_quantize_weights(dtype, count, rows, K, w, codes, scales=None, alpha=Non
     d = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     _check(_lib.moe_quantize_weights(d, count, rows, K, _ptr(w), _ptr(codes), _ptr(scales), _ptr(alpha),
                                      _stream(stream)), "moe_quantize_weights")
+
+
+def moe_nvfp4_fold_global_scale(count, rows, K, scales_in, alpha_in, scales_out=None, alpha_out=None, stream=None):
+    """NVFP4 weights: fold alpha into the block scales (in place unless outputs are given)."""
+    so = scales_in if scales_out is None else scales_out
+    ao = alpha_in if alpha_out is None else alpha_out
+    _check(_lib.moe_nvfp4_fold_global_scale(count, rows, K, _ptr(scales_in), _ptr(alpha_in), _ptr(so), _ptr(ao),
+                                            _stream(stream)), "moe_nvfp4_fold_global_scale")
 
 
 def moe_prepare_weights(shape, w13_codes, w13_scales, w13_alpha, w2_codes, w2_scales, w2_alpha, packed,

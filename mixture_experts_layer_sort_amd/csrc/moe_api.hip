@@ -142,6 +142,17 @@ size_t moe_hq_scale_offset(const moe_shape* s, int32_t T) {
   return act_scale_offset(s->dtype, T * s->top_k, s->inter);
 }
 
+moe_status moe_nvfp4_fold_global_scale(int32_t count, int32_t rows, int32_t K, const void* scales_in,
+                                       const float* alpha_in, void* scales_out, float* alpha_out, hipStream_t stream) {
+  if (count < 0 || rows < 1 || K < 1) return MOE_ERR_INVALID_ARG;
+  if (K % 16) return MOE_ERR_UNSUPPORTED;
+  if ((long long)count * rows * (K / 16) > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  if (count == 0) return MOE_OK;
+  if (!scales_in || !alpha_in || !scales_out || !alpha_out) return MOE_ERR_INVALID_ARG;
+  return launched(launch_fold_global_scale(count, (long long)rows * (K / 16), (const uint8_t*)scales_in, alpha_in,
+                                           (uint8_t*)scales_out, alpha_out, stream));
+}
+
 moe_status moe_quantize_weights(int32_t dtype, int32_t count, int32_t rows, int32_t K, const float* w, void* codes,
                                 void* scales, float* alpha, hipStream_t stream) {
   if (dtype < MOE_BF16 || dtype > MOE_BF16_MXFP8) return MOE_ERR_UNSUPPORTED;

@@ -19,6 +19,10 @@ hipError_t launch_quantize_weights(int dt, int count, int rows, int K, const flo
                                    float* alpha, hipStream_t s);
 
 // gated: SwiGLU experts (W13 of 2I rows); otherwise ReLU^2 (W1 of I rows)
+// NVFP4: scales_out = e4m3(fp32(e4m3(scales_in) * alpha_in[matrix])), then alpha_out = 1
+hipError_t launch_fold_global_scale(int count, long long scales_per_matrix, const uint8_t* scales_in,
+                                    const float* alpha_in, uint8_t* scales_out, float* alpha_out, hipStream_t s);
+
 hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t* w13, const uint8_t* w13s,
                           const float* w13a, const uint8_t* w2, const uint8_t* w2s, const float* w2a, uint8_t* packed,
                           hipStream_t s);

@@ -126,6 +126,26 @@ __global__ void fill_u32_kernel(unsigned int* __restrict__ p, long long n, unsig
     p[i] = v;
 }
 
+// NVFP4 global-scale fold: one e4m3 block scale per thread (grid-stride).
+__global__ void fold_scale_kernel(const uint8_t* __restrict__ in, const float* __restrict__ alpha, long long n,
+                                  long long per_matrix, uint8_t* __restrict__ out) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    out[i] = (uint8_t)e4m3_from_f32(e4m3_to_f32(in[i]) * alpha[i / per_matrix]);
+}
+
+hipError_t launch_fold_global_scale(int count, long long scales_per_matrix, const uint8_t* scales_in,
+                                    const float* alpha_in, uint8_t* scales_out, float* alpha_out, hipStream_t s) {
+  const long long n = (long long)count * scales_per_matrix;
+  const int threads = 256, blocks = (int)min((n + threads - 1) / threads, (long long)65536);
+  hipLaunchKernelGGL(fold_scale_kernel, dim3(blocks), dim3(threads), 0, s, scales_in, alpha_in, n, scales_per_matrix,
+                     scales_out);
+  // a second launch, so that alpha_out may alias alpha_in
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((count + 255) / 256), dim3(256), 0, s,
+                     reinterpret_cast<unsigned int*>(alpha_out), (long long)count, 0x3F800000u);
+  return hipGetLastError();
+}
+
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* wts, hipStream_t s) {

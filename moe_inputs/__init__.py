@@ -53,6 +53,7 @@ class Workload:
     bias: str       # "none" | "normal2" | "zipf1.1"
     cid: int        # seed id of the workload
     act: str = "swiglu"  # "swiglu" (gated, W13 of 2I rows) | "relu2" (non-gated, W1 of I rows)
+    fold: bool = False   # NVFP4: weight alpha folded into the block scales after quantisation
 
     @property
     def R13(self) -> int:
@@ -86,6 +87,8 @@ WORKLOADS = {
         Workload("bf16_mxfp8_prefill", 8192, 7168, 2048, 256, 8, "bf16_mxfp8", "zipf1.1", 5),
         # non-gated squared-ReLU experts (W1 of I rows) at the NVFP4 decode shape
         Workload("relu2_nvfp4_decode_t128", 128, 7168, 2048, 384, 8, "nvfp4", "none", 4, "relu2"),
+        # NVFP4 weights with the per-tensor alpha folded into the block scales (same masters)
+        Workload("nvfp4_folded_decode_t128", 128, 7168, 2048, 384, 8, "nvfp4", "none", 4, "swiglu", True),
     ]
 }
 

@@ -140,13 +140,18 @@ class Weights:
         return w13, w2
 
 
-def quantize_weights(w13_f32: dict, w2_f32: dict, dtype: str, act: str = "swiglu") -> Weights:
-    """Quantise fp32 master weights {e: array} into canonical form (harness)."""
+def quantize_weights(w13_f32: dict, w2_f32: dict, dtype: str, act: str = "swiglu", fold: bool = False) -> Weights:
+    """Quantise fp32 master weights {e: array} into canonical form (harness).
+    fold (NVFP4): then fold each tensor's alpha into its block scales."""
     out = {k: {} for k in ("w13", "w13_s", "w13_a", "w2", "w2_s", "w2_a")}
     wf = weight_format(dtype)
     for e in w13_f32:
         out["w13"][e], out["w13_s"][e], out["w13_a"][e] = quant.quantize_weight(w13_f32[e], wf)
         out["w2"][e], out["w2_s"][e], out["w2_a"][e] = quant.quantize_weight(w2_f32[e], wf)
+    if fold and wf == "nvfp4":
+        for e in w13_f32:
+            out["w13_s"][e], out["w13_a"][e] = quant.nvfp4_fold_global_scale(out["w13_s"][e], out["w13_a"][e])
+            out["w2_s"][e], out["w2_a"][e] = quant.nvfp4_fold_global_scale(out["w2_s"][e], out["w2_a"][e])
     if wf == "bf16":
         for n in ("w13_s", "w13_a", "w2_s", "w2_a"):
             out[n] = None

@@ -139,6 +139,17 @@ def nvfp4_quantize_weight(w32: np.ndarray):
     return codecs.pack_e2m1(codes.reshape(w.shape)), sc_code, alpha
 
 
+def nvfp4_fold_global_scale(scales: np.ndarray, alpha):
+    """Fold an NVFP4 weight tensor's alpha into its block scales, as the pages'
+    weight preprocessing does [vLLM PR 40082 report, "Key source excerpts",
+    process_weights_after_loading: the block scales are multiplied in fp32 by
+    the per-tensor factor and cast back to e4m3; the factor becomes 1].
+
+    Returns (new e4m3 scale codes, fp32 alpha 1.0)."""
+    prod = (codecs.e4m3_decode(scales).astype(np.float32) * np.float32(alpha)).astype(np.float32)
+    return codecs.e4m3_encode(prod), np.float32(1.0)
+
+
 # ------------------------------------------------------------------- BF16
 
 

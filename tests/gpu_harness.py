@@ -76,6 +76,9 @@ def quantize_expert(w: mi.Workload, cw: CanonicalWeights, e: int, w13_f32: torch
     """Quantise expert e's fp32 master weights (device tensors) with the library."""
     lib.moe_quantize_weights(w.dtype, 1, w.R13, w.H, w13_f32, cw.w13[e:e + 1], _sub(cw.w13_s, e), _sub(cw.w13_a, e))
     lib.moe_quantize_weights(w.dtype, 1, w.H, w.I, w2_f32, cw.w2[e:e + 1], _sub(cw.w2_s, e), _sub(cw.w2_a, e))
+    if w.fold:
+        lib.moe_nvfp4_fold_global_scale(1, w.R13, w.H, _sub(cw.w13_s, e), _sub(cw.w13_a, e))
+        lib.moe_nvfp4_fold_global_scale(1, w.H, w.I, _sub(cw.w2_s, e), _sub(cw.w2_a, e))
 
 
 def canonical_from_host_master(w: mi.Workload):
@@ -87,6 +90,9 @@ def canonical_from_host_master(w: mi.Workload):
     t2 = torch.from_numpy(w2f).to(dev())
     lib.moe_quantize_weights(w.dtype, w.E, w.R13, w.H, t13, cw.w13, cw.w13_s, cw.w13_a)
     lib.moe_quantize_weights(w.dtype, w.E, w.H, w.I, t2, cw.w2, cw.w2_s, cw.w2_a)
+    if w.fold:  # NVFP4: alpha folded into the block scales, in place
+        lib.moe_nvfp4_fold_global_scale(w.E, w.R13, w.H, cw.w13_s, cw.w13_a)
+        lib.moe_nvfp4_fold_global_scale(w.E, w.H, w.I, cw.w2_s, cw.w2_a)
     return cw, w13f, w2f
 
 

@@ -123,6 +123,11 @@ def test_invalid_arguments_rejected_on_host():
     assert st.moe_prepare_weights(ctypes.byref(s4), P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), P(FAKE), P(FAKE),
                                   1 << 40, None) == INVALID
     assert st.moe_quantize_weights(1, 1, 4, 48, P(FAKE), P(FAKE), P(FAKE), None, None) == UNSUPPORTED  # K % 32
+    # NVFP4 global-scale fold
+    assert st.moe_nvfp4_fold_global_scale(2, 4, 40, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == UNSUPPORTED  # K % 16
+    assert st.moe_nvfp4_fold_global_scale(2, 4, 64, P(FAKE), None, P(FAKE), P(FAKE), None) == INVALID
+    assert st.moe_nvfp4_fold_global_scale(-1, 4, 64, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == INVALID
+    assert st.moe_nvfp4_fold_global_scale(0, 4, 64, None, None, None, None, None) == OK  # nothing to do
     assert st.moe_quantize_weights(2, 1, 4, 64, P(FAKE), P(FAKE), P(FAKE), None, None) == INVALID  # no alpha
     assert st.moe_quantize_weights(7, 1, 4, 64, P(FAKE), P(FAKE), P(FAKE), None, None) == UNSUPPORTED
     # T == 0 is a no-op that succeeds without touching anything

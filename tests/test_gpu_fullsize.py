@@ -42,8 +42,14 @@ def pool():
 
 
 def _quantize_pair(args):
-    w13, w2, dtype = args
-    return oquant.quantize_weight(w13, gh.weight_format(dtype)), oquant.quantize_weight(w2, gh.weight_format(dtype))
+    w13, w2, dtype, fold = args
+    out = []
+    for m in (w13, w2):
+        c, s, a = oquant.quantize_weight(m, gh.weight_format(dtype))
+        if fold:
+            s, a = oquant.nvfp4_fold_global_scale(s, a)
+        out.append((c, s, a))
+    return tuple(out)
 
 
 def _pick_tokens(ids, k, limit):
@@ -63,6 +69,7 @@ def _pick_tokens(ids, k, limit):
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "bf16_decode", "mxfp8_decode", "nvfp4_decode_t8",
                                   "nvfp4_decode_t128", "bf16_mxfp8_decode", "relu2_nvfp4_decode_t128",
+                                  "nvfp4_folded_decode_t128",
                                   "mxfp8_prefill"])
 def test_fullsize_parity(name, pool):
     w = W[name]
@@ -112,7 +119,7 @@ def test_fullsize_parity(name, pool):
     for e in experts:
         a, b = mi.device_master_weights(w, e, dev)
         masters[e] = (a.cpu().numpy(), b.cpu().numpy())
-    results = list(pool.map(_quantize_pair, [(masters[e][0], masters[e][1], w.dtype) for e in experts]))
+    results = list(pool.map(_quantize_pair, [(masters[e][0], masters[e][1], w.dtype, w.fold) for e in experts]))
     del masters
     got = gh.canonical_to_numpy(cw, experts)
     ow = {n: {} for n in ("w13", "w13_s", "w13_a", "w2", "w2_s", "w2_a")}

@@ -44,6 +44,9 @@ SMALL = {
     "relu2_mxfp8_prefill_skewed": W["mxfp8_prefill"].scaled(T=520, H=256, I=384, E=8, k=2, act="relu2"),
     "relu2_nvfp4_prefill_tiles": W["nvfp4_decode_t128"].scaled(T=200, H=384, I=256, E=4, k=2, act="relu2"),
     "relu2_bf16_mxfp8_prefill": W["bf16_mxfp8_prefill"].scaled(T=300, H=256, I=256, E=4, k=2, act="relu2"),
+    # NVFP4 with the weight alpha folded into the block scales
+    "nvfp4_folded_decode_small": W["nvfp4_decode_t8"].scaled(T=13, H=512, I=256, E=48, fold=True),
+    "nvfp4_folded_prefill_tiles": W["nvfp4_decode_t128"].scaled(T=200, H=384, I=128, E=4, k=2, fold=True),
     # the largest expert count and top-k the library accepts
     "max_experts_topk32": W["tiny_bf16"].scaled(E=1024, k=32, T=40, H=128, I=128),
     "max_experts_topk32_nvfp4": W["nvfp4_decode_t8"].scaled(E=1024, k=32, T=24, H=128, I=128),
@@ -52,7 +55,8 @@ SMALL = {
 
 def _setup(w):
     cw, w13f, w2f = gh.canonical_from_host_master(w)
-    Wo = omoe.quantize_weights({e: w13f[e] for e in range(w.E)}, {e: w2f[e] for e in range(w.E)}, w.dtype, w.act)
+    Wo = omoe.quantize_weights({e: w13f[e] for e in range(w.E)}, {e: w2f[e] for e in range(w.E)}, w.dtype, w.act,
+                               w.fold)
     return cw, Wo
 
 
@@ -255,6 +259,31 @@ def test_graph_capture_replays_match_eager(name):
                 assert np.array_equal(eager, refs[i])
         del g
     assert not layer.sync_words().any()
+
+
+def test_nvfp4_fold_global_scale_bit_exact():
+    """The library's fold of every e4m3 scale code under several alphas (the
+    weight quantiser's magnitude, powers of two, > 1) equals the oracle's,
+    out of place and in place; alpha becomes 1."""
+    rng = np.random.default_rng(17)
+    alphas = np.array([3.7e-5, 1.2e-4, 2.0 ** -10, 0.5, 1.0, 3.1], np.float32)
+    count, rows, K = len(alphas), 8, 256
+    scales = rng.integers(0, 0x7F, (count, rows, K // 16)).astype(np.uint8)
+    scales[0, 0, :] = np.arange(16, dtype=np.uint8) * 7  # spread over the code range
+    ref = np.stack([oquant.nvfp4_fold_global_scale(scales[e], alphas[e])[0] for e in range(count)])
+    d = gh.dev()
+    s_in = torch.from_numpy(scales).to(d)
+    a_in = torch.from_numpy(alphas).to(d)
+    s_out = torch.empty_like(s_in)
+    a_out = torch.empty_like(a_in)
+    lib.moe_nvfp4_fold_global_scale(count, rows, K, s_in, a_in, s_out, a_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(s_out.cpu().numpy(), ref)
+    assert np.array_equal(a_out.cpu().numpy(), np.ones(count, np.float32))
+    assert np.array_equal(s_in.cpu().numpy(), scales)  # input untouched
+    lib.moe_nvfp4_fold_global_scale(count, rows, K, s_in, a_in)  # in place
+    torch.cuda.synchronize()
+    assert np.array_equal(s_in.cpu().numpy(), ref) and np.all(a_in.cpu().numpy() == 1.0)
 
 
 def test_zero_tokens_is_a_noop():

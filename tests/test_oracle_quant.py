@@ -207,3 +207,63 @@ def test_bf16_weight_is_nearest():
     b, _, _ = quant.quantize_weight(w, "bf16")
     wh = quant.bf16_dequantize(b)
     assert np.all(np.abs(wh - w) <= 2.0**-8 * np.abs(w))  # half ulp, 8 significant bits
+
+
+# ------------------------------------------------------------------ NVFP4 global-scale fold
+
+
+def _nearest_e4m3_positive(v):
+    """Brute force: the positive e4m3 code nearest to each v >= 0 (ties to the
+    even code; values past 448 saturate to 448), by exhaustive distance."""
+    codes = np.arange(0x7F, dtype=np.uint8)  # 0x00 .. 0x7E, all finite non-negative codes
+    vals = codecs.e4m3_decode(codes)
+    d = np.abs(np.asarray(v, np.float64)[:, None] - vals[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = np.where(d == best, codes[None, :].astype(np.int64), 1 << 20)
+    even = np.where(cand % 2 == 0, cand, 1 << 20).min(axis=1)
+    return np.where(even < (1 << 20), even, cand.min(axis=1)).astype(np.uint8)
+
+
+def test_nvfp4_fold_alpha_one_is_identity():
+    codes = np.arange(0x7F, dtype=np.uint8)
+    out, a = quant.nvfp4_fold_global_scale(codes, 1.0)
+    assert np.array_equal(out, codes) and a == np.float32(1.0)
+
+
+@pytest.mark.parametrize("k", [1, 3, 6])
+def test_nvfp4_fold_power_of_two_alpha_shifts_exponents(k):
+    """alpha = 2^-k multiplies exactly: every scale whose product stays in
+    e4m3's normal range (>= 2^-6) keeps its mantissa."""
+    codes = np.arange(0x7F, dtype=np.uint8)
+    out, _ = quant.nvfp4_fold_global_scale(codes, 2.0 ** -k)
+    v = codecs.e4m3_decode(codes) * 2.0 ** -k
+    normal = v >= 2.0 ** -6
+    assert np.array_equal(codecs.e4m3_decode(out)[normal], v[normal])
+
+
+def test_nvfp4_fold_is_nearest_e4m3_of_the_fp32_product():
+    """Brute force over every scale code and alphas of the weight quantiser's
+    magnitude (amax / 2688 for N(0, 0.02) weights) and beyond."""
+    rng = np.random.default_rng(11)
+    codes = np.arange(0x7F, dtype=np.uint8)
+    for alpha in list(np.float32(rng.uniform(1e-5, 1e-4, 6))) + [np.float32(0.37), np.float32(3.1)]:
+        out, _ = quant.nvfp4_fold_global_scale(codes, alpha)
+        prod = (codecs.e4m3_decode(codes).astype(np.float32) * np.float32(alpha)).astype(np.float64)
+        assert np.array_equal(out, _nearest_e4m3_positive(prod)), alpha
+
+
+def test_nvfp4_fold_of_weights_reaches_the_subnormal_range():
+    """The pages' fold on N(0, 0.02) weights: alpha ~ 4e-5 puts the folded
+    scales (~1e-2) into e4m3's subnormal range, so the folded weights differ
+    from the unfolded ones by more than the unfolded quantisation error."""
+    rng = np.random.default_rng(4)
+    w = (rng.standard_normal((64, 512)) * 0.02).astype(np.float32)
+    c, s, a = quant.nvfp4_quantize_weight(w)
+    fs, fa = quant.nvfp4_fold_global_scale(s, a)
+    assert fa == np.float32(1.0)
+    assert np.mean(codecs.e4m3_decode(fs) < 2.0 ** -6) > 0.5
+    ref = quant.nvfp4_dequantize(c, s, a)
+    got = quant.nvfp4_dequantize(c, fs, fa)
+    err_fold = np.linalg.norm(got - w) / np.linalg.norm(w)
+    err_ref = np.linalg.norm(ref - w) / np.linalg.norm(w)
+    assert err_fold > err_ref
