@@ -28,8 +28,17 @@ namespace moe {
 // older waves win the issue arbitration.  Each block therefore rotates its
 // waves' priority by item, starting from its slot, so the blocks of one unit
 // take turns at the top priority (3-4 % faster MXFP8 / NVFP4 decode GEMMs).
+// Waves per SIMD the register allocation must allow.  Four resident blocks
+// per compute unit keep more weight bytes in flight for NVFP4 (its steps are
+// the smallest): measured 2-3 % faster gate/up GEMMs than the three the
+// compiler picks by itself; the other formats keep the compiler's choice
+// (MXFP8 would spill at four).
+template <int DT, int NT>
+constexpr int gemm_min_waves_per_simd() { return DT == DT_NVFP4 && NT == 1 ? 4 : 1; }
+
 template <int DT, int NT, bool G13>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(gemm_min_waves_per_simd<DT, NT>())))
+void gemm_kernel(GemmArgs a) {
   __shared__ int cum[1025];
   __shared__ int wsum[4];
   __shared__ f32x4_t red[3][4 * NT][64];
