@@ -116,8 +116,8 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   const int per2 = V == 2 ? (a.g2.G + kPfGroups - 1) / kPfGroups : a.g2.G;
   auto item = [&](const GemmArgs& g, bool g13, long long w) __attribute__((always_inline)) -> int {
     if constexpr (V == 2) {
-      const auto st = pf_make_stages<DT>();
-      return g13 ? prefill_item<DT, true, 1>(g, w, cum, st) : prefill_item<DT, false, 1>(g, w, cum, st);
+      const auto st = pf_make_stages<DT, kPfRows>();
+      return g13 ? prefill_item<DT, true, 1, kPfRows>(g, w, cum, st) : prefill_item<DT, false, 1, kPfRows>(g, w, cum, st);
     } else {
       auto* red = reinterpret_cast<f32x4_t(*)[4 * NT][64]>(smem);
       return g13 ? gemm_item<DT, NT, true>(g, w, cum, red) : gemm_item<DT, NT, false>(g, w, cum, red);

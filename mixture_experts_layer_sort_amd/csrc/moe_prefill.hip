@@ -11,14 +11,23 @@ namespace moe {
 
 constexpr int kPfThreads = 2 * kGemmThreads;  // 8 waves: 4 row groups x 2 token halves
 
+// Routed rows per item: 256 for the down GEMM of LDS-staged (MXFP8) weights
+// (measured 7 % faster than 128: half the weight loads per flop), else 128
+// (the gate/up epilogue and register-staged weights leave no registers for
+// a 64 x 128 wave tile; at 256 rows the MXFP8 gate/up GEMM spills and runs
+// 4 % slower).
+template <int DT, bool G13>
+constexpr int pf_stage_rows() { return pf_alds<DT>() && !G13 ? kPfRowsStage : kPfRows; }
+
 template <int DT, bool G13>
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmArgs a) {
+  constexpr int ROWS = pf_stage_rows<DT, G13>();
   __shared__ int cum[1025];
   __shared__ int wsum[4];
-  const auto st = pf_make_stages<DT>();
-  const int total_mt = build_schedule(a.offsets, a.E, kPfRows, cum, wsum);
+  const auto st = pf_make_stages<DT, ROWS>();
+  const int total_mt = build_schedule(a.offsets, a.E, ROWS, cum, wsum);
   const long long total = (long long)total_mt * ((a.G + kPfGroups - 1) / kPfGroups);
-  for (long long w = xcd_logical_block(); w < total; w += gridDim.x) prefill_item<DT, G13, 2>(a, w, cum, st);
+  for (long long w = xcd_logical_block(); w < total; w += gridDim.x) prefill_item<DT, G13, 2, ROWS>(a, w, cum, st);
 }
 
 template <int DT, bool G13>

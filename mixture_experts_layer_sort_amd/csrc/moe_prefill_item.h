@@ -30,10 +30,15 @@
 
 namespace moe {
 
-constexpr int kPfRows = 128;                  // routed rows per item: 4 sub-tiles of 32
+constexpr int kPfRows = 128;                  // routed rows per item of the single-launch kernel: 4 sub-tiles of 32
+constexpr int kPfRowsStage = 256;             // routed rows per item of the stage kernel: 8 sub-tiles of 32
 constexpr int kPfGroups = 4;                  // weight row groups per item, one per wave
-constexpr int kPfBand = 8;                    // m-tiles per band of the item order
-constexpr int kPfTokSlots = 8 * 2 * 64;       // token part of a stage: 8 blocks of 32 rows x 32 K, 16-byte slots (16 KB)
+// m-tiles per band of the item order (a band's token rows: 1024)
+template <int ROWS>
+constexpr int pf_band() { return 1024 / ROWS; }
+// token part of a stage: ROWS / 32 sub-tiles x 2 chunks of 32 K, 32 rows x 64 B each, in 16-byte slots
+template <int ROWS>
+constexpr int pf_tok_slots() { return ROWS / 32 * 2 * 128; }
 #ifndef MOE_PF_STAGES_Q
 #define MOE_PF_STAGES_Q 4  // pipeline depth for MXFP8 / NVFP4 weights
 #endif
@@ -41,8 +46,8 @@ constexpr int kPfMaxStages = 8;
 // pipeline depth (K steps in flight + the one computed); 16-bit weights need
 // twice the registers per step (the depth barely matters once loads are
 // interleaved with the MFMAs: measured flat from 3 to 8 for MXFP8)
-template <int DT>
-constexpr int pf_stages() { return DT == DT_BF16 ? 3 : MOE_PF_STAGES_Q; }
+template <int DT, int ROWS>
+constexpr int pf_stages() { return DT == DT_BF16 || (DT == DT_MXFP8 && ROWS > 128) ? 3 : MOE_PF_STAGES_Q; }
 
 // Weights of MXFP8 items also go through LDS (direct loads in fragment
 // order, shared by the two waves of a row group): the per-instruction cost of
@@ -51,8 +56,8 @@ template <int DT>
 constexpr bool pf_alds() { return DT == DT_MXFP8; }
 // 16-byte slots of one stage: tokens, then for LDS weights the codes
 // [group 4][f 2][m 2][64 lanes] (16 KB) and per-wave scale copies [wave 8][64 words]
-template <int DT>
-constexpr int pf_stage_slots() { return pf_alds<DT>() ? kPfTokSlots + 1024 + 128 : kPfTokSlots; }
+template <int DT, int ROWS>
+constexpr int pf_stage_slots() { return pf_alds<DT>() ? pf_tok_slots<ROWS>() + 1024 + 128 : pf_tok_slots<ROWS>(); }
 // weight loads per wave per K step (register path)
 template <int DT>
 constexpr int pf_a_ops() { return DT == DT_BF16 ? 8 : 6; }
@@ -126,9 +131,9 @@ __device__ __forceinline__ u32x4_t (*pf_stage())[SLOTS] {
   __shared__ u32x4_t buf[SLOTS];
   return &buf;
 }
-template <int DT>
-__device__ __forceinline__ PfStages<pf_stage_slots<DT>()> pf_make_stages() {
-  constexpr int NS = pf_stages<DT>(), SL = pf_stage_slots<DT>();
+template <int DT, int ROWS>
+__device__ __forceinline__ PfStages<pf_stage_slots<DT, ROWS>()> pf_make_stages() {
+  constexpr int NS = pf_stages<DT, ROWS>(), SL = pf_stage_slots<DT, ROWS>();
   static_assert(NS >= 3 && NS <= kPfMaxStages, "stages");
   PfStages<SL> st{};
   st.s[0] = pf_stage<0, SL>();
@@ -151,18 +156,18 @@ __device__ __forceinline__ int pf_swz(int r) { return (r >> 2) & 3; }
 
 // Epilogue of a 64 x 32 NSA wave tile in the 32x32 accumulator layout: lane l,
 // element e of acc[f][S] is weight row 32f + (e & 3) + 8 (e >> 2) + 4 (l >> 5)
-// of row group g, routed row r0 + 32 S + (l & 31).  Gate/up GEMM: SwiGLU of
+// of row group g, routed row r0 + SSTR S + (l & 31).  Gate/up GEMM: SwiGLU of
 // the f = 0 (gate) and f = 1 (up) values (ReLU^2 experts: relu(v)^2 of both
 // fragments, 64 intermediates), requantised per token row; down GEMM: bf16 y
 // rows of the pair.
-template <int DT, bool G13, int NSA, int SW>
+template <int DT, bool G13, int NSA, int SW, int SSTR>
 __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2][SW], int r0, int r_end, int g, int e,
                                             int lane) {
   const int hl = lane >> 5, l32 = lane & 31;
   const float alpha = DT == DT_NVFP4 ? a.walpha[e] : 1.f;
 #pragma unroll
   for (int S = 0; S < NSA; ++S) {
-    const int r = r0 + 32 * S + l32;
+    const int r = r0 + SSTR * S + l32;
     const bool ok = r < r_end;
     if constexpr (G13) {
       const int I = a.n_out;
@@ -275,28 +280,34 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
 }
 
 // One prefill work item.  `w` numbers items expert-major; within an expert,
-// bands of up to kPfBand m-tiles, n-block-major inside a band, so kPfBand^2
-// consecutive items form a square of weight x token tiles.  `cum` holds the
-// per-expert 128-row m-tile prefix from build_schedule.  Returns the item's
+// bands of up to pf_band m-tiles, n-block-major inside a band, so that
+// consecutive items share weight and token tiles.  `cum` holds the
+// per-expert ROWS-row m-tile prefix from build_schedule.  Returns the item's
 // expert; ends with every load landed and the block's LDS free for reuse.
 //
 // TW (1 or 2) is the number of waves along the token dimension: the block
-// has 4 TW waves; wave wv owns row group wv % 4 and token sub-tiles
-// (wv / 4) * 4/TW .. + 4/TW.  With TW = 2 a wave's tile is 64 x 64 (64
-// accumulator registers), so two waves fit per SIMD and one wave's LDS
-// reads, loads and converts overlap the other's MFMAs.
-template <int DT, bool G13, int TW>
+// has 4 TW waves; wave wv owns row group wv % 4 and every TW-th of the
+// item's ROWS / 32 token sub-tiles, starting at wv / 4 (interleaved, so a
+// partly filled m-tile still splits its rows evenly).  With TW = 2 and 256
+// rows a wave's tile is 64 x 128 (128 accumulator registers) and two waves
+// fit per SIMD, so one wave's LDS reads, loads and converts overlap the
+// other's MFMAs; the 256-row tile halves the weight bytes loaded per flop.
+template <int DT, bool G13, int TW, int ROWS>
 __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, const int* cum,
-                                            const PfStages<pf_stage_slots<DT>()>& st) {
+                                            const PfStages<pf_stage_slots<DT, ROWS>()>& st) {
   static_assert(TW == 1 || TW == 2, "waves along tokens");
+  static_assert(ROWS == 128 || ROWS == 256, "rows per item");
   constexpr bool kALds = pf_alds<DT>();
-  constexpr int kSlots = pf_stage_slots<DT>();
-  constexpr int kSW = 4 / TW;                       // token sub-tiles per wave
-  constexpr int kDma = 4 / TW;                      // token loads per wave per K step (16 per block)
+  constexpr int kSlots = pf_stage_slots<DT, ROWS>();
+  constexpr int kTokSlots = pf_tok_slots<ROWS>();
+  constexpr int kSub = ROWS / 32;                   // token sub-tiles per item
+  constexpr int kSW = kSub / TW;                    // token sub-tiles per wave
+  constexpr int kDma = kSub / TW;                   // token loads per wave per K step (4 kSub per block)
   constexpr int kADma = 4 / TW;                     // LDS weights: code loads per wave per K step (16 per block)
+  constexpr int kBand = pf_band<ROWS>();
   // vector-memory operations per wave per K step
   constexpr int kOps = kDma + (kALds ? kADma + 1 : pf_a_ops<DT>());
-  constexpr int kPfStages = pf_stages<DT>();
+  constexpr int kPfStages = pf_stages<DT, ROWS>();
   const int tid = threadIdx.x, lane = tid & 63, i16 = lane & 15, hl = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wg = wv & 3, th = wv >> 2;
   const int NB = (a.G + kPfGroups - 1) / kPfGroups;
@@ -304,17 +315,17 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
   const int e = find_expert(cum, a.E, (int)(w / NB));
   const int mts = cum[e + 1] - cum[e];
   const long long local = w - (long long)cum[e] * NB;
-  const int band = (int)(local / (kPfBand * NB)), full = mts / kPfBand;
-  const int bsize = band < full ? kPfBand : mts - full * kPfBand;
-  const int inner = (int)(local - (long long)band * kPfBand * NB);
-  const int nb = inner / bsize, mt = band * kPfBand + inner % bsize;
-  const int r0 = a.offsets[e] + mt * kPfRows, r_end = a.offsets[e + 1];
+  const int band = (int)(local / (kBand * NB)), full = mts / kBand;
+  const int bsize = band < full ? kBand : mts - full * kBand;
+  const int inner = (int)(local - (long long)band * kBand * NB);
+  const int nb = inner / bsize, mt = band * kBand + inner % bsize;
+  const int r0 = a.offsets[e] + mt * ROWS, r_end = a.offsets[e + 1];
   // this wave's row group; a group past the end (G not a multiple of 4) reads group G-1 and discards it
   const int g = kPfGroups * nb + wg, gl = min(g, a.G - 1);
 
-  // Token loads: the block's 16 per K step are (sub-tile d / 4, chunk
-  // (d / 2) % 2, row half d % 2), d = 0..15; this wave issues d = wv kDma ..
-  // + kDma, all in sub-tile dS.  Load lane: row 16 half + lane / 4, the
+  // Token loads: the block's 4 kSub per K step are (sub-tile d / 4, chunk
+  // (d / 2) % 2, row half d % 2), d = 0..4 kSub - 1; this wave issues d =
+  // wv kDma .. + kDma, all in sub-tile dS.  Load lane: row 16 half + lane / 4, the
   // row's 16-byte piece (lane % 4) ^ swizzle.  Rows past the expert's end
   // load its last row, whose results are discarded.
   const int dS = (wv * kDma) >> 2;
@@ -356,11 +367,11 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
         // codes of fragment pair (f, m) of this row group, in fragment-lane order
         const int f = TW == 2 ? th : (idx >> 1), m = TW == 2 ? idx : (idx & 1);
         __builtin_amdgcn_global_load_lds(wc + (tk + 2 * f) * tcode + h * 1024 + m * 512,
-                                         &stage[kPfTokSlots + ((wg * 2 + f) * 2 + m) * 64], 16, 0, 0);
+                                         &stage[kTokSlots + ((wg * 2 + f) * 2 + m) * 64], 16, 0, 0);
       } else {
         // this wave's copy of the group's 4 tile scale blocks (256 contiguous bytes)
         __builtin_amdgcn_global_load_lds(a.wscales + (tile0 + tk) * tscale + lane * 4,
-                                         &stage[kPfTokSlots + 1024 + wv * 16], 4, 0, 0);
+                                         &stage[kTokSlots + 1024 + wv * 16], 4, 0, 0);
       }
       return;
     }
@@ -414,7 +425,7 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
     // token fragments of the active sub-tiles, K slice (chunk cc, m)
     auto read_b = [&](u32x4_t(&bf)[kSW], const u32x4_t(&stage)[kSlots], int cc, int m) {
 #pragma unroll
-      for (int S = 0; S < NSA; ++S) bf[S] = stage[(2 * (th * kSW + S) + cc) * 128 + boff[m]];
+      for (int S = 0; S < NSA; ++S) bf[S] = stage[(2 * (TW * S + th) + cc) * 128 + boff[m]];
     };
 
     // Operands of slice 0 of a step, read ahead across the step boundary:
@@ -428,8 +439,8 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
 #pragma unroll
-          for (int m = 0; m < 2; ++m) cr.AL.c[f][m] = stage[kPfTokSlots + ((wg * 2 + f) * 2 + m) * 64 + lane];
-          cr.AL.s[f] = reinterpret_cast<const uint32_t*>(&stage[kPfTokSlots + 1024 + wv * 16])[(2 * f + ltile) * 16 + i16];
+          for (int m = 0; m < 2; ++m) cr.AL.c[f][m] = stage[kTokSlots + ((wg * 2 + f) * 2 + m) * 64 + lane];
+          cr.AL.s[f] = reinterpret_cast<const uint32_t*>(&stage[kTokSlots + 1024 + wv * 16])[(2 * f + ltile) * 16 + i16];
         }
       }
       read_b(cr.bf0, stage, 0, 0);
@@ -534,10 +545,11 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
     }
     pf_wait_barrier<0>();
     if constexpr (NSA > 0)
-      if (g < a.G) pf_epilogue<DT, G13, NSA, kSW>(a, acc, r0 + 32 * th * kSW, r_end, g, e, lane);
+      if (g < a.G) pf_epilogue<DT, G13, NSA, kSW, 32 * TW>(a, acc, r0 + 32 * th, r_end, g, e, lane);
   };
-  // this wave's active 32-row sub-tiles (uniform across the wave)
-  const int nsa = min(kSW, max(0, ((r_end - r0 + 31) >> 5) - th * kSW));
+  // this wave's active 32-row sub-tiles th, th + TW, ... (uniform across the wave)
+  const int nact = min(kSub, (r_end - r0 + 31) >> 5);
+  const int nsa = min(kSW, max(0, (nact - th + TW - 1) / TW));
   if constexpr (TW == 1) {
     switch (nsa) {
       case 1: run(std::integral_constant<int, 1>{}); break;
@@ -545,11 +557,19 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
       case 3: run(std::integral_constant<int, 3>{}); break;
       default: run(std::integral_constant<int, 4>{}); break;
     }
-  } else {
+  } else if constexpr (kSW == 2) {
     switch (nsa) {
       case 0: run(std::integral_constant<int, 0>{}); break;
       case 1: run(std::integral_constant<int, 1>{}); break;
       default: run(std::integral_constant<int, 2>{}); break;
+    }
+  } else {
+    switch (nsa) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      default: run(std::integral_constant<int, 4>{}); break;
     }
   }
   // Drain the epilogue's stores: with stores and loads both pending, the
