@@ -88,7 +88,7 @@ constexpr size_t fused_lds_bytes() {
 template <int DT, int V>
 __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   constexpr int NT = V == 2 ? 1 : V + 1;  // decode items: token sub-tiles of 16
-  constexpr int MT = V == 2 ? kPfRows : 16 * NT;
+  constexpr int MT = V == 2 ? kPfRows : kDecodeMT;
   __shared__ int cum[1025];
   __shared__ int wsum[4];
   __shared__ __align__(16) unsigned char smem[fused_lds_bytes<V>()];

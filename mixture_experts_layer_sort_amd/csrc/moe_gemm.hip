@@ -2,7 +2,7 @@
 // repacking and the top-k combine, for gfx950.
 //
 // GEMM work decomposition.  The pairs routed to expert e occupy sorted rows
-// [offsets[e], offsets[e+1]); they are cut into m-tiles of MT = 16*NT rows.
+// [offsets[e], offsets[e+1]); they are cut into m-tiles of kDecodeMT = 32 rows.
 // One work item = (expert, m-tile, weight row group of 64 rows); items are
 // numbered m-tile-major so neighbouring blocks share activation rows.  The
 // grid is persistent (sized to the resident capacity) and each block walks
@@ -11,7 +11,8 @@
 // no host synchronisation or extra launch is needed.  Inside a block the 4
 // waves split K into quarters, each streaming its slice of the 4 weight
 // tiles (16 rows each) through registers into MFMAs with the weights in the
-// M slot and the (<= 16*NT) routed tokens in the N slot, then reduce through
+// M slot and the (<= 16*NT) routed tokens in the N slot (an item of 17-32
+// rows with NT = 1 runs as two halves of two waves each), then reduce through
 // LDS.  This is the decode-shaped ("swap A/B") arrangement: weight rows fill
 // the matrix unit's 16-row side so a handful of tokens per expert wastes no
 // weight bandwidth [MegaMoE drop workflow, §1: the NVFP4 kernel package is
@@ -34,20 +35,87 @@ namespace moe {
 // compiler picks by itself; the other formats keep the compiler's choice
 // (MXFP8 would spill at four).
 template <int DT, int NT>
-constexpr int gemm_min_waves_per_simd() { return DT == DT_NVFP4 && NT == 1 ? 4 : 1; }
+constexpr int gemm_min_waves_per_simd() { return NT == 1 ? (DT == DT_NVFP4 ? 4 : (DT == DT_MXFP8 ? 3 : 2)) : 1; }
+
+// Paired m-tiles of an expert with `rows` routed rows (NT = 1 decode items
+// of 17-32 rows, which take twice as long as the others): its full 32-row
+// m-tiles and a last partial one of more than 16 rows.  Its other m-tile,
+// if any, is the last one, of at most 16 rows.
+__device__ __forceinline__ int paired_mtiles(int rows) { return rows / kDecodeMT + (rows % kDecodeMT > 16 ? 1 : 0); }
+
+// Execution order of the NT = 1 decode items.  Blocks take positions
+// blockIdx.x, + gridDim.x, ... (round-robin, so blocks running together
+// stream neighbouring weight rows).  The N = q*B + r items leave blocks r..B-1
+// one item short; the P paired items go to positions rp .. rp + P - 1, rp =
+// min(r, N - P), i.e. to those blocks first, and the single items fill the
+// other positions in order.  Within each kind the order is m-tile-major.
+// cum / pcum: per-expert prefixes of m-tiles / paired m-tiles.
+// Returns the item; `e` receives its expert.
+__device__ __forceinline__ long long decode_item_at(long long x, long long rp, long long P, const GemmArgs& a,
+                                                     const int* cum, const int* pcum, int& e) {
+  const long long G = a.G;
+  int lo = 0, hi = a.E;
+  if (x >= rp && x < rp + P) {  // the k-th paired m-tile: expert lo with pcum[lo] <= k < pcum[lo + 1]
+    const long long k = (x - rp) / G, g = (x - rp) % G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pcum[mid] <= k) lo = mid;
+      else hi = mid;
+    }
+    e = lo;
+    return ((long long)cum[lo] + (k - pcum[lo])) * G + g;
+  }
+  const long long y = x < rp ? x : x - P;  // the k-th single m-tile, its expert's last
+  const long long k = y / G, g = y % G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cum[mid] - pcum[mid] <= k) lo = mid;
+    else hi = mid;
+  }
+  e = lo;
+  return ((long long)cum[lo + 1] - 1) * G + g;
+}
 
 template <int DT, int NT, bool G13>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(gemm_min_waves_per_simd<DT, NT>())))
 void gemm_kernel(GemmArgs a) {
   __shared__ int cum[1025];
+  __shared__ int pcum[NT == 1 ? 1025 : 1];
   __shared__ int wsum[4];
   __shared__ f32x4_t red[3][4 * NT][64];
-  const int total_mt = build_schedule(a.offsets, a.E, 16 * NT, cum, wsum);
+  // m-tiles (low 16 bits) and, for NT = 1, paired m-tiles (high 16 bits) per
+  // expert in one scan.  NT = 1 runs only for T * k <= 16 E <= 16384 routed
+  // rows, so both totals stay below 2^16; NT = 2 scans m-tiles alone.
+  int total_mt, total_pairs = 0;
+  if constexpr (NT == 1) {
+    const int both = build_prefix<int>(
+        a.offsets, a.E, [](int c) { return (c + kDecodeMT - 1) / kDecodeMT + (paired_mtiles(c) << 16); },
+        [&](int e, int v) {
+          cum[e] = v & 0xFFFF;
+          pcum[e] = v >> 16;
+        },
+        wsum);
+    total_mt = both & 0xFFFF;
+    total_pairs = both >> 16;
+  } else {
+    total_mt = build_schedule(a.offsets, a.E, kDecodeMT, cum, wsum);
+  }
   const long long total = (long long)total_mt * a.G;
   int turn = (int)(blockIdx.x >> 8);
-  for (long long w = blockIdx.x; w < total; w += gridDim.x, ++turn) {
-    set_wave_priority(turn & 3);
-    gemm_item<DT, NT, G13>(a, w, cum, red);
+  if (total_pairs > 0) {
+    const long long P = (long long)total_pairs * a.G;
+    const long long rp = min(total % gridDim.x, total - P);
+    for (long long x = blockIdx.x; x < total; x += gridDim.x, ++turn) {
+      set_wave_priority(turn & 3);
+      int e;
+      const long long w = decode_item_at(x, rp, P, a, cum, pcum, e);
+      gemm_item<DT, NT, G13>(a, w, cum, red, e);
+    }
+  } else {
+    for (long long w = blockIdx.x; w < total; w += gridDim.x, ++turn) {
+      set_wave_priority(turn & 3);
+      gemm_item<DT, NT, G13>(a, w, cum, red);
+    }
   }
 }
 

@@ -33,49 +33,63 @@ __device__ __forceinline__ void set_wave_priority(int p) {
   }
 }
 
-// cum[e] = m-tiles of experts < e (LDS), returns the total.  The first
-// kGemmThreads threads do the scan; a larger block only waits for it.
-// wsum holds kGemmThreads / 64 ints.
-__device__ int build_schedule(const int* __restrict__ offsets, int E, int MT, int* cum, int* wsum) {
+// Exclusive prefix over experts of count(rows of e), a 32-bit value or two
+// packed into 64 bits: out(e, prefix) stores the prefix of expert e, and
+// out(E, total) the total.  The first kGemmThreads threads do the scan (one
+// load of the offsets, one wave scan, two barriers); a larger block only
+// waits for it.  wsum holds kGemmThreads / 64 values.
+template <typename V, typename CountFn, typename OutFn>
+__device__ V build_prefix(const int* __restrict__ offsets, int E, CountFn count, OutFn out, V* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid >= kGemmThreads) {
     __syncthreads();
+    V total = 0;
+    for (int ww = 0; ww < kGemmThreads / 64; ++ww) total += wsum[ww];
     __syncthreads();
-    return cum[E];
+    return total;
   }
   const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 4 (E <= 1024)
   const int e0 = tid * per;
-  int cnt[4] = {0, 0, 0, 0}, local = 0;
+  V cnt[4] = {0, 0, 0, 0}, local = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     int e = e0 + j;
     if (j < per && e < E) {
-      cnt[j] = (offsets[e + 1] - offsets[e] + MT - 1) / MT;
+      cnt[j] = count(offsets[e + 1] - offsets[e]);
       local += cnt[j];
     }
   }
-  int incl = local;
+  V incl = local;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int o = __shfl_up(incl, d, 64);
+    V o = __shfl_up(incl, d, 64);
     if (lane >= d) incl += o;
   }
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  int wbase = 0;
-  for (int ww = 0; ww < w; ++ww) wbase += wsum[ww];
-  int run = wbase + incl - local;
+  V wbase = 0, total = 0;
+  for (int ww = 0; ww < kGemmThreads / 64; ++ww) {
+    if (ww < w) wbase += wsum[ww];
+    total += wsum[ww];
+  }
+  V run = wbase + incl - local;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     int e = e0 + j;
     if (j < per && e < E) {
-      cum[e] = run;
+      out(e, run);
       run += cnt[j];
     }
   }
-  if (tid == kGemmThreads - 1) cum[E] = wbase + incl;
+  if (tid == 0) out(E, total);
   __syncthreads();
-  return cum[E];
+  return total;
+}
+
+// cum[e] = m-tiles of MT rows of experts < e (LDS); returns the total.
+__device__ __forceinline__ int build_schedule(const int* __restrict__ offsets, int E, int MT, int* cum, int* wsum) {
+  return build_prefix<int>(offsets, E, [MT](int c) { return (c + MT - 1) / MT; },
+                           [cum](int e, int v) { cum[e] = v; }, wsum);
 }
 
 __device__ __forceinline__ int find_expert(const int* cum, int E, int mtg) {
@@ -381,31 +395,49 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
   }
 }
 
-// One work item (expert, m-tile, 64-row weight group) of a grouped GEMM:
-// the four waves stream their K slices into MFMAs, reduce through LDS, and
-// wave 0 runs the epilogue (SwiGLU + requantisation for the gate/up GEMM,
-// bf16 y rows for the down GEMM).  `w` numbers items m-tile-major; `cum`
-// holds the per-expert m-tile prefix from build_schedule.  Returns the
-// item's expert.  Ends with the block's LDS free for reuse.
+// Routed rows per decode work item (m-tile), for both token-tile widths.
+constexpr int kDecodeMT = 32;
+
+// One work item (expert, m-tile of kDecodeMT sorted rows, 64-row weight
+// group) of a grouped GEMM: the four waves stream their K slices into MFMAs,
+// reduce through LDS, and run the epilogue (SwiGLU + requantisation for the
+// gate/up GEMM, bf16 y rows for the down GEMM).  `w` numbers items
+// m-tile-major; `cum` holds the per-expert m-tile prefix from
+// build_schedule; `e_known` is the item's expert if the caller has it, else
+// -1.  Returns the item's expert.  Ends with the block's LDS free for reuse.
+//
+// NT = 2: every wave covers the item's 32 rows (two 16-row token
+// sub-tiles) and a quarter of K.  NT = 1: an item of at most 16 rows is
+// split over K four ways as above; an item of 17-32 rows runs as two halves,
+// waves 0-1 on rows r0.. and waves 2-3 on rows r0 + 16.., each pair
+// splitting K two ways.  Both halves then read every weight tile at nearly
+// the same time, so an expert with up to 32 rows fetches its weights from
+// HBM once (two 16-row items had them read twice: measured +10 % HBM bytes
+// on the MXFP8 decode layer, whose skewed routing gives a few experts
+// 17-32 rows).
 template <int DT, int NT, bool G13>
 __device__ __forceinline__ int gemm_item(const GemmArgs& a, long long w, const int* cum,
-                                         f32x4_t (*red)[4 * NT][64]) {
-  constexpr int MT = 16 * NT;
+                                         f32x4_t (*red)[4 * NT][64], int e_known = -1) {
+  static_assert(16 * NT <= kDecodeMT, "token sub-tiles");
   constexpr int U = StepK<DT>::U;
   constexpr bool NTLD = MOE_GEMM_NTLOAD && NT == 1;  // decode: weights are streamed once
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int i16 = lane & 15, q = lane >> 4;
-  // K slices are dealt to the 4 waves in rounds of 4U consecutive kgroups
-  // (wave w takes kgroups 4U*j + U*w .. +U), so a block streams one
-  // contiguous region; steps are double-buffered.
-  const int nrounds = (a.KG + 4 * U - 1) / (4 * U);
   const int mtg = (int)(w / a.G), g = (int)(w % a.G);
-  const int e = find_expert(cum, a.E, mtg);
-  const int r0 = a.offsets[e] + (mtg - cum[e]) * MT, r_end = a.offsets[e + 1];
+  const int e = e_known >= 0 ? e_known : find_expert(cum, a.E, mtg);
+  const int r0 = a.offsets[e] + (mtg - cum[e]) * kDecodeMT, r_end = a.offsets[e + 1];
+  // halves (uniform across the block): nw waves share one set of rows starting at rs
+  const bool pair = NT == 1 && r_end - r0 > 16;
+  const int nw = pair ? 2 : 4, wl = pair ? (wv & 1) : wv;
+  const int rs = pair ? r0 + 16 * (wv >> 1) : r0;
+  // K slices are dealt to the nw waves in rounds of nw*U consecutive kgroups
+  // (wave wl takes kgroups nw*U*j + U*wl .. +U), so the waves stream one
+  // contiguous region; steps are double-buffered.
+  const int nrounds = (a.KG + nw * U - 1) / (nw * U);
   int brow[NT];
 #pragma unroll
   for (int s = 0; s < NT; ++s) {
-    int r = r0 + 16 * s + i16;
+    int r = rs + 16 * s + i16;
     brow[s] = r < r_end ? (G13 ? a.sorted_pairs[r] / a.k : r) : -1;
   }
   f32x4_t acc[4][NT];
@@ -419,14 +451,14 @@ __device__ __forceinline__ int gemm_item(const GemmArgs& a, long long w, const i
   auto load_step = [&](KFrag<DT, NT>(&F)[U], int j) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kg = 4 * U * j + U * wv + u;
+      const int kg = nw * U * j + U * wl + u;
       if (kg < a.KG) load_kfrag<DT, NT, G13, NTLD>(F[u], a, (tbase + kg) * 4, kg, brow, lane, i16, q);
     }
   };
   auto mma_step = [&](const KFrag<DT, NT>(&F)[U], int j) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kg = 4 * U * j + U * wv + u;
+      const int kg = nw * U * j + U * wl + u;
       if (kg < a.KG) mma_kfrag<DT, NT>(acc, F[u], q);
     }
   };
@@ -447,20 +479,35 @@ __device__ __forceinline__ int gemm_item(const GemmArgs& a, long long w, const i
     }
   }
 
-  // reduce the four waves' partial sums into wave 0
-  if (wv > 0) {
+  // reduce the partial sums into the first wave of each set, in wave order
+  if (pair) {
+    if (wl == 1) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < NT; ++s) red[wv >> 1][t * NT + s][lane] = acc[t][s];
+    }
+  } else if (wv > 0) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int s = 0; s < NT; ++s) red[wv - 1][t * NT + s][lane] = acc[t][s];
   }
   __syncthreads();
-  if (wv == 0) {
+  if (wl == 0) {
+    if (pair) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int s = 0; s < NT; ++s) acc[t][s] += red[0][t * NT + s][lane] + red[1][t * NT + s][lane] + red[2][t * NT + s][lane];
-    gemm_epilogue<DT, NT, G13>(a, acc, r0, r_end, g, e, lane);
+        for (int s = 0; s < NT; ++s) acc[t][s] += red[wv >> 1][t * NT + s][lane];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < NT; ++s)
+          acc[t][s] += red[0][t * NT + s][lane] + red[1][t * NT + s][lane] + red[2][t * NT + s][lane];
+    }
+    gemm_epilogue<DT, NT, G13>(a, acc, rs, r_end, g, e, lane);
   }
   __syncthreads();
   return e;
