@@ -90,6 +90,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   constexpr int NT = V == 2 ? 1 : V + 1;  // decode items: token sub-tiles of 16
   constexpr int MT = V == 2 ? kPfRows : kDecodeMT;
   __shared__ int cum[1025];
+  __shared__ int pcum[V == 0 ? 1025 : 1];
   __shared__ int wsum[4];
   __shared__ __align__(16) unsigned char smem[fused_lds_bytes<V>()];
   const unsigned G = gridDim.x;
@@ -114,31 +115,42 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   // items per m-tile: one per 64-row weight group (decode) or per 4 groups (prefill)
   const int per13 = V == 2 ? (a.g13.G + kPfGroups - 1) / kPfGroups : a.g13.G;
   const int per2 = V == 2 ? (a.g2.G + kPfGroups - 1) / kPfGroups : a.g2.G;
-  auto item = [&](const GemmArgs& g, bool g13, long long w) __attribute__((always_inline)) -> int {
+  auto item = [&](const GemmArgs& g, bool g13, long long w, int e = -1) __attribute__((always_inline)) -> int {
     if constexpr (V == 2) {
       const auto st = pf_make_stages<DT, kPfRows>();
       return g13 ? prefill_item<DT, true, 1, kPfRows>(g, w, cum, st) : prefill_item<DT, false, 1, kPfRows>(g, w, cum, st);
     } else {
       auto* red = reinterpret_cast<f32x4_t(*)[4 * NT][64]>(smem);
-      return g13 ? gemm_item<DT, NT, true>(g, w, cum, red) : gemm_item<DT, NT, false>(g, w, cum, red);
+      return g13 ? gemm_item<DT, NT, true>(g, w, cum, red, e) : gemm_item<DT, NT, false>(g, w, cum, red, e);
     }
   };
-  const int total_mt = build_schedule(a.offsets, a.E, MT, cum, wsum);
+  int total_pairs = 0;
+  const int total_mt =
+      V == 2 ? build_schedule(a.offsets, a.E, MT, cum, wsum) : build_decode_schedule<NT>(a.offsets, a.E, cum, pcum, wsum, total_pairs);
   const long long n13 = (long long)total_mt * per13, n2 = (long long)total_mt * per2;
   const int lb = V == 2 ? xcd_logical_block() : (int)blockIdx.x;
   // decode items: the blocks of a compute unit take turns at the top issue
   // priority, as in the stage kernels (later-placed blocks otherwise lag)
   int turn = (int)(blockIdx.x >> 8);
+  // decode items of 17-32 rows (NT = 1) take twice as long: the stage
+  // kernels' execution order (decode_item_at) keeps the blocks balanced
+  auto run_items = [&](const GemmArgs& g, bool g13, long long n) __attribute__((always_inline)) {
+    const long long P = (long long)total_pairs * g.G, rp = min(n % (long long)G, n - P);
+    for (long long x = lb; x < n; x += G, ++turn) {
+      if constexpr (V != 2) set_wave_priority(turn & 3);
+      if (total_pairs > 0) {
+        int e;
+        const long long w = decode_item_at(x, rp, P, g, cum, pcum, e);
+        item(g, g13, w, e);
+      } else {
+        item(g, g13, x);
+      }
+    }
+  };
   if constexpr (MOE_FUSED_GEMM_BARRIER) {
-    for (long long w = lb; w < n13; w += G, ++turn) {
-      if constexpr (V != 2) set_wave_priority(turn & 3);
-      item(a.g13, true, w);
-    }
+    run_items(a.g13, true, n13);
     grid_barrier(a.sync, 3 * G);
-    for (long long w = lb; w < n2; w += G, ++turn) {
-      if constexpr (V != 2) set_wave_priority(turn & 3);
-      item(a.g2, false, w);
-    }
+    run_items(a.g2, false, n2);
     set_wave_priority(0);
     grid_barrier(a.sync, 4 * G);
   } else {

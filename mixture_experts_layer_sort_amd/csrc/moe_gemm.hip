@@ -37,45 +37,6 @@ namespace moe {
 template <int DT, int NT>
 constexpr int gemm_min_waves_per_simd() { return NT == 1 ? (DT == DT_NVFP4 ? 4 : (DT == DT_MXFP8 ? 3 : 2)) : 1; }
 
-// Paired m-tiles of an expert with `rows` routed rows (NT = 1 decode items
-// of 17-32 rows, which take twice as long as the others): its full 32-row
-// m-tiles and a last partial one of more than 16 rows.  Its other m-tile,
-// if any, is the last one, of at most 16 rows.
-__device__ __forceinline__ int paired_mtiles(int rows) { return rows / kDecodeMT + (rows % kDecodeMT > 16 ? 1 : 0); }
-
-// Execution order of the NT = 1 decode items.  Blocks take positions
-// blockIdx.x, + gridDim.x, ... (round-robin, so blocks running together
-// stream neighbouring weight rows).  The N = q*B + r items leave blocks r..B-1
-// one item short; the P paired items go to positions rp .. rp + P - 1, rp =
-// min(r, N - P), i.e. to those blocks first, and the single items fill the
-// other positions in order.  Within each kind the order is m-tile-major.
-// cum / pcum: per-expert prefixes of m-tiles / paired m-tiles.
-// Returns the item; `e` receives its expert.
-__device__ __forceinline__ long long decode_item_at(long long x, long long rp, long long P, const GemmArgs& a,
-                                                     const int* cum, const int* pcum, int& e) {
-  const long long G = a.G;
-  int lo = 0, hi = a.E;
-  if (x >= rp && x < rp + P) {  // the k-th paired m-tile: expert lo with pcum[lo] <= k < pcum[lo + 1]
-    const long long k = (x - rp) / G, g = (x - rp) % G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pcum[mid] <= k) lo = mid;
-      else hi = mid;
-    }
-    e = lo;
-    return ((long long)cum[lo] + (k - pcum[lo])) * G + g;
-  }
-  const long long y = x < rp ? x : x - P;  // the k-th single m-tile, its expert's last
-  const long long k = y / G, g = y % G;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cum[mid] - pcum[mid] <= k) lo = mid;
-    else hi = mid;
-  }
-  e = lo;
-  return ((long long)cum[lo + 1] - 1) * G + g;
-}
-
 template <int DT, int NT, bool G13>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(gemm_min_waves_per_simd<DT, NT>())))
 void gemm_kernel(GemmArgs a) {
@@ -83,23 +44,8 @@ void gemm_kernel(GemmArgs a) {
   __shared__ int pcum[NT == 1 ? 1025 : 1];
   __shared__ int wsum[4];
   __shared__ f32x4_t red[3][4 * NT][64];
-  // m-tiles (low 16 bits) and, for NT = 1, paired m-tiles (high 16 bits) per
-  // expert in one scan.  NT = 1 runs only for T * k <= 16 E <= 16384 routed
-  // rows, so both totals stay below 2^16; NT = 2 scans m-tiles alone.
-  int total_mt, total_pairs = 0;
-  if constexpr (NT == 1) {
-    const int both = build_prefix<int>(
-        a.offsets, a.E, [](int c) { return (c + kDecodeMT - 1) / kDecodeMT + (paired_mtiles(c) << 16); },
-        [&](int e, int v) {
-          cum[e] = v & 0xFFFF;
-          pcum[e] = v >> 16;
-        },
-        wsum);
-    total_mt = both & 0xFFFF;
-    total_pairs = both >> 16;
-  } else {
-    total_mt = build_schedule(a.offsets, a.E, kDecodeMT, cum, wsum);
-  }
+  int total_pairs;
+  const int total_mt = build_decode_schedule<NT>(a.offsets, a.E, cum, pcum, wsum, total_pairs);
   const long long total = (long long)total_mt * a.G;
   int turn = (int)(blockIdx.x >> 8);
   if (total_pairs > 0) {

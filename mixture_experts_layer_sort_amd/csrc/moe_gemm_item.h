@@ -513,6 +513,69 @@ __device__ __forceinline__ int gemm_item(const GemmArgs& a, long long w, const i
   return e;
 }
 
+// Paired m-tiles of an expert with `rows` routed rows (NT = 1 decode items
+// of 17-32 rows, which take twice as long as the others): its full 32-row
+// m-tiles and a last partial one of more than 16 rows.  Its other m-tile,
+// if any, is the last one, of at most 16 rows.
+__device__ __forceinline__ int paired_mtiles(int rows) { return rows / kDecodeMT + (rows % kDecodeMT > 16 ? 1 : 0); }
+
+// Execution order of the NT = 1 decode items.  Blocks take positions
+// blockIdx.x, + gridDim.x, ... (round-robin, so blocks running together
+// stream neighbouring weight rows).  The N = q*B + r items leave blocks r..B-1
+// one item short; the P paired items go to positions rp .. rp + P - 1, rp =
+// min(r, N - P), i.e. to those blocks first, and the single items fill the
+// other positions in order.  Within each kind the order is m-tile-major.
+// cum / pcum: per-expert prefixes of m-tiles / paired m-tiles.
+// Returns the item; `e` receives its expert.
+__device__ __forceinline__ long long decode_item_at(long long x, long long rp, long long P, const GemmArgs& a,
+                                                     const int* cum, const int* pcum, int& e) {
+  const long long G = a.G;
+  int lo = 0, hi = a.E;
+  if (x >= rp && x < rp + P) {  // the k-th paired m-tile: expert lo with pcum[lo] <= k < pcum[lo + 1]
+    const long long k = (x - rp) / G, g = (x - rp) % G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pcum[mid] <= k) lo = mid;
+      else hi = mid;
+    }
+    e = lo;
+    return ((long long)cum[lo] + (k - pcum[lo])) * G + g;
+  }
+  const long long y = x < rp ? x : x - P;  // the k-th single m-tile, its expert's last
+  const long long k = y / G, g = y % G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cum[mid] - pcum[mid] <= k) lo = mid;
+    else hi = mid;
+  }
+  e = lo;
+  return ((long long)cum[lo + 1] - 1) * G + g;
+}
+
+// Per-expert prefixes of the decode items' m-tiles (cum) and, for NT = 1,
+// of their paired m-tiles (pcum), in one scan: the two counts are packed in
+// 16-bit halves.  NT = 1 runs only for T * k <= 16 E <= 16384 routed rows,
+// so both totals stay below 2^16; NT = 2 scans m-tiles alone.  Returns the
+// m-tile total; total_pairs receives the paired total (0 for NT = 2).
+template <int NT>
+__device__ __forceinline__ int build_decode_schedule(const int* __restrict__ offsets, int E, int* cum, int* pcum,
+                                                     int* wsum, int& total_pairs) {
+  total_pairs = 0;
+  if constexpr (NT == 1) {
+    const int both = build_prefix<int>(
+        offsets, E, [](int c) { return (c + kDecodeMT - 1) / kDecodeMT + (paired_mtiles(c) << 16); },
+        [&](int e, int v) {
+          cum[e] = v & 0xFFFF;
+          pcum[e] = v >> 16;
+        },
+        wsum);
+    total_pairs = both >> 16;
+    return both & 0xFFFF;
+  } else {
+    return build_schedule(offsets, E, kDecodeMT, cum, wsum);
+  }
+}
+
 hipError_t launch_prefill(int dt, bool g13, const GemmArgs& a, int grid, hipStream_t s);
 
 }  // namespace moe

@@ -21,6 +21,10 @@ SMALL = {
     "bf16_ragged": W["bf16_decode"].scaled(T=33, H=512, I=384, E=16),
     "mxfp8_decode_small": W["mxfp8_decode"].scaled(T=40, H=640, I=256, E=32),
     "nvfp4_decode_small": W["nvfp4_decode_t8"].scaled(T=13, H=512, I=256, E=48),
+    # decode-shaped GEMMs whose experts get 17-32 routed rows (items run as
+    # two wave pairs; mxfp8_decode_small and bf16_ragged also have them, and
+    # experts above 32 rows)
+    "nvfp4_decode_paired": W["nvfp4_decode_t8"].scaled(T=60, H=512, I=256, E=16, k=4),
     "mxfp8_prefill_small": W["mxfp8_prefill"].scaled(T=300, H=512, I=256, E=16, k=4),
     "nvfp4_prefill_small": W["nvfp4_decode_t128"].scaled(T=96, H=384, I=128, E=8, k=3),
     "bf16_prefill_small": W["bf16_decode"].scaled(T=150, H=256, I=256, E=6, k=2),
