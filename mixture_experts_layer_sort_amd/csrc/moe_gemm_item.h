@@ -371,7 +371,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
           for (int j = 0; j < 4; ++j) {
             if (a.gated) {
               const float gv = acc[tp][s][j] * alpha, uv = acc[2 + tp][s][j] * alpha;
-              h[tp][j] = gv / (1.0f + expf(-gv)) * uv;
+              // silu with the hardware exp and reciprocal (~1 ulp each): h is requantised
+              // to at most 8 significant bits, so a code moves only within a few ulps of a midpoint
+              h[tp][j] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
             } else {
               const float v = fmaxf((hh ? acc[2 + tp][s][j] : acc[tp][s][j]) * alpha, 0.f);
               h[tp][j] = v * v;

@@ -250,7 +250,9 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float gv = acc[0][S][i] * alpha, uv = acc[1][S][i] * alpha;
-            h[i] = gv / (1.0f + expf(-gv)) * uv;
+            // silu with the hardware exp and reciprocal (~1 ulp each): h is requantised
+            // to at most 8 significant bits, so a code moves only within a few ulps of a midpoint
+            h[i] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
           }
         } else {
 #pragma unroll
