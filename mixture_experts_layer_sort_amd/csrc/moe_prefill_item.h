@@ -195,15 +195,11 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
             uint16_t* od = a.out_deq + (size_t)r * I + 32 * gg + 4 * hl;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-              uint32_t v = 0, d[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const uint32_t c = e4m3_from_f32(ldexpf(h[4 * b + j], -sx));
-                v |= c << (8 * j);
-                d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), sx)) >> 16;  // exact in bf16
-              }
+              uint2 dq;
+              const uint32_t v = mx_encode4(ldexpf(h[4 * b], -sx), ldexpf(h[4 * b + 1], -sx),
+                                            ldexpf(h[4 * b + 2], -sx), ldexpf(h[4 * b + 3], -sx), sx, dq);
               *reinterpret_cast<uint32_t*>(o + 8 * b) = v;
-              *reinterpret_cast<uint2*>(od + 8 * b) = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+              *reinterpret_cast<uint2*>(od + 8 * b) = dq;
             }
             if (hl == 0) a.out_scales[(size_t)r * (I / 32) + gg] = (uint8_t)(sx + 127);
           }
