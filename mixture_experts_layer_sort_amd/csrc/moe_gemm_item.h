@@ -138,37 +138,6 @@ __device__ __forceinline__ bf16x8_t mxfp8_dequant8(uint32_t lo, uint32_t hi, uin
   return o;
 }
 
-// Four values of one MX block, already scaled by 2^-sx into e4m3's range,
-// -> their e4m3 codes (bytes 0..3) and the exact dequantised values code *
-// 2^sx as 4 bf16 (two words).  The hardware converter at scale 1 after a
-// clamp to +-448 gives the same codes as e4m3_from_f32 (nearest, ties to
-// even, saturating, sign kept): checked on MI355X over every bf16 value,
-// every e4m3 rounding midpoint and its fp32 neighbours and 2M random fp32
-// values (no mismatch).  sx = -127 (an all-zero or sub-2^-118 block, e8m0
-// byte 0) takes the integer path, so the copy stays exact there too.
-__device__ __forceinline__ uint32_t mx_encode4(float a, float b, float c, float d, int sx, uint2& deq) {
-  typedef short v2s __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  auto sat = [](float v) { return fminf(fmaxf(v, -448.f), 448.f); };
-  v2s o = {0, 0};
-  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, sat(a), sat(b), 1.0f, false);
-  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, sat(c), sat(d), 1.0f, true);
-  const uint32_t v = (uint32_t)(uint16_t)o[0] | ((uint32_t)(uint16_t)o[1] << 16);
-  if (sx > -127) {
-    const float sc = __uint_as_float((uint32_t)(sx + 127) << 23);  // 2^sx
-    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, sc, false);
-    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, sc, true);
-    __builtin_memcpy(&deq.x, &p0, 4);
-    __builtin_memcpy(&deq.y, &p1, 4);
-  } else {
-    uint32_t dd[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dd[j] = __float_as_uint(ldexpf(e4m3_to_f32((v >> (8 * j)) & 0xFFu), sx)) >> 16;
-    deq = make_uint2(dd[0] | (dd[1] << 16), dd[2] | (dd[3] << 16));
-  }
-  return v;
-}
-
 // ------------------------------------------------------------------ K-slice fragments
 // Raw bytes of one 128-wide K slice ("kgroup") for the 4 weight tiles of a
 // work item and its NT token sub-tiles, as loaded from memory; converted and
@@ -353,8 +322,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp) {
               uint2 dq;
-              const uint32_t v = mx_encode4(ldexpf(h[tp][0], -sx), ldexpf(h[tp][1], -sx), ldexpf(h[tp][2], -sx),
-                                            ldexpf(h[tp][3], -sx), sx, dq);
+              const uint32_t v = mx_encode4(h[tp][0], h[tp][1], h[tp][2], h[tp][3], sx, dq);
               *reinterpret_cast<uint32_t*>(o + 16 * tp) = v;
               *reinterpret_cast<uint2*>(od + 16 * tp) = dq;
             }

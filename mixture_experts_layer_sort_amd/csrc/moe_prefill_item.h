@@ -196,8 +196,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
               uint2 dq;
-              const uint32_t v = mx_encode4(ldexpf(h[4 * b], -sx), ldexpf(h[4 * b + 1], -sx),
-                                            ldexpf(h[4 * b + 2], -sx), ldexpf(h[4 * b + 3], -sx), sx, dq);
+              const uint32_t v = mx_encode4(h[4 * b], h[4 * b + 1], h[4 * b + 2], h[4 * b + 3], sx, dq);
               *reinterpret_cast<uint32_t*>(o + 8 * b) = v;
               *reinterpret_cast<uint2*>(od + 8 * b) = dq;
             }

@@ -57,8 +57,7 @@ __global__ void quant_w_mxfp8_kernel(const float* __restrict__ w, long long n, u
     float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     amax = wave_max_xor(amax, 1, 4);
     int s = mx_scale_exp(amax);
-    uint32_t out = e4m3_from_f32(ldexpf(v.x, -s)) | (e4m3_from_f32(ldexpf(v.y, -s)) << 8) |
-                   (e4m3_from_f32(ldexpf(v.z, -s)) << 16) | (e4m3_from_f32(ldexpf(v.w, -s)) << 24);
+    const uint32_t out = e4m3x4_from_f32(ldexpf(v.x, -s), ldexpf(v.y, -s), ldexpf(v.z, -s), ldexpf(v.w, -s));
     if (ok) {
       reinterpret_cast<uint32_t*>(codes)[i] = out;
       if ((i & 7) == 0) scales[i >> 3] = (uint8_t)(s + 127);

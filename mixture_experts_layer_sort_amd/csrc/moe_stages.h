@@ -195,17 +195,12 @@ __device__ void quantize_x_blocks(const uint16_t* __restrict__ x, long long n_el
       const long long blk = i / LPB;
       if constexpr (DT == DT_MXFP8) {
         int s = mx_scale_exp(amax);
-        uint32_t out = 0, d[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t c = e4m3_from_f32(ldexpf(v[j], -s));
-          out |= c << (8 * j);
-          d[j] = __float_as_uint(ldexpf(e4m3_to_f32(c), s)) >> 16;  // exact in bf16
-        }
+        uint2 dq;
+        const uint32_t out = mx_encode4(v[0], v[1], v[2], v[3], s, dq);
         if (ok) {
           reinterpret_cast<uint32_t*>(codes)[i] = out;
           if (sub == 0) scales[blk] = (uint8_t)(s + 127);
-          reinterpret_cast<uint2*>(deq)[i] = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
+          reinterpret_cast<uint2*>(deq)[i] = dq;
         }
       } else {
         uint32_t sc_code = e4m3_from_f32(amax / 6.0f);
