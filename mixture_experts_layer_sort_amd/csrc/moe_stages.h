@@ -12,13 +12,14 @@ namespace moe {
 // (logit descending, id ascending) pick the experts; slot j is the j-th pick.
 // Weights: softmax over the k picked logits [vLLM PR 40082 report,
 // "Implementation" item 1: routing inside the fused call].
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
-                                            int* __restrict__ ids, float* __restrict__ wts, int lane) {
+template <int NV>
+__device__ __forceinline__ void route_token_n(const float* __restrict__ logits, int t, int E, int k,
+                                              int* __restrict__ ids, float* __restrict__ wts, int lane) {
   const float* row = logits + (size_t)t * E;
-  float v[16];
+  float v[NV];
   uint32_t taken = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NV; ++i) {
     int e = lane + 64 * i;
     float x = e < E ? row[e] : -INFINITY;
     v[i] = (x == x) ? x : -INFINITY;  // NaN never wins; results stay in range
@@ -30,7 +31,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NV; ++i) {
       int id = lane + 64 * i;
       bool better = !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && id < bi));
       bv = better ? v[i] : bv;
@@ -59,6 +60,17 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
     ids[(size_t)t * k + lane] = my_id;
     wts[(size_t)t * k + lane] = ex / sum;
   }
+}
+
+// One token's routing with NV = ceil(E / 64) rounded up to a power of two
+// logits per lane (E <= 1024), so small expert counts skip empty slots.
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            int* __restrict__ ids, float* __restrict__ wts, int lane) {
+  if (E <= 64) route_token_n<1>(logits, t, E, k, ids, wts, lane);
+  else if (E <= 128) route_token_n<2>(logits, t, E, k, ids, wts, lane);
+  else if (E <= 256) route_token_n<4>(logits, t, E, k, ids, wts, lane);
+  else if (E <= 512) route_token_n<8>(logits, t, E, k, ids, wts, lane);
+  else route_token_n<16>(logits, t, E, k, ids, wts, lane);
 }
 
 // ------------------------------------------------------------------ permutation
