@@ -68,6 +68,37 @@ def _setup(w):
 def test_layer_parity_small(name):
     w = SMALL[name]
     print(f"case {name}: {w}", flush=True)
+    _check_layer(w, name, mi.host_x(w), mi.host_logits(w))
+
+
+def _decode_boundary_logits(w, counts, seed):
+    """Logits that route exactly counts[e] of the T*2 (token, slot) pairs to
+    expert e: token t picks first[t] and second[t] (always distinct)."""
+    picks = [e for e, c in enumerate(counts) for _ in range(c)]
+    assert len(picks) == 2 * w.T and w.k == 2
+    first, second = picks[: w.T], picks[w.T:]
+    rng = np.random.default_rng(seed)
+    logits = (rng.standard_normal((w.T, w.E)) - 10.0).astype(np.float32)
+    for t in range(w.T):
+        assert first[t] != second[t]
+        logits[t, first[t]] = np.float32(5.0 + rng.uniform(-0.1, 0.1))
+        logits[t, second[t]] = np.float32(4.0 + rng.uniform(-0.1, 0.1))
+    return logits
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8", "nvfp4"])
+def test_decode_item_boundaries(dtype):
+    """Decode-shaped layer (T*k <= 16 E: one 16-wide token tile per wave)
+    whose experts get exactly 16, 17, 33 and 30 routed rows: a single 16-row
+    item, items of 17-32 rows run as two wave pairs, and a 32-row item
+    followed by a 1-row one, all tokens against the oracle."""
+    base = {"bf16": W["bf16_decode"], "mxfp8": W["mxfp8_decode"], "nvfp4": W["nvfp4_decode_t8"]}[dtype]
+    w = base.scaled(T=48, H=256, I=256, E=8, k=2)
+    logits = _decode_boundary_logits(w, [16, 17, 33, 30, 0, 0, 0, 0], seed=21)
+    _check_layer(w, f"boundaries_{dtype}", mi.host_x(w), logits)
+
+
+def _check_layer(w, name, x, logits):
     cw, Wo = _setup(w)
     # the library's weight quantiser reproduces the oracle's canonical codes bit for bit
     got = gh.canonical_to_numpy(cw)
@@ -79,8 +110,6 @@ def test_layer_parity_small(name):
         for e in range(w.E):
             assert np.array_equal(np.asarray(got[n][e]), np.asarray(ref[e])), (n, e)
 
-    x = mi.host_x(w)
-    logits = mi.host_logits(w)
     layer = gh.DeviceLayer(w, cw)
     xd, ld = gh.to_device_x(x), torch.from_numpy(logits).to(gh.dev())
     r = layer.staged(xd, ld)
