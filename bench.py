@@ -4,8 +4,10 @@
 
 One step = one pass of the whole layer over one batch (route -> permute +
 activation quantisation -> gate/up GEMM + SwiGLU + requant -> down GEMM ->
-combine), i.e. one moe_forward call, with inputs and prepared weights already resident in HBM.  The default
-workload is the bf16 decode layer (T=64, H=4096, I=1408, E=64, top-6).
+combine), i.e. one moe_forward call, with inputs and prepared weights already
+resident in HBM.  The default workload is the MXFP8 prefill layer (T=8192,
+H=7168, I=2048, E=256, top-8, Zipf(1.1)-skewed routing); --workload picks any
+other (e.g. bf16_decode, mxfp8_decode, nvfp4_decode_t8, nvfp4_decode_t128).
 Prints one JSON line with tokens/s (K steps of moe_forward, the five stage
 kernels back to back on torch's stream, each step between HIP events, with
 the L2 and the Infinity Cache flushed by reading 1 GiB before every step
@@ -15,8 +17,8 @@ region of K steps through the staged entry points, flushed the same way),
 whole-layer HBM / MFMA fractions, the back-to-back (unflushed) step time,
 the step time when the same moe_forward call is captured into a HIP graph
 and replayed,
-the single-launch entry's step time, measured achievable peaks (device copy
-GB/s, a register-only MFMA loop) and the CPU oracle timed on a bounded
+the single-launch entry's step time, a measured device copy (GB/s) for
+context, and the CPU oracle (its expert-grouped BLAS form) timed on a bounded
 sample of the same workload.
 """
 from __future__ import annotations
@@ -32,14 +34,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-# dense MFMA peak of the arithmetic the contraction runs in: bf16 MFMA for bf16
-# and MXFP8 (exact fp8 -> bf16), fp16 MFMA for NVFP4 (exact e2m1 x e4m3 -> fp16)
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 2500.0, "nvfp4": 2500.0, "bf16_mxfp8": 2500.0}
+# MI355X dense matrix peaks, published (no sparsity)
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+# The prefill roofline is priced at the dense peak of the layer format's own
+# data type: MXFP8 layers against the fp8 peak (whatever instruction the
+# kernel uses), bf16 and NVFP4 (run as exact fp16 products) against the
+# 16-bit peak; bf16 x MXFP8 runs bf16 products, priced at the bf16 peak.
+MFMA_PEAK_TFLOPS = {"bf16": BF16_PEAK_TFLOPS, "mxfp8": FP8_PEAK_TFLOPS, "nvfp4": BF16_PEAK_TFLOPS,
+                    "bf16_mxfp8": BF16_PEAK_TFLOPS}
 # the arithmetic type of the contractions per layer format ("bf16_mxfp8": bf16
 # activations over MXFP8 weights)
 ARITH_DTYPE = {"bf16": "bf16", "mxfp8": "bf16", "nvfp4": "f16", "bf16_mxfp8": "bf16"}
-FP8_PEAK_TFLOPS = 5000.0
-DEFAULT_WORKLOAD = "bf16_decode"
+DEFAULT_WORKLOAD = "mxfp8_prefill"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mixture_experts_layer_sort_amd", "csrc")
 
@@ -79,25 +86,76 @@ def load_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
+class Layer:
+    """One layer on the device: canonical weights quantised from the seeded
+    fp32 masters by the library (expert by expert), the packed weights and the
+    forward workspace."""
+
+    def __init__(self, lib, w, device):
+        import torch
+
+        E, H, I, R = w.E, w.H, w.I, w.R13
+        wf = "mxfp8" if w.dtype == "bf16_mxfp8" else w.dtype
+        u8 = torch.uint8
+        if wf == "bf16":
+            c13, c2 = (torch.empty(E, R, H, dtype=torch.bfloat16, device=device),
+                       torch.empty(E, H, I, dtype=torch.bfloat16, device=device))
+            s13 = s2 = a13 = a2 = None
+        elif wf == "mxfp8":
+            c13, c2 = torch.empty(E, R, H, dtype=u8, device=device), torch.empty(E, H, I, dtype=u8, device=device)
+            s13, s2 = (torch.empty(E, R, H // 32, dtype=u8, device=device),
+                       torch.empty(E, H, I // 32, dtype=u8, device=device))
+            a13 = a2 = None
+        else:
+            c13, c2 = (torch.empty(E, R, H // 2, dtype=u8, device=device),
+                       torch.empty(E, H, I // 2, dtype=u8, device=device))
+            s13, s2 = (torch.empty(E, R, H // 16, dtype=u8, device=device),
+                       torch.empty(E, H, I // 16, dtype=u8, device=device))
+            a13, a2 = torch.empty(E, dtype=torch.float32, device=device), torch.empty(E, dtype=torch.float32,
+                                                                                       device=device)
+
+        def sub(t, e):
+            return None if t is None else t[e:e + 1]
+
+        import moe_inputs as mi
+
+        for e in range(E):
+            m13, m2 = mi.device_master_weights(w, e, device)
+            lib.moe_quantize_weights(w.dtype, 1, R, H, m13, c13[e:e + 1], sub(s13, e), sub(a13, e))
+            lib.moe_quantize_weights(w.dtype, 1, H, I, m2, c2[e:e + 1], sub(s2, e), sub(a2, e))
+            if w.fold:
+                lib.moe_nvfp4_fold_global_scale(1, R, H, sub(s13, e), sub(a13, e))
+                lib.moe_nvfp4_fold_global_scale(1, H, I, sub(s2, e), sub(a2, e))
+            del m13, m2
+        self.w = w
+        self.shape = lib.make_shape(H, I, E, w.k, w.T, w.dtype, w.act)
+        self.packed = torch.empty(lib.moe_packed_weight_bytes(self.shape), dtype=u8, device=device)
+        lib.moe_prepare_weights(self.shape, c13, s13, a13, c2, s2, a2, self.packed)
+        self.ws = torch.empty(lib.moe_workspace_bytes(self.shape), dtype=u8, device=device)
+        lib.moe_workspace_init(self.shape, self.ws)
+        torch.cuda.synchronize()
+        del c13, c2, s13, s2, a13, a2
+
+    def sync_words(self):
+        """The single-launch kernel's synchronisation words (word 2: spin timeout)."""
+        import numpy as np
+
+        return self.ws[: 4 * (4 + self.w.E)].cpu().numpy().view(np.uint32)
+
+
 def build_layer(w, device):
-    """Device inputs (seeded generators), library-quantised canonical weights
-    and the prepared (packed) weights."""
+    """Device inputs (seeded generators) and the layer with library-quantised,
+    prepared weights."""
     import torch
 
     import mixture_experts_layer_sort_amd as lib
     import moe_inputs as mi
-    from tests import gpu_harness as gh
 
-    cw = gh.alloc_canonical(w)
-    for e in range(w.E):
-        w13, w2 = mi.device_master_weights(w, e, device)
-        gh.quantize_expert(w, cw, e, w13, w2)
-        del w13, w2
-    layer = gh.DeviceLayer(w, cw)
+    layer = Layer(lib, w, device)
     x = mi.device_x(w, device)
     logits = mi.device_logits(w, device)
     torch.cuda.synchronize()
-    return lib, gh, cw, layer, x, logits
+    return lib, layer, x, logits
 
 
 class StagedStep:
@@ -168,9 +226,37 @@ def gemm13_bytes(w, n_active):
             + w.T * w.k * w.I * act_bytes_per_elem(w.dtype))
 
 
-def cpu_baseline(w, device, ids, max_seconds=25.0):
-    """The CPU oracle on a bounded sample of the same workload (first tokens),
-    with its own weights quantised from the same seeded fp32 masters."""
+def _quantize_expert(args):
+    """Oracle quantisation of one expert's fp32 masters (worker process)."""
+    w13, w2, dtype, act, fold = args
+    from oracle import moe as omoe
+
+    W = omoe.quantize_weights({0: w13}, {0: w2}, dtype, act, fold)
+    return tuple(None if getattr(W, n) is None else getattr(W, n)[0]
+                 for n in ("w13", "w2", "w13_s", "w2_s", "w13_a", "w2_a"))
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, device, ids, max_experts=12, max_tokens=1024):
+    """The CPU oracle's expert-grouped form (BLAS matrix products) timed on a
+    bounded sample of the same workload: the tokens (in index order, at most
+    max_tokens) whose k experts all lie among the max_experts experts with the
+    most routed rows, with the oracle's own weights quantised from the same
+    seeded fp32 masters (quantisation not timed; dequantisation of the sampled
+    experts and routing -> output timed)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -178,42 +264,57 @@ def cpu_baseline(w, device, ids, max_seconds=25.0):
     import moe_inputs as mi
     from oracle import moe as omoe
 
-    x = mi.device_x(w, device).view(torch.int16).cpu().numpy().view(np.uint16)
-    logits = mi.device_logits(w, device).cpu().numpy()
-    # sample size: tokens whose experts' dequantisation + products take ~10-25 s
-    per_expert_s = {"bf16": 0.25, "mxfp8": 2.0, "nvfp4": 2.5, "bf16_mxfp8": 2.0}[w.dtype] * (w.H * w.I) / (4096 * 1408)
-    n = 0
-    experts = set()
-    while n < w.T:
-        nxt = experts | set(ids[n].tolist())
-        if n > 0 and len(nxt) * per_expert_s > max_seconds:
-            break
-        experts, n = nxt, n + 1
-    w13, w2 = {}, {}
-    for e in sorted(experts):
+    counts = np.bincount(ids.ravel(), minlength=w.E)
+    hot = set(int(e) for e in np.argsort(-counts, kind="stable")[:max_experts] if counts[e] > 0)
+    toks = [t for t in range(w.T) if set(ids[t].tolist()) <= hot][:max_tokens]
+    if not toks:  # fall back to the first tokens whose experts fit the budget
+        experts = set()
+        for t in range(w.T):
+            nxt = experts | set(ids[t].tolist())
+            if toks and len(nxt) > max_experts:
+                break
+            toks.append(t)
+            experts = nxt
+        hot = experts
+    toks = np.array(toks)
+    experts = sorted(set(int(e) for e in ids[toks].ravel()))
+    x = mi.device_x(w, device).view(torch.int16).cpu().numpy().view(np.uint16)[toks]
+    logits = mi.device_logits(w, device).cpu().numpy()[toks]
+    jobs = []
+    for e in experts:
         a, b = mi.device_master_weights(w, e, device)
-        w13[e], w2[e] = a.cpu().numpy(), b.cpu().numpy()
-    Wo = omoe.quantize_weights(w13, w2, w.dtype, w.act, w.fold)  # weight quantisation: not timed
-    del w13, w2
+        jobs.append((a.cpu().numpy(), b.cpu().numpy(), w.dtype, w.act, w.fold))
+    with cf.ProcessPoolExecutor(max_workers=min(16, len(jobs)), mp_context=mp.get_context("spawn")) as ex:
+        parts = list(ex.map(_quantize_expert, jobs))
+    del jobs
+    # a dense expert dimension: experts outside the sample are never routed to here
+    full = {n: {} for n in ("w13", "w2", "w13_s", "w2_s", "w13_a", "w2_a")}
+    for e, p in zip(experts, parts):
+        for n, v in zip(("w13", "w2", "w13_s", "w2_s", "w13_a", "w2_a"), p):
+            full[n][e] = v
+    Wo = omoe.Weights(w.dtype, full["w13"], full["w2"], full["w13_s"] or None, full["w2_s"] or None,
+                      full["w13_a"] if all(v is not None for v in full["w13_a"].values()) else None,
+                      full["w2_a"] if all(v is not None for v in full["w2_a"].values()) else None, act=w.act)
+    if Wo.w13_s is not None and any(v is None for v in Wo.w13_s.values()):
+        Wo.w13_s = Wo.w2_s = None
+    # route on the sampled tokens' logits; the grouped form dequantises each routed expert once
     threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    # repeat a short sample until about 10 s of CPU work have been timed
     reps, dt = 0, 0.0
-    while reps == 0 or (dt < 10.0 and reps < 50):
+    while reps == 0 or (dt < 10.0 and reps < 20):
         t0 = time.perf_counter()
-        omoe.moe_layer(x[:n], logits[:n], Wo, w.k)
+        omoe.moe_layer_grouped(x, logits, Wo, w.k)
         dt += time.perf_counter() - t0
         reps += 1
-    return {"value": n * reps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} of {w.T} tokens ({len(experts)} experts) x {reps} passes, fp64 per-token loop, "
-                      f"{dt:.1f} s wall, weight quantisation excluded"}
+    return {"value": len(toks) * reps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+            "sample": f"{len(toks)} of {w.T} tokens (those routed only to the {len(hot)} experts with the most "
+                      f"rows; {len(experts)} experts) x {reps} passes of the expert-grouped oracle (numpy BLAS, "
+                      f"fp64), {dt:.1f} s wall incl. dequantisation, weight quantisation excluded"}
 
 
 def measure_achievable(torch, device):
-    """Measured context for the peaks: a 1 GiB device-to-device copy (GB/s of
-    read + write traffic) and a register-only loop of 32x32x16 bf16 MFMAs
-    (the contraction the prefill GEMM uses) at one and two blocks per CU."""
-    import ctypes
-
+    """Measured context for the HBM peak: a 1 GiB device-to-device copy (GB/s
+    of read + write traffic)."""
     res = {}
     a = torch.empty(1 << 28, dtype=torch.float32, device=device)
     b = torch.empty_like(a)
@@ -227,24 +328,6 @@ def measure_achievable(torch, device):
     torch.cuda.synchronize()
     res["device_copy_gbs"] = 5 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del a, b
-    path = os.path.join(ROOT, "mixture_experts_layer_sort_amd", "libmoe_probe.so")
-    if os.path.exists(path):
-        probe = ctypes.CDLL(path)
-        cus = torch.cuda.get_device_properties(device).multi_processor_count
-        out = torch.empty(2 * cus * 256, dtype=torch.float32, device=device)
-        stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
-        best, iters = 0.0, 4000
-        for bpc in (1, 2):
-            blocks = bpc * cus
-            probe.moe_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, 100, stream)
-            e0.record()
-            rc = probe.moe_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, iters, stream)
-            e1.record()
-            torch.cuda.synchronize()
-            if rc == 0:
-                flops = blocks * 4 * iters * 8 * 32768.0
-                best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
-        res["mfma_bf16_32x32x16_loop_tflops"] = best
     return res
 
 
@@ -280,8 +363,7 @@ def main():
         return
 
     w = mi.WORKLOADS[args.workload]
-    lib, gh, cw, layer, x, logits = build_layer(w, device)
-    del cw
+    lib, layer, x, logits = build_layer(w, device)
     out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=device)
     ids_t = torch.empty(w.T, w.k, dtype=torch.int32, device=device)
     wts_t = torch.empty(w.T, w.k, dtype=torch.float32, device=device)
@@ -400,6 +482,7 @@ def main():
     else:
         roof = {"bound": "mfma", "kernel": "gemm13_swiglu_quant", "achieved": g13_tflops,
                 "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s", "frac": g13_tflops / MFMA_PEAK_TFLOPS[w.dtype],
+                "frac_of_bf16_peak": g13_tflops / BF16_PEAK_TFLOPS,
                 "traffic": traffic, "algorithmic_flops_per_launch": w.T * w.k * 2.0 * w.H * w.R13,
                 "avg_launch_ms": kms["gemm13"]}
     rec = {
@@ -422,7 +505,7 @@ def main():
         "layer": {"algorithmic_bytes": B, "flops": F, "gpu_ms_per_step": gpu_ms_step, "hbm_gbs": layer_gbs,
                   "hbm_frac": layer_gbs / HBM_PEAK_GBS, "mfma_tflops": tflops,
                   "mfma_frac": tflops / MFMA_PEAK_TFLOPS[w.dtype],
-                  "mfma_frac_of_fp8_peak": tflops / FP8_PEAK_TFLOPS if w.dtype in ("mxfp8", "bf16_mxfp8") else None,
+                  "mfma_frac_of_bf16_peak": tflops / BF16_PEAK_TFLOPS,
                   "regime": "decode" if decode else "prefill", "staged_kernel_ms": kms,
                   "step_ms_min_median_max": [step_ms[0], ms_step, step_ms[-1]],
                   "back_to_back_unflushed_ms_per_step": b2b_ms_step,

@@ -37,10 +37,6 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the MoE library)")
 
 
-PROBE_DIR = os.path.join(PKG_DIR, "probe")
-PROBE_LIB_PATH = os.path.join(PKG_DIR, "libmoe_probe.so")
-
-
 def _compile(srcs, out, verbose):
     tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", os.path.join(PKG_DIR, "..", "include"), "-o", tmp, *srcs]
@@ -54,10 +50,8 @@ def _compile(srcs, out, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source under csrc/ into LIB_PATH (and the benchmark's
-    roofline probe into PROBE_LIB_PATH); returns LIB_PATH."""
+    """Compile every HIP source under csrc/ into LIB_PATH; returns LIB_PATH."""
     _compile(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), LIB_PATH, verbose)
-    _compile(sorted(glob.glob(os.path.join(PROBE_DIR, "*.hip"))), PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

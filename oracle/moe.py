@@ -197,6 +197,22 @@ def quantize_x(x_bits: np.ndarray, dtype: str):
     return c, s, quant.dequantize_act(c, s, dtype)
 
 
+def expert_mlp(xh: np.ndarray, w13: np.ndarray, w2: np.ndarray, act: str, dtype: str):
+    """One routed pair through its expert: xh the dequantised activation row
+    (float64 [H]), w13 / w2 the expert's dequantised weights.  Gate/up product,
+    SwiGLU (or squared ReLU), requantisation of the intermediate in the layer
+    format, down product.  Returns ((codes, scales, dequantised) of the
+    intermediate, y float64 [H])."""
+    if act == "relu2":
+        h = relu2(w13 @ xh)
+    else:
+        I = w13.shape[0] // 2
+        h = silu_mul(w13[:I] @ xh, w13[I:] @ xh)
+    hc, hsc, hh = requant_h(h[None, :], dtype)
+    y = w2 @ hh[0]
+    return (hc[0], None if hsc is None else hsc[0], hh[0]), y
+
+
 @dataclasses.dataclass
 class LayerResult:
     out: np.ndarray            # bf16 bits [T, H] (rows of the requested tokens)
@@ -230,17 +246,11 @@ def moe_layer(x_bits, logits, W: Weights, k: int, tokens=None, keep=False) -> La
             if e not in cache:
                 cache[e] = W.dequant(e)
             w13, w2 = cache[e]
-            if W.act == "relu2":
-                h = relu2(w13 @ xh)
-            else:
-                I = w13.shape[0] // 2
-                h = silu_mul(w13[:I] @ xh, w13[I:] @ xh)
-            hc, hsc, hh = requant_h(h[None, :], W.dtype)
-            y = w2 @ hh[0]
+            hq, y = expert_mlp(xh, w13, w2, W.act, W.dtype)
             acc += wts[t, j] * y
             if keep:
                 ys[(t, j)] = y
-                hs[(t, j)] = (hc[0], None if hsc is None else hsc[0], hh[0])
+                hs[(t, j)] = hq
         out64[row] = acc
     out = codecs.bf16_encode(out64.astype(np.float32))
     return LayerResult(out, out64, ids, wts, ys, hs)

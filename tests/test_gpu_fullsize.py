@@ -67,6 +67,27 @@ def _pick_tokens(ids, k, limit):
     return sorted(toks), sorted(experts)
 
 
+def _sorted_positions(off, n_hot=4, item_rows=(128, 256)):
+    """Sorted rows of the `n_hot` experts with the most routed rows: the first
+    row, the rows on both sides of every 128- and 256-row item boundary among
+    the first three, a middle row, the first row of the last (ragged) item and
+    the last row.  Returns {expert: sorted row positions}."""
+    counts = np.diff(off)
+    hot = [int(e) for e in np.argsort(-counts, kind="stable")[:n_hot] if counts[e] > 0]
+    out = {}
+    for e in hot:
+        lo, hi = int(off[e]), int(off[e + 1])
+        c = hi - lo
+        pos = {lo, lo + c // 2, hi - 1}
+        for m in item_rows:
+            for b in (1, 2, 3):
+                if b * m < c:
+                    pos.update({lo + b * m - 1, lo + b * m})
+            pos.add(lo + ((c - 1) // m) * m)  # first row of the last item
+        out[e] = sorted(p for p in pos if lo <= p < hi)
+    return out
+
+
 @pytest.mark.parametrize("name", ["tiny_bf16", "bf16_decode", "mxfp8_decode", "nvfp4_decode_t8",
                                   "nvfp4_decode_t128", "bf16_mxfp8_decode", "relu2_nvfp4_decode_t128",
                                   "nvfp4_folded_decode_t128",
@@ -154,5 +175,32 @@ def test_fullsize_parity(name, pool):
             assert gh.rel_l2(y_got, ref.y[(t, j)]) <= tol, (t, j)
     rel, mad = gh.check_out(gh.bf16_numpy(r["out"])[toks], ref.out, w.dtype, name)
     _log(f"{name}: sampled tokens out relL2 {rel:.2e} max|d|/rms {mad:.2e}")
+
+    if w.T * w.k >= 64 * w.E:
+        # prefill-shaped GEMMs: rows at fixed sorted positions of the hottest
+        # experts (item boundaries, the ragged last item), intermediate and y
+        # per routed pair against the oracle's expert MLP
+        sample = _sorted_positions(off)
+        hot = sorted(sample)
+        _log(f"{name}: sorted-position sample of experts {hot}: {sum(len(v) for v in sample.values())} rows")
+        res = list(pool.map(_quantize_pair, [(*[m.cpu().numpy() for m in mi.device_master_weights(w, e, dev)],
+                                              w.dtype, w.fold) for e in hot]))
+        Wh = omoe.Weights(w.dtype, {e: r_[0][0] for e, r_ in zip(hot, res)}, {e: r_[1][0] for e, r_ in zip(hot, res)},
+                          {e: r_[0][1] for e, r_ in zip(hot, res)}, {e: r_[1][1] for e, r_ in zip(hot, res)},
+                          {e: r_[0][2] for e, r_ in zip(hot, res)}, {e: r_[1][2] for e, r_ in zip(hot, res)}, act=w.act)
+        worst = 0.0
+        for e in hot:
+            w13d, w2d = Wh.dequant(e)
+            for row in sample[e]:
+                p = int(sp[row])
+                _, _, xh = omoe.quantize_x(x_bits[p // w.k: p // w.k + 1], w.dtype)
+                (_, _, h_ref), y_ref = omoe.expert_mlp(xh[0], w13d, w2d, w.act, w.dtype)
+                h_got = oquant.dequantize_act(hc[row:row + 1], None if hs is None else hs[row:row + 1],
+                                              gh.act_format(w.dtype))[0]
+                y_got = (y[p].astype(np.uint32) << 16).view(np.float32)
+                rh, ry = gh.rel_l2(h_got, h_ref), gh.rel_l2(y_got, y_ref)
+                assert rh <= tol and ry <= tol, (e, row, rh, ry)
+                worst = max(worst, rh, ry)
+        _log(f"{name}: sorted-position rows within tolerance (worst relL2 {worst:.2e})")
     del layer, cw, r, out_fwd, out_fused
     torch.cuda.empty_cache()
