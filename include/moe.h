@@ -253,6 +253,28 @@ MOE_API moe_status moe_forward_fused(const moe_shape* shape, int32_t T, const vo
                                      const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Size of the device scratch array behind moe_forward_noalloc (64 MiB per
+ * device, held until the process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the layer
+ * of moe_forward (same kernels, bitwise the same results) with its
+ * intermediates in a library-owned static device array instead of a caller
+ * workspace.  Nothing is allocated, freed or synchronised.  The intermediates
+ * of T tokens must fit: moe_workspace_bytes of `shape` with max_tokens = T
+ * must not exceed MOE_NOALLOC_SCRATCH_BYTES, else MOE_ERR_WORKSPACE (nothing
+ * enqueued) -- decode-sized batches fit (e.g. T = 128, H = 7168, I = 2048,
+ * top-8 NVFP4 needs ~21 MiB), prefill-sized ones do not.  All calls on one
+ * device share that device's array, which keeps the last call's contents:
+ * calls that may overlap on one device (different streams or host threads
+ * without ordering) race and give undefined results; stream-ordered calls
+ * are safe.  MOE_ERR_LAUNCH if the array's device address cannot be
+ * obtained. */
+MOE_API moe_status moe_forward_noalloc(const moe_shape* shape, int32_t T, const void* packed, const float* logits,
+                                       const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
+                                       hipStream_t stream);
+
 /* Zero the synchronisation words at the start of a workspace (enqueued on
  * `stream`); needed once per workspace before moe_forward_fused. */
 MOE_API moe_status moe_workspace_init(const moe_shape* shape, void* ws, size_t ws_bytes, hipStream_t stream);

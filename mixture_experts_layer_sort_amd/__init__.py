@@ -44,6 +44,7 @@ EXPORTED = [
     "moe_combine",
     "moe_forward",
     "moe_forward_fused",
+    "moe_forward_noalloc",
     "moe_workspace_init",
 ]
 
@@ -100,6 +101,7 @@ def _load():
         "moe_combine": (I32, [S, I32, P, P, P, P]),
         "moe_forward": (I32, [S, I32, P, P, P, P, P, P, P, SZ, P]),
         "moe_forward_fused": (I32, [S, I32, P, P, P, P, P, P, P, SZ, P]),
+        "moe_forward_noalloc": (I32, [S, I32, P, P, P, P, P, P, P]),
         "moe_workspace_init": (I32, [S, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -256,6 +258,12 @@ def moe_forward_fused(shape, T, packed, logits, x, out, ws, ws_bytes=None, topk_
     nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
     _check(_lib.moe_forward_fused(ctypes.byref(shape), T, _ptr(packed), _ptr(logits), _ptr(x), _ptr(out),
                                   _ptr(topk_ids), _ptr(topk_w), _ptr(ws), nbytes, _stream(stream)), "moe_forward_fused")
+
+
+def moe_forward_noalloc(shape, T, packed, logits, x, out, topk_ids=None, topk_w=None, stream=None):
+    """moe_forward with its intermediates in the library's static device scratch (no workspace)."""
+    _check(_lib.moe_forward_noalloc(ctypes.byref(shape), T, _ptr(packed), _ptr(logits), _ptr(x), _ptr(out),
+                                    _ptr(topk_ids), _ptr(topk_w), _stream(stream)), "moe_forward_noalloc")
 
 
 def moe_workspace_init(shape, ws, ws_bytes=None, stream=None):

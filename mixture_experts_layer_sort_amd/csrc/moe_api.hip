@@ -87,6 +87,31 @@ moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LA
 
 }  // namespace
 
+// Device scratch of moe_forward_noalloc: the staged layer's intermediates for
+// callers that cannot allocate.  Each device holds its own copy for the life
+// of the process; in host code only the per-device address from
+// hipGetSymbolAddress is used (the array's name is a host-side stand-in).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<uint8_t*> g_scratch[kMaxDevices];
+
+// Address of this device's scratch array (looked up once per device, with the
+// device current); nullptr if the lookup fails.
+uint8_t* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  uint8_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  g_scratch[dev].store(static_cast<uint8_t*>(q), std::memory_order_release);
+  return static_cast<uint8_t*>(q);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* moe_status_string(int32_t status) {
@@ -261,14 +286,13 @@ static moe_status check_forward(const moe_shape* s, int32_t T, const void* packe
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const float* logits, const uint16_t* x,
-                       uint16_t* out, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
-  moe_status st = check_forward(s, T, packed, logits, x, out, ws, ws_bytes);
-  if (st != MOE_OK || T == 0) return st;
+// The five stage kernels of the layer on `stream`, intermediates in the
+// workspace at `base` laid out for `cap` tokens (cap >= T).
+static moe_status forward_staged(const moe_shape* s, int32_t T, int cap, const void* packed, const float* logits,
+                                 const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w, uint8_t* base,
+                                 hipStream_t stream) {
   const int dt = s->dtype, E = s->num_experts, H = s->hidden, I = s->inter, k = s->top_k;
-  const WorkspaceLayout W = workspace_layout(dt, E, H, I, k, s->max_tokens);
-  uint8_t* base = (uint8_t*)ws;
+  const WorkspaceLayout W = workspace_layout(dt, E, H, I, k, cap);
   int32_t* ids = topk_ids ? topk_ids : (int32_t*)(base + W.ids);
   float* wts = topk_w ? topk_w : (float*)(base + W.wts);
   int32_t* offsets = (int32_t*)(base + W.offsets);
@@ -288,6 +312,28 @@ moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const 
                      gemm_grid(dt, false, T, k, E), stream);
   if (e == hipSuccess) e = launch_combine(T, H, k, y, wts, out, stream);
   return launched(e);
+}
+
+moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const float* logits, const uint16_t* x,
+                       uint16_t* out, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status st = check_forward(s, T, packed, logits, x, out, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  return forward_staged(s, T, s->max_tokens, packed, logits, x, out, topk_ids, topk_w, (uint8_t*)ws, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_shape* s, int32_t T, const void* packed, const float* logits,
+                               const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
+                               hipStream_t stream) {
+  moe_status st = check_T(s, T);
+  if (st != MOE_OK || T == 0) return st;
+  if (!packed || !logits || !x || !out) return MOE_ERR_INVALID_ARG;
+  const size_t need = workspace_layout(s->dtype, s->num_experts, s->hidden, s->inter, s->top_k, T).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  uint8_t* base = scratch_address();
+  if (!base) return MOE_ERR_LAUNCH;
+  // every intermediate is written before it is read: nothing needs clearing
+  return forward_staged(s, T, T, packed, logits, x, out, topk_ids, topk_w, base, stream);
 }
 
 moe_status moe_forward_fused(const moe_shape* s, int32_t T, const void* packed, const float* logits,
