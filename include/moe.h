@@ -170,6 +170,10 @@ MOE_API moe_status moe_nvfp4_fold_global_scale(int32_t count, int32_t rows, int3
  * "Review highlights": the MMA-layout scale conversion is cached at load
  * time; vLLM PR 38050 report, "Implementation": scale conversion and
  * interleave when preparing weights for the CuteDSL kernel].
+ * MOE_MXFP8 layers also get a second copy of the W2 codes in the operand
+ * order of the block-scaled fp8 matrix instruction (32-row x 64-K fragments)
+ * for the down GEMM of prefill-sized batches (moe_packed_weight_bytes
+ * includes it; E * H * I bytes more).
  * Scales / alpha are NULL for BF16; alpha is NULL for MXFP8. */
 MOE_API moe_status moe_prepare_weights(const moe_shape* shape,
                                const void* w13_codes, const void* w13_scales, const float* w13_alpha,
@@ -213,6 +217,10 @@ MOE_API moe_status moe_gemm13_swiglu_quant(const moe_shape* shape, int32_t T, co
 /* Down grouped GEMM: for each expert e and sorted row r of it,
  * y[sorted_pairs[r]] = bf16(W2[e] . hq[r]) (fp32 accumulation, NVFP4 scaled
  * by the W2 alpha).  y is bf16 [T*k, H], row p = t*k + j (slot-major).
+ * MOE_MXFP8 layers with 64 or more routed rows per expert on average run it
+ * on the block-scaled fp8 matrix instruction (e4m3 x e4m3 with the e8m0
+ * block scales applied by the hardware; its 64-product sums carry a relative
+ * error of ~1e-5, far below the bf16 rounding of y).
  * ws / ws_bytes: unused, may be NULL / 0. */
 MOE_API moe_status moe_gemm2(const moe_shape* shape, int32_t T, const void* packed,
                      const int32_t* offsets, const int32_t* sorted_pairs, const void* hq,

@@ -27,19 +27,21 @@ int device_cu_count() {
   return n;
 }
 
-// occupancy of each GEMM variant, per device: [dev][dt][g13][variant]
-std::atomic<int> g_occ[kMaxDevices][3][2][3];
+// occupancy of each GEMM variant, per device: [dev][dt][g13][variant], variant 3 = the fp8 prefill GEMM
+std::atomic<int> g_occ[kMaxDevices][3][2][4];
 
-int gemm_grid(int dt, bool g13, int T, int k, int E) {
-  dt = weight_dt(dt);  // the kernels are those of the weight format
+int gemm_grid(int layer_dt, bool g13, int T, int k, int E) {
+  const int dt = weight_dt(layer_dt);  // the kernels are those of the weight format
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  const int v = gemm_variant(T, k, E);
+  int v = gemm_variant(T, k, E);
+  if (v == 2 && has_fp8_gemm(layer_dt)) v = 3;
   int occ = 1;
   if (dev >= 0 && dev < kMaxDevices) {
     occ = g_occ[dev][dt][g13][v].load(std::memory_order_relaxed);
     if (occ <= 0) {
-      occ = v == 2 ? prefill_blocks_per_cu(dt, g13) : gemm_blocks_per_cu(dt, g13, v + 1);
+      occ = v == 3 ? prefill_f8_blocks_per_cu(g13) : v == 2 ? prefill_blocks_per_cu(dt, g13)
+                                                             : gemm_blocks_per_cu(dt, g13, v + 1);
       g_occ[dev][dt][g13][v].store(occ, std::memory_order_relaxed);
     }
   }
@@ -47,13 +49,13 @@ int gemm_grid(int dt, bool g13, int T, int k, int E) {
 }
 
 // co-resident blocks of the fused kernel, per device: [dev][dt][variant]; -1 = unusable
-std::atomic<int> g_fused_occ[kMaxDevices][3][3];
+std::atomic<int> g_fused_occ[kMaxDevices][3][4];
 
-int fused_grid(int dt, int T, int k, int E) {
-  dt = weight_dt(dt);
+int fused_grid(int layer_dt, int T, int k, int E) {
+  const int dt = weight_dt(layer_dt);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  const int v = gemm_variant(T, k, E);
+  const int v = fused_variant(layer_dt, T, k, E);
   int occ = g_fused_occ[dev][dt][v].load(std::memory_order_relaxed);
   if (occ == 0) {
     occ = fused_blocks_per_cu(dt, v);

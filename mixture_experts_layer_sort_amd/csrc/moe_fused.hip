@@ -21,6 +21,7 @@
 // (garbage output, never a hang).  The last block out resets every
 // synchronisation word to zero for the next launch.
 #include "moe_gemm_item.h"
+#include "moe_prefill_fp8.h"
 #include "moe_prefill_item.h"
 #include "moe_stages.h"
 
@@ -77,18 +78,45 @@ __device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned target) {
 // LDS of one block, reused phase by phase: the permutation's histograms, then
 // the decode items' cross-wave reduction.  (Prefill items keep their token
 // stages in LDS objects of their own.)  V is the GEMM variant: 0 / 1 decode
-// items of 16 / 32 rows, 2 prefill items.
+// items of 16 / 32 rows, 2 prefill items, 3 prefill items of MXFP8 layers on
+// the fp8 matrix instruction.
 template <int V>
 constexpr size_t fused_lds_bytes() {
   constexpr size_t perm = sizeof(int) * permute_lds_ints<kGemmThreads / 64>();
-  constexpr size_t gemm = V == 2 ? 0 : sizeof(f32x4_t) * 3 * 4 * (V + 1) * 64;
+  constexpr size_t gemm = V >= 2 ? 0 : sizeof(f32x4_t) * 3 * 4 * (V + 1) * 64;
   return perm > gemm ? perm : gemm;
 }
 
+// A prefill item of the single-launch kernel (128 rows, one wave per row group).
+template <int DT>
+__device__ __forceinline__ int fused_prefill_item(const GemmArgs& g, bool g13, long long w, const int* cum) {
+  const auto st = pf_make_stages<DT, kPfRows>();
+  return g13 ? prefill_item<DT, true, 1, kPfRows>(g, w, cum, st) : prefill_item<DT, false, 1, kPfRows>(g, w, cum, st);
+}
+
+// An fp8 down item of the single-launch kernel; its token stages reuse the
+// LDS of the prefill items' stages (the two GEMM phases are separated by a
+// grid barrier).
+template <int DT>
+__device__ __forceinline__ int fused_f8_down_item(const GemmArgs& g, long long w, const int* cum) {
+  static_assert(pf_stages<DT, kPfRows>() >= kF8Stages && pf_stage_slots<DT, kPfRows>() >= kF8StageSlots,
+                "fp8 stages fit the prefill stages");
+  const auto st = pf_make_stages<DT, kPfRows>();
+  F8Stages st8;
+  for (int i = 0; i < kF8Stages; ++i) st8.s[i] = reinterpret_cast<u32x4_t(*)[kF8StageSlots]>(st.s[i]);
+  return f8_item<false>(g, w, cum, st8);
+}
+
+// Waves per SIMD the register allocation may fall to: the fp8 items keep 256
+// accumulators per lane and need one wave per SIMD.
+template <int V>
+constexpr int fused_max_waves() { return V == 3 ? 1 : 8; }
+
 template <int DT, int V>
-__global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
-  constexpr int NT = V == 2 ? 1 : V + 1;  // decode items: token sub-tiles of 16
-  constexpr int MT = V == 2 ? kPfRows : kDecodeMT;
+__global__ __launch_bounds__(kGemmThreads)
+void fused_kernel(FusedArgs a) {
+  constexpr int NT = V >= 2 ? 1 : V + 1;  // decode items: token sub-tiles of 16
+  constexpr int MT = V >= 2 ? kPfRows : kDecodeMT;
   __shared__ int cum[1025];
   __shared__ int pcum[V == 0 ? 1025 : 1];
   __shared__ int wsum[4];
@@ -113,12 +141,14 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
 
   // 3. the two grouped GEMMs
   // items per m-tile: one per 64-row weight group (decode) or per 4 groups (prefill)
-  const int per13 = V == 2 ? (a.g13.G + kPfGroups - 1) / kPfGroups : a.g13.G;
-  const int per2 = V == 2 ? (a.g2.G + kPfGroups - 1) / kPfGroups : a.g2.G;
+  const int per13 = V >= 2 ? (a.g13.G + kPfGroups - 1) / kPfGroups : a.g13.G;
+  const int per2 = V >= 2 ? (a.g2.G + kPfGroups - 1) / kPfGroups : a.g2.G;
   auto item = [&](const GemmArgs& g, bool g13, long long w, int e = -1) __attribute__((always_inline)) -> int {
-    if constexpr (V == 2) {
-      const auto st = pf_make_stages<DT, kPfRows>();
-      return g13 ? prefill_item<DT, true, 1, kPfRows>(g, w, cum, st) : prefill_item<DT, false, 1, kPfRows>(g, w, cum, st);
+    if constexpr (V == 3) {
+      // gate/up items on the 16-bit path, down items on the fp8 instruction (256-row m-tiles)
+      return g13 ? fused_prefill_item<DT>(g, true, w, cum) : fused_f8_down_item<DT>(g, w, cum);
+    } else if constexpr (V == 2) {
+      return fused_prefill_item<DT>(g, g13, w, cum);
     } else {
       auto* red = reinterpret_cast<f32x4_t(*)[4 * NT][64]>(smem);
       return g13 ? gemm_item<DT, NT, true>(g, w, cum, red, e) : gemm_item<DT, NT, false>(g, w, cum, red, e);
@@ -126,9 +156,10 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   };
   int total_pairs = 0;
   const int total_mt =
-      V == 2 ? build_schedule(a.offsets, a.E, MT, cum, wsum) : build_decode_schedule<NT>(a.offsets, a.E, cum, pcum, wsum, total_pairs);
-  const long long n13 = (long long)total_mt * per13, n2 = (long long)total_mt * per2;
-  const int lb = V == 2 ? xcd_logical_block() : (int)blockIdx.x;
+      V >= 2 ? build_schedule(a.offsets, a.E, MT, cum, wsum) : build_decode_schedule<NT>(a.offsets, a.E, cum, pcum, wsum, total_pairs);
+  const long long n13 = (long long)total_mt * per13;
+  long long n2 = (long long)total_mt * per2;
+  const int lb = V >= 2 ? xcd_logical_block() : (int)blockIdx.x;
   // decode items: the blocks of a compute unit take turns at the top issue
   // priority, as in the stage kernels (later-placed blocks otherwise lag)
   int turn = (int)(blockIdx.x >> 8);
@@ -137,7 +168,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   auto run_items = [&](const GemmArgs& g, bool g13, long long n) __attribute__((always_inline)) {
     const long long P = (long long)total_pairs * g.G, rp = min(n % (long long)G, n - P);
     for (long long x = lb; x < n; x += G, ++turn) {
-      if constexpr (V != 2) set_wave_priority(turn & 3);
+      if constexpr (V < 2) set_wave_priority(turn & 3);
       if (total_pairs > 0) {
         int e;
         const long long w = decode_item_at(x, rp, P, g, cum, pcum, e);
@@ -149,11 +180,16 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   };
   if constexpr (MOE_FUSED_GEMM_BARRIER) {
     run_items(a.g13, true, n13);
+    if constexpr (V == 3) {  // the fp8 down items' m-tiles of 256 rows
+      __syncthreads();
+      n2 = (long long)build_schedule(a.offsets, a.E, kF8Rows, cum, wsum) * per2;
+    }
     grid_barrier(a.sync, 3 * G);
     run_items(a.g2, false, n2);
     set_wave_priority(0);
     grid_barrier(a.sync, 4 * G);
   } else {
+    static_assert(V != 3, "the fp8 down items need the grid barrier between the GEMMs");
     for (long long w = lb; w < n13 + n2; w += G) {
       if (w < n13) {
         const int e = item(a.g13, true, w);
@@ -184,6 +220,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_kernel(FusedArgs a) {
   }
 }
 
+
 __global__ void zero_u32_kernel(unsigned* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
 }
@@ -192,6 +229,7 @@ template <int DT>
 static const void* fused_fn(int v) {
   if (v == 0) return reinterpret_cast<const void*>(fused_kernel<DT, 0>);
   if (v == 1) return reinterpret_cast<const void*>(fused_kernel<DT, 1>);
+  if (v == 3) return reinterpret_cast<const void*>(fused_kernel<DT_MXFP8, 3>);
   return reinterpret_cast<const void*>(fused_kernel<DT, 2>);
 }
 
@@ -261,10 +299,16 @@ hipError_t launch_fused(int dt, bool gated, int E, int H, int I, int k, int T, c
   h.act_bf16 = dt == DT_BF16_MXFP8;
   h.gated = gated;
   h.E = E; h.K = I; h.G = L.G2; h.KG = L.KG2; h.k = k; h.n_out = H;
+  g.act_scales = h.act_scales = nullptr;
+  const int v = fused_variant(dt, T, k, E);
+  if (v == 3) {  // the fp8 down items: fragment-order weights, e4m3 hq codes and e8m0 scales
+    h.wcodes = packed + L.w2_frag;
+    h.act = hq;
+    h.act_scales = hq + act_scale_offset(dt, T * k, I);
+  }
   (void)ws_bytes;
   void* args[] = {&f};
-  return hipLaunchCooperativeKernel(fused_ptr(weight_dt(dt), gemm_variant(T, k, E)), dim3(grid), dim3(kGemmThreads), args, 0,
-                                    s);
+  return hipLaunchCooperativeKernel(fused_ptr(weight_dt(dt), v), dim3(grid), dim3(kGemmThreads), args, 0, s);
 }
 
 hipError_t launch_zero_sync(uint8_t* ws, int dt, int E, int H, int I, int k, int max_tokens, hipStream_t s) {

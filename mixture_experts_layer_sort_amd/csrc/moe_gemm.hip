@@ -109,6 +109,29 @@ __global__ void prepare_kernel(const uint8_t* __restrict__ src, const uint8_t* _
   }
 }
 
+// MXFP8 codes in the fp8 fragment order (see moe_layout.h): one thread per
+// 16-byte unit (expert, row group, 64-K step, fragment, half, lane).  Used for
+// W2 (w13 = 0); the SwiGLU W13 order (w13 = 1) is kept for completeness.
+__global__ void prepare_frag_kernel(const uint8_t* __restrict__ src, int E, int R, int K, int G, int I, int w13,
+                                    uint8_t* __restrict__ dst) {
+  const int KS = K / 64;
+  const long long n = (long long)E * G * KS * 4 * 64;
+  for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < n;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int l = (int)(idx & 63), q = (int)((idx >> 6) & 1), f = (int)((idx >> 7) & 1);
+    long long rest = idx >> 8;
+    const int s = (int)(rest % KS);
+    rest /= KS;
+    const int g = (int)(rest % G);
+    const int e = (int)(rest / G);
+    const int m = l & 31, h = l >> 5;
+    // group row 32 f + m: gate rows then the matching up rows (SwiGLU W13), else 64 consecutive rows
+    const int row = w13 ? (f == 0 ? 32 * g + m : I + 32 * g + m) : 64 * g + 32 * f + m;
+    *reinterpret_cast<uint4*>(dst + idx * 16) =
+        *reinterpret_cast<const uint4*>(src + ((size_t)e * R + row) * K + 64 * s + 32 * q + 16 * h);
+  }
+}
+
 __global__ void copy_f32_kernel(const float* __restrict__ s, float* __restrict__ d, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) d[i] = s[i];
@@ -166,6 +189,7 @@ hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, 
   a.out = hq;
   a.out_scales = hq + act_scale_offset(dt, T * k, I);
   a.out_deq = reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
+  a.act_scales = nullptr;
   a.act_bf16 = dt == DT_BF16_MXFP8;
   a.gated = gated;
   a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
@@ -187,9 +211,16 @@ hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, c
   a.out = reinterpret_cast<uint8_t*>(y);
   a.out_scales = nullptr;
   a.out_deq = nullptr;
+  a.act_scales = nullptr;
   a.act_bf16 = dt == DT_BF16_MXFP8;
   a.gated = gated;
   a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
+  if (gemm_prefill(T, k, E) && has_fp8_gemm(dt)) {
+    a.wcodes = packed + L.w2_frag;
+    a.act = hq;  // e4m3 codes
+    a.act_scales = hq + act_scale_offset(dt, T * k, I);
+    return launch_prefill_f8(false, a, grid, s);
+  }
   if (gemm_prefill(T, k, E)) return launch_prefill(weight_dt(dt), false, a, grid, s);
   return dispatch_gemm<false>(weight_dt(dt), gemm_nt(T, k, E), a, grid, s);
 }
@@ -198,6 +229,7 @@ hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t
                           const float* w13a, const uint8_t* w2, const uint8_t* w2s, const float* w2a, uint8_t* packed,
                           hipStream_t s) {
   const PackedLayout L = packed_layout(dt, E, H, I, gated);
+  const int layer_dt = dt;
   const int threads = 256;
   auto blocks = [&](long long n) { return (int)std::min((n + threads - 1) / threads, 1LL << 20); };
   long long n13 = (long long)E * L.G13 * L.KG13 * 4 * 64, n2 = (long long)E * L.G2 * L.KG2 * 4 * 64;
@@ -217,6 +249,11 @@ hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t
                        reinterpret_cast<float*>(packed + L.w2_alpha), E);
   }
 #undef MOE_PREP
+  if (has_fp8_gemm(layer_dt)) {
+    const long long f2 = (long long)E * L.G2 * (I / 64) * 256;
+    hipLaunchKernelGGL(prepare_frag_kernel, dim3(blocks(f2)), dim3(threads), 0, s, w2, E, H, I, L.G2, I, 0,
+                       packed + L.w2_frag);
+  }
   return hipGetLastError();
 }
 

@@ -14,7 +14,9 @@ struct GemmArgs {
   const float* walpha;
   const int* offsets;
   const int* sorted_pairs;
-  const uint8_t* act;         // B operand rows, 16-bit: xq (gemm13, row = token) or hq (gemm2, row = sorted row)
+  const uint8_t* act;         // B operand rows, 16-bit: xq (gemm13, row = token) or hq (gemm2, row = sorted row);
+                              // the fp8 prefill GEMM: their e4m3 codes
+  const uint8_t* act_scales;  // the fp8 prefill GEMM: the e8m0 scales of those rows
   uint8_t* out;               // hq codes (gemm13) or y (gemm2)
   uint8_t* out_scales;        // hq scales (gemm13)
   uint16_t* out_deq;          // hq dequantised 16-bit copy (gemm13; MXFP8, NVFP4)
@@ -574,5 +576,8 @@ __device__ __forceinline__ int build_decode_schedule(const int* __restrict__ off
 }
 
 hipError_t launch_prefill(int dt, bool g13, const GemmArgs& a, int grid, hipStream_t s);
+// MXFP8 layers: the prefill-shaped down GEMM on the fp8 matrix instruction (a.wcodes: fragment
+// region, a.act / a.act_scales: e4m3 codes / e8m0 scales of the hq rows); g13 must be false
+hipError_t launch_prefill_f8(bool g13, const GemmArgs& a, int grid, hipStream_t s);
 
 }  // namespace moe

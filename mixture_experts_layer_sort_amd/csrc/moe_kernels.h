@@ -49,7 +49,14 @@ inline int gemm_nt(int T, int k, int E) { return (long long)T * k > 16LL * E ? 2
 inline bool gemm_prefill(int T, int k, int E) { return (long long)T * k >= 64LL * E; }
 // GEMM variant index for caches: 0 decode NT=1, 1 decode NT=2, 2 prefill.
 inline int gemm_variant(int T, int k, int E) { return gemm_prefill(T, k, E) ? 2 : gemm_nt(T, k, E) - 1; }
+// GEMM variant of the single-launch kernel (layer format dt): as gemm_variant,
+// and 3 for the prefill-shaped GEMMs of MXFP8 layers (fp8 matrix instruction).
+inline int fused_variant(int dt, int T, int k, int E) {
+  const int v = gemm_variant(T, k, E);
+  return v == 2 && has_fp8_gemm(dt) ? 3 : v;
+}
 int prefill_blocks_per_cu(int dt, bool g13);
+int prefill_f8_blocks_per_cu(bool g13);
 
 // The whole layer in one cooperative launch; `grid` must not exceed the
 // co-resident capacity (fused_blocks_per_cu * compute units).
@@ -57,7 +64,7 @@ hipError_t launch_fused(int dt, bool gated, int E, int H, int I, int k, int T, c
                         const float* logits,
                         const uint16_t* x, uint16_t* out, int* ids, float* wts, uint8_t* ws, size_t ws_bytes,
                         int max_tokens, int grid, hipStream_t s);
-int fused_blocks_per_cu(int dt, int variant);  // variant as gemm_variant
+int fused_blocks_per_cu(int dt, int variant);  // variant as fused_variant
 // Zero the workspace's synchronisation words.
 hipError_t launch_zero_sync(uint8_t* ws, int dt, int E, int H, int I, int k, int max_tokens, hipStream_t s);
 

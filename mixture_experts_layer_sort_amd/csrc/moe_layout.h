@@ -16,6 +16,13 @@
 //         [lane][4 chunks x 4 B] of e2m1 nibbles, lane (i,q) of chunk c holds
 //         k = 32c + 8q .. +8; scales [row i][8 e4m3 bytes] in K order, lane
 //         (i,q) of chunk c uses byte 2c + q/2            (1024 B + 128 B)
+// MXFP8 layers (not bf16 x MXFP8) also hold their W2 codes in fragment order
+// for the prefill-shaped down GEMM on the block-scaled fp8 matrix
+// instruction: per (expert, row group of 64, 64-wide K step) 4 KB =
+// [fragment f<2 (group rows 32f..32f+32)][half q<2][lane 64][16 B], lane
+// l = m + 32h holding row m's K bytes 64s + 32q + 16h .. +16 (the
+// instruction's operand order); that GEMM reads the scales of the tile region
+// above.
 // Row groups: W13 group g = gate rows 32g..32g+32 (tiles 0,1) and up rows
 // I+32g..I+32g+32 (tiles 2,3), so SwiGLU pairs sit in the same lanes;
 // W2 group g = rows 64g..64g+64 (tiles 0..3).  Block (e, g, kgroup) holds its
@@ -69,8 +76,15 @@ MOE_HD size_t row_scale_bytes(int dt, int K) {
 
 struct PackedLayout {
   int G13, KG13, G2, KG2;
-  size_t w13_codes, w13_scales, w2_codes, w2_scales, w13_alpha, w2_alpha, total;
+  size_t w13_codes, w13_scales, w2_codes, w2_scales, w13_alpha, w2_alpha, w2_frag, total;
 };
+
+// The layer formats whose prefill-shaped down GEMM runs on the fp8 matrix
+// instruction (its output is not requantised: the instruction's ~1e-5
+// relative accumulation error stays far below the bf16 rounding of y; the
+// gate/up GEMM keeps exact products with fp32 accumulation, as its
+// requantised output turns such errors into code flips).
+MOE_HD bool has_fp8_gemm(int dt) { return dt == DT_MXFP8; }
 
 // gated: SwiGLU experts, W13 row group g = 32 gate rows + the matching 32 up
 // rows; otherwise (ReLU^2) W1 of I rows in groups of 64.
@@ -89,6 +103,7 @@ MOE_HD PackedLayout packed_layout(int dt, int E, int H, int I, bool gated = true
   L.w2_scales = off; off = align256(off + n2 * tile_scale_bytes(dt));
   L.w13_alpha = off; off = align256(off + (weight_dt(dt) == DT_NVFP4 ? (size_t)E * 4 : 0));
   L.w2_alpha = off; off = align256(off + (weight_dt(dt) == DT_NVFP4 ? (size_t)E * 4 : 0));
+  L.w2_frag = off; off = align256(off + (has_fp8_gemm(dt) ? n2 * tile_code_bytes(dt) : 0));
   L.total = off;
   return L;
 }

@@ -5,6 +5,7 @@
 // The grid is persistent, derives the item map from `offsets` on the device
 // and walks items in XCD-contiguous order.  The epilogue (SwiGLU +
 // requantisation, or y rows) is the decode kernel's.
+#include "moe_prefill_fp8.h"
 #include "moe_prefill_item.h"
 
 namespace moe {
@@ -39,6 +40,34 @@ static const void* prefill_ptr(int dt, bool g13) {
   if (dt == DT_BF16) return g13 ? prefill_fn<DT_BF16, true>() : prefill_fn<DT_BF16, false>();
   if (dt == DT_MXFP8) return g13 ? prefill_fn<DT_MXFP8, true>() : prefill_fn<DT_MXFP8, false>();
   return g13 ? prefill_fn<DT_NVFP4, true>() : prefill_fn<DT_NVFP4, false>();
+}
+
+// MXFP8 layers: one 4-wave block per compute unit (256 accumulators per lane)
+template <bool G13>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_f8_kernel(GemmArgs a) {
+  __shared__ int cum[1025];
+  __shared__ int wsum[4];
+  const F8Stages st = f8_make_stages();
+  const int total_mt = build_schedule(a.offsets, a.E, kF8Rows, cum, wsum);
+  const long long total = (long long)total_mt * ((a.G + kPfGroups - 1) / kPfGroups);
+  for (long long w = xcd_logical_block(); w < total; w += gridDim.x) f8_item<G13>(a, w, cum, st);
+}
+
+static const void* prefill_f8_ptr(bool g13) {
+  (void)g13;  // the down GEMM only
+  return reinterpret_cast<const void*>(gemm_f8_kernel<false>);
+}
+
+int prefill_f8_blocks_per_cu(bool g13) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_f8_ptr(g13), kGemmThreads, 0) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+
+hipError_t launch_prefill_f8(bool g13, const GemmArgs& a, int grid, hipStream_t s) {
+  void* args[] = {const_cast<GemmArgs*>(&a)};
+  return hipLaunchKernel(prefill_f8_ptr(g13), dim3(grid), dim3(kGemmThreads), args, 0, s);
 }
 
 int prefill_blocks_per_cu(int dt, bool g13) {

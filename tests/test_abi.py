@@ -59,7 +59,10 @@ def test_sizes_match_layouts():
     assert lib.moe_packed_weight_bytes(s) == 64 * 3 * 4096 * 1408 * 2
     s = S(7168, 2048, 256, 8, 8192, "mxfp8")
     canon = 256 * 3 * 7168 * 2048
-    assert lib.moe_packed_weight_bytes(s) == canon + canon // 32
+    # MXFP8 layers also hold W2's codes in the fp8 instruction's fragment order
+    assert lib.moe_packed_weight_bytes(s) == canon + canon // 32 + 256 * 7168 * 2048
+    # bf16 activations over MXFP8 weights: no fragment copy
+    assert lib.moe_packed_weight_bytes(S(7168, 2048, 256, 8, 8192, "bf16_mxfp8")) == canon + canon // 32
     s = S(7168, 2048, 384, 8, 128, "nvfp4")
     canon = 384 * 3 * 7168 * 2048
     assert lib.moe_packed_weight_bytes(s) == canon // 2 + canon // 16 + 2 * 1536  # + alpha regions (256-aligned)
@@ -78,12 +81,13 @@ def test_sizes_match_layouts():
     assert lib.moe_packed_weight_bytes(s) == 64 * 2 * 4096 * 1408 * 2
     s = S(7168, 2048, 256, 8, 8192, "mxfp8", "relu2")
     canon = 256 * 2 * 7168 * 2048
-    assert lib.moe_packed_weight_bytes(s) == canon + canon // 32
+    assert lib.moe_packed_weight_bytes(s) == canon + canon // 32 + 256 * 7168 * 2048
     assert lib.moe_workspace_bytes(s) == lib.moe_workspace_bytes(S(7168, 2048, 256, 8, 8192, "mxfp8"))
     # bf16 activations over MXFP8 weights: the weights of MXFP8, the activations of BF16
     for shape in [(7168, 2048, 256, 8, 8192), (512, 256, 8, 4, 64)]:
         a, m, b = S(*shape, "bf16_mxfp8"), S(*shape, "mxfp8"), S(*shape, "bf16")
-        assert lib.moe_packed_weight_bytes(a) == lib.moe_packed_weight_bytes(m)
+        # (the MXFP8 layer adds W2's fp8 fragment copy)
+        assert lib.moe_packed_weight_bytes(a) == lib.moe_packed_weight_bytes(m) - shape[2] * shape[0] * shape[1]
         for f in (lib.moe_xq_bytes, lib.moe_xq_scale_offset, lib.moe_hq_bytes, lib.moe_hq_scale_offset):
             assert f(a, T) == f(b, T), f
         assert lib.moe_workspace_bytes(a) == lib.moe_workspace_bytes(b)
