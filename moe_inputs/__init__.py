@@ -54,6 +54,7 @@ class Workload:
     cid: int        # seed id of the workload
     act: str = "swiglu"  # "swiglu" (gated, W13 of 2I rows) | "relu2" (non-gated, W1 of I rows)
     fold: bool = False   # NVFP4: weight alpha folded into the block scales after quantisation
+    limit: float = 0.0   # gate/up clamp of SwiGLU experts (0: none)
 
     @property
     def R13(self) -> int:
@@ -89,6 +90,9 @@ WORKLOADS = {
         Workload("relu2_nvfp4_decode_t128", 128, 7168, 2048, 384, 8, "nvfp4", "none", 4, "relu2"),
         # NVFP4 weights with the per-tensor alpha folded into the block scales (same masters)
         Workload("nvfp4_folded_decode_t128", 128, 7168, 2048, 384, 8, "nvfp4", "none", 4, "swiglu", True),
+        # SwiGLU experts with a gate/up clamp at 1.0 (gate and up values have a
+        # standard deviation of ~1.7 at this shape, so about half are clamped)
+        Workload("clamp_mxfp8_decode", 32, 7168, 2048, 256, 8, "mxfp8", "normal2", 3, "swiglu", False, 1.0),
     ]
 }
 

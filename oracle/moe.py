@@ -30,6 +30,12 @@ Readings where the pages are silent (all documented with the design):
    experts, such as Nemotron, are rejected by the b12x backend [vLLM PR 40082
    report, "Risks" item 4]): W1 = W13 holds I rows and h = relu(W1 x)^2,
    requantised like the SwiGLU intermediate; the rest of the layer is the same.
+9. Gate/up clamp (the pages name a resolve_gate_up_clamp step of the kernels'
+   adaptation layer and give no value or rule [MegaMoE drop workflow, §2, the
+   shim/comm.py entry]): an optional limit L > 0 of the SwiGLU experts, applied
+   to the fp32 products before the activation, gate = min(gate, L) and
+   up = clamp(up, -L, L) (the gate bounded from above only, since silu of a
+   very negative gate already vanishes); L = 0 means no clamp.
 
 Arithmetic: dequantised operands are exact in float64, dot products and the
 SwiGLU are evaluated in float64, and rounding to fp32 happens only where the
@@ -128,6 +134,7 @@ class Weights:
     w13_a: object = None
     w2_a: object = None
     act: str = "swiglu"
+    limit: float = 0.0  # gate/up clamp of SwiGLU experts (0: none)
 
     def dequant(self, e: int):
         """Exact float64 dequantised (W13 [2I, H], W2 [H, I]) of expert e."""
@@ -140,9 +147,11 @@ class Weights:
         return w13, w2
 
 
-def quantize_weights(w13_f32: dict, w2_f32: dict, dtype: str, act: str = "swiglu", fold: bool = False) -> Weights:
+def quantize_weights(w13_f32: dict, w2_f32: dict, dtype: str, act: str = "swiglu", fold: bool = False,
+                     limit: float = 0.0) -> Weights:
     """Quantise fp32 master weights {e: array} into canonical form (harness).
-    fold (NVFP4): then fold each tensor's alpha into its block scales."""
+    fold (NVFP4): then fold each tensor's alpha into its block scales.
+    limit: the experts' gate/up clamp (0: none)."""
     out = {k: {} for k in ("w13", "w13_s", "w13_a", "w2", "w2_s", "w2_a")}
     wf = weight_format(dtype)
     for e in w13_f32:
@@ -157,15 +166,20 @@ def quantize_weights(w13_f32: dict, w2_f32: dict, dtype: str, act: str = "swiglu
             out[n] = None
     if wf == "mxfp8":
         out["w13_a"] = out["w2_a"] = None
-    return Weights(dtype=dtype, act=act, **out)
+    return Weights(dtype=dtype, act=act, limit=float(limit), **out)
 
 
 # ------------------------------------------------------------------ the layer
 
 
-def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+def silu_mul(g: np.ndarray, u: np.ndarray, limit: float = 0.0) -> np.ndarray:
     """SwiGLU activation silu(g) * u (act_and_mul) [vLLM PR 40082 report,
-    "Implementation" item 1; "Risks" item 4: only gated act-and-mul MLPs]."""
+    "Implementation" item 1; "Risks" item 4: only gated act-and-mul MLPs],
+    after the optional gate/up clamp (reading 9): with limit L > 0 the gate is
+    min(g, L) and the up value is clamped to [-L, L]."""
+    if limit > 0:
+        g = np.minimum(g, limit)
+        u = np.clip(u, -limit, limit)
     with np.errstate(over="ignore"):
         return g / (1.0 + np.exp(-g)) * u
 
@@ -197,7 +211,7 @@ def quantize_x(x_bits: np.ndarray, dtype: str):
     return c, s, quant.dequantize_act(c, s, dtype)
 
 
-def expert_mlp(xh: np.ndarray, w13: np.ndarray, w2: np.ndarray, act: str, dtype: str):
+def expert_mlp(xh: np.ndarray, w13: np.ndarray, w2: np.ndarray, act: str, dtype: str, limit: float = 0.0):
     """One routed pair through its expert: xh the dequantised activation row
     (float64 [H]), w13 / w2 the expert's dequantised weights.  Gate/up product,
     SwiGLU (or squared ReLU), requantisation of the intermediate in the layer
@@ -207,7 +221,7 @@ def expert_mlp(xh: np.ndarray, w13: np.ndarray, w2: np.ndarray, act: str, dtype:
         h = relu2(w13 @ xh)
     else:
         I = w13.shape[0] // 2
-        h = silu_mul(w13[:I] @ xh, w13[I:] @ xh)
+        h = silu_mul(w13[:I] @ xh, w13[I:] @ xh, limit)
     hc, hsc, hh = requant_h(h[None, :], dtype)
     y = w2 @ hh[0]
     return (hc[0], None if hsc is None else hsc[0], hh[0]), y
@@ -246,7 +260,7 @@ def moe_layer(x_bits, logits, W: Weights, k: int, tokens=None, keep=False) -> La
             if e not in cache:
                 cache[e] = W.dequant(e)
             w13, w2 = cache[e]
-            hq, y = expert_mlp(xh, w13, w2, W.act, W.dtype)
+            hq, y = expert_mlp(xh, w13, w2, W.act, W.dtype, W.limit)
             acc += wts[t, j] * y
             if keep:
                 ys[(t, j)] = y
@@ -284,7 +298,7 @@ def moe_layer_grouped(x_bits, logits, W: Weights, k: int, acc_dtype=np.float64):
             I = w13.shape[0] // 2
             G = X @ w13[:I].T.astype(acc_dtype)
             U = X @ w13[I:].T.astype(acc_dtype)
-            Hm = silu_mul(G.astype(np.float64), U.astype(np.float64))
+            Hm = silu_mul(G.astype(np.float64), U.astype(np.float64), W.limit)
         _, _, hh = requant_h(Hm, W.dtype)
         y[pairs] = hh.astype(acc_dtype) @ w2.T.astype(acc_dtype)
     y = y.reshape(T, k, H)
