@@ -128,7 +128,7 @@ class Layer:
                 lib.moe_nvfp4_fold_global_scale(1, H, I, sub(s2, e), sub(a2, e))
             del m13, m2
         self.w = w
-        self.shape = lib.make_shape(H, I, E, w.k, w.T, w.dtype, w.act)
+        self.shape = lib.make_shape(H, I, E, w.k, w.T, w.dtype, w.act, w.limit)
         self.packed = torch.empty(lib.moe_packed_weight_bytes(self.shape), dtype=u8, device=device)
         lib.moe_prepare_weights(self.shape, c13, s13, a13, c2, s2, a2, self.packed)
         self.ws = torch.empty(lib.moe_workspace_bytes(self.shape), dtype=u8, device=device)
@@ -294,7 +294,8 @@ def cpu_baseline(w, device, ids, max_experts=12, max_tokens=1024):
             full[n][e] = v
     Wo = omoe.Weights(w.dtype, full["w13"], full["w2"], full["w13_s"] or None, full["w2_s"] or None,
                       full["w13_a"] if all(v is not None for v in full["w13_a"].values()) else None,
-                      full["w2_a"] if all(v is not None for v in full["w2_a"].values()) else None, act=w.act)
+                      full["w2_a"] if all(v is not None for v in full["w2_a"].values()) else None, act=w.act,
+                      limit=w.limit)
     if Wo.w13_s is not None and any(v is None for v in Wo.w13_s.values()):
         Wo.w13_s = Wo.w2_s = None
     # route on the sampled tokens' logits; the grouped form dequantises each routed expert once

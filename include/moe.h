@@ -88,7 +88,12 @@ typedef enum {
 /* Layer shape.  Supported: hidden % 128 == 0, inter % 128 == 0,
  * 1 <= num_experts <= 1024, 1 <= top_k <= min(num_experts, 32),
  * 1 <= max_tokens and max_tokens * top_k <= 2^24, dtype a moe_dtype,
- * activation a moe_activation. */
+ * activation a moe_activation, gate_up_limit finite and >= 0 (0 with
+ * MOE_RELU2 experts).
+ * gate_up_limit: the SwiGLU experts' gate/up clamp L (the pages name a
+ * resolve_gate_up_clamp step and no rule [MegaMoE drop workflow, §2, the
+ * adaptation layer's comm.py]; reading: before the activation the gate is
+ * min(gate, L) and the up value clamp(up, -L, L)); 0 = no clamp. */
 typedef struct {
   int32_t hidden;      /* H */
   int32_t inter;       /* I, per expert */
@@ -97,6 +102,7 @@ typedef struct {
   int32_t max_tokens;  /* workspace capacity in tokens */
   int32_t dtype;       /* moe_dtype of weights and activations */
   int32_t activation;  /* moe_activation of the experts */
+  float gate_up_limit; /* gate/up clamp L of SwiGLU experts, 0 = none */
 } moe_shape;
 
 /* Text of a status code (static storage). */
@@ -208,7 +214,8 @@ MOE_API moe_status moe_permute(const moe_shape* shape, int32_t T, const int32_t*
  * dynamic per-block quantisation with global scale 1].
  * For each expert e and sorted row r in [offsets[e], offsets[e+1]):
  *   g, u = W13[e] . xq[sorted_pairs[r] / k]  (fp32 accumulation; NVFP4 scaled
- *   by the W13 alpha), h = silu(g) * u, hq[r] = requant(h) (layout of
+ *   by the W13 alpha; with gate_up_limit L > 0: g = min(g, L),
+ *   u = clamp(u, -L, L)), h = silu(g) * u, hq[r] = requant(h) (layout of
  *   moe_hq_bytes).  MOE_RELU2: g = W1[e] . xq[...], h = relu(g)^2.  ws / ws_bytes: unused, may be NULL / 0. */
 MOE_API moe_status moe_gemm13_swiglu_quant(const moe_shape* shape, int32_t T, const void* packed,
                                    const int32_t* offsets, const int32_t* sorted_pairs, const void* xq,

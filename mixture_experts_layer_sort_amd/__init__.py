@@ -62,17 +62,20 @@ class moe_shape(ctypes.Structure):
         ("max_tokens", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("activation", ctypes.c_int32),
+        ("gate_up_limit", ctypes.c_float),
     ]
 
     def __repr__(self):
         return (f"moe_shape(H={self.hidden}, I={self.inter}, E={self.num_experts}, k={self.top_k}, "
-                f"max_tokens={self.max_tokens}, dtype={self.dtype}, activation={self.activation})")
+                f"max_tokens={self.max_tokens}, dtype={self.dtype}, activation={self.activation}, "
+                f"gate_up_limit={self.gate_up_limit})")
 
 
-def make_shape(hidden, inter, num_experts, top_k, max_tokens, dtype, activation="swiglu") -> moe_shape:
+def make_shape(hidden, inter, num_experts, top_k, max_tokens, dtype, activation="swiglu",
+               gate_up_limit=0.0) -> moe_shape:
     d = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     a = ACTIVATIONS[activation] if isinstance(activation, str) else int(activation)
-    return moe_shape(hidden, inter, num_experts, top_k, max_tokens, d, a)
+    return moe_shape(hidden, inter, num_experts, top_k, max_tokens, d, a, gate_up_limit)
 
 
 def _load():

@@ -75,6 +75,8 @@ moe_status check_shape(const moe_shape* s) {
   if (s->top_k < 1 || s->top_k > 32 || s->top_k > s->num_experts) return MOE_ERR_UNSUPPORTED;
   if (s->max_tokens < 1 || (long long)s->max_tokens * s->top_k > (1LL << 24)) return MOE_ERR_UNSUPPORTED;
   if (s->activation != MOE_SWIGLU && s->activation != MOE_RELU2) return MOE_ERR_UNSUPPORTED;
+  if (!(s->gate_up_limit >= 0.f) || s->gate_up_limit > 3.0e38f) return MOE_ERR_INVALID_ARG;  // NaN, < 0, inf
+  if (s->activation == MOE_RELU2 && s->gate_up_limit != 0.f) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -251,7 +253,7 @@ moe_status moe_gemm13_swiglu_quant(const moe_shape* s, int32_t T, const void* pa
   if (!packed || !offsets || !sorted_pairs || !xq || !hq) return MOE_ERR_INVALID_ARG;
   return launched(launch_gemm13(s->dtype, gated(s), s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
                                 offsets, sorted_pairs, (const uint8_t*)xq, (uint8_t*)hq,
-                                gemm_grid(s->dtype, true, T, s->top_k, s->num_experts), stream));
+                                gemm_grid(s->dtype, true, T, s->top_k, s->num_experts), stream, s->gate_up_limit));
 }
 
 moe_status moe_gemm2(const moe_shape* s, int32_t T, const void* packed, const int32_t* offsets,
@@ -308,7 +310,7 @@ static moe_status forward_staged(const moe_shape* s, int32_t T, int cap, const v
     e = launch_permute(dt, ids, T, k, E, H, offsets, sorted_pairs, pair_pos, x, xq, stream);
   if (e == hipSuccess)
     e = launch_gemm13(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, xq, hq,
-                      gemm_grid(dt, true, T, k, E), stream);
+                      gemm_grid(dt, true, T, k, E), stream, s->gate_up_limit);
   if (e == hipSuccess)
     e = launch_gemm2(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, hq, y,
                      gemm_grid(dt, false, T, k, E), stream);
@@ -351,7 +353,7 @@ moe_status moe_forward_fused(const moe_shape* s, int32_t T, const void* packed, 
   const int grid = fused_grid(dt, T, k, E);
   if (grid <= 0) return MOE_ERR_UNSUPPORTED;
   return launched(launch_fused(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, logits, x, out, ids, wts, base, ws_bytes,
-                               s->max_tokens, grid, stream));
+                               s->max_tokens, grid, stream, s->gate_up_limit));
 }
 
 }  // extern "C"

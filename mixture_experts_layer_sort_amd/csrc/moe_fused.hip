@@ -248,7 +248,7 @@ int fused_blocks_per_cu(int dt, int v) {
 
 hipError_t launch_fused(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
                         const float* logits, const uint16_t* x, uint16_t* out, int* ids, float* wts, uint8_t* ws,
-                        size_t ws_bytes, int max_tokens, int grid, hipStream_t s) {
+                        size_t ws_bytes, int max_tokens, int grid, hipStream_t s, float limit) {
   const WorkspaceLayout W = workspace_layout(dt, E, H, I, k, max_tokens);
   const PackedLayout L = packed_layout(dt, E, H, I, gated);
   FusedArgs f;
@@ -300,6 +300,8 @@ hipError_t launch_fused(int dt, bool gated, int E, int H, int I, int k, int T, c
   h.gated = gated;
   h.E = E; h.K = I; h.G = L.G2; h.KG = L.KG2; h.k = k; h.n_out = H;
   g.act_scales = h.act_scales = nullptr;
+  g.limit = gated ? limit : 0.f;
+  h.limit = 0.f;
   const int v = fused_variant(dt, T, k, E);
   if (v == 3) {  // the fp8 down items: fragment-order weights, e4m3 hq codes and e8m0 scales
     h.wcodes = packed + L.w2_frag;

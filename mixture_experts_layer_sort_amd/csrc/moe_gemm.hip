@@ -177,7 +177,7 @@ int gemm_blocks_per_cu(int dt, bool g13, int nt) {
 
 hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
                          const int* offsets, const int* sorted_pairs, const uint8_t* xq, uint8_t* hq, int grid,
-                         hipStream_t s) {
+                         hipStream_t s, float limit) {
   const PackedLayout L = packed_layout(dt, E, H, I, gated);
   GemmArgs a;
   a.wcodes = packed + L.w13_codes;
@@ -192,6 +192,7 @@ hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, 
   a.act_scales = nullptr;
   a.act_bf16 = dt == DT_BF16_MXFP8;
   a.gated = gated;
+  a.limit = gated ? limit : 0.f;
   a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
   if (gemm_prefill(T, k, E)) return launch_prefill(weight_dt(dt), true, a, grid, s);
   return dispatch_gemm<true>(weight_dt(dt), gemm_nt(T, k, E), a, grid, s);
@@ -214,6 +215,7 @@ hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, c
   a.act_scales = nullptr;
   a.act_bf16 = dt == DT_BF16_MXFP8;
   a.gated = gated;
+  a.limit = 0.f;
   a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
   if (gemm_prefill(T, k, E) && has_fp8_gemm(dt)) {
     a.wcodes = packed + L.w2_frag;

@@ -22,6 +22,7 @@ struct GemmArgs {
   uint16_t* out_deq;          // hq dequantised 16-bit copy (gemm13; MXFP8, NVFP4)
   int act_bf16;               // MXFP8 weights with bf16 activations: the intermediate is rounded to bf16
   int gated;                  // gate/up GEMM: 1 SwiGLU (gate/up row pairs), 0 ReLU^2 (64 W1 rows per group)
+  float limit;                // SwiGLU gate/up clamp L (0: none): gate = min(gate, L), up = clamp(up, -L, L)
   int E, K, G, KG, k, n_out;
 };
 
@@ -367,7 +368,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if (a.gated) {
-              const float gv = acc[tp][s][j] * alpha, uv = acc[2 + tp][s][j] * alpha;
+              float gv = acc[tp][s][j] * alpha, uv = acc[2 + tp][s][j] * alpha;
+              if (a.limit > 0.f) {
+                gv = fminf(gv, a.limit);
+                uv = fminf(fmaxf(uv, -a.limit), a.limit);
+              }
               // silu with the hardware exp and reciprocal (~1 ulp each): h is requantised
               // to at most 8 significant bits, so a code moves only within a few ulps of a midpoint
               h[tp][j] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;

@@ -30,7 +30,7 @@ hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t
 // Grouped GEMMs.  `grid` is the persistent grid size (blocks).
 hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
                          const int* offsets, const int* sorted_pairs, const uint8_t* xq, uint8_t* hq, int grid,
-                         hipStream_t s);
+                         hipStream_t s, float limit = 0.f);
 
 hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
                         const int* offsets, const int* sorted_pairs, const uint8_t* hq, uint16_t* y, int grid,
@@ -63,7 +63,7 @@ int prefill_f8_blocks_per_cu(bool g13);
 hipError_t launch_fused(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
                         const float* logits,
                         const uint16_t* x, uint16_t* out, int* ids, float* wts, uint8_t* ws, size_t ws_bytes,
-                        int max_tokens, int grid, hipStream_t s);
+                        int max_tokens, int grid, hipStream_t s, float limit = 0.f);
 int fused_blocks_per_cu(int dt, int variant);  // variant as fused_variant
 // Zero the workspace's synchronisation words.
 hipError_t launch_zero_sync(uint8_t* ws, int dt, int E, int H, int I, int k, int max_tokens, hipStream_t s);

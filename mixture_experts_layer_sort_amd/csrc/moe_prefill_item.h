@@ -244,7 +244,11 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
         if (a.gated) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float gv = acc[0][S][i] * alpha, uv = acc[1][S][i] * alpha;
+            float gv = acc[0][S][i] * alpha, uv = acc[1][S][i] * alpha;
+            if (a.limit > 0.f) {
+              gv = fminf(gv, a.limit);
+              uv = fminf(fmaxf(uv, -a.limit), a.limit);
+            }
             // silu with the hardware exp and reciprocal (~1 ulp each): h is requantised
             // to at most 8 significant bits, so a code moves only within a few ulps of a midpoint
             h[i] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;

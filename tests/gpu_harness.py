@@ -122,7 +122,7 @@ class DeviceLayer:
 
     def __init__(self, w: mi.Workload, cw: CanonicalWeights, max_tokens: int | None = None):
         self.w = w
-        self.shape = lib.make_shape(w.H, w.I, w.E, w.k, max_tokens or w.T, w.dtype, w.act)
+        self.shape = lib.make_shape(w.H, w.I, w.E, w.k, max_tokens or w.T, w.dtype, w.act, w.limit)
         assert lib.moe_check_shape(self.shape) == 0, self.shape
         nbytes = lib.moe_packed_weight_bytes(self.shape)
         self.packed = torch.empty(nbytes, dtype=torch.uint8, device=dev())

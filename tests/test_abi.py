@@ -53,6 +53,17 @@ def test_shape_validation(kw, status):
     assert lib.moe_check_shape(S(**args)) == status
 
 
+def test_gate_up_limit_validation():
+    s = S(256, 512, 8, 2, 16, "bf16")
+    for limit, status in ((0.0, OK), (1.5, OK), (1e30, OK), (-1.0, INVALID), (float("nan"), INVALID),
+                          (float("inf"), INVALID)):
+        s.gate_up_limit = limit
+        assert lib.moe_check_shape(s) == status, limit
+    r = S(256, 512, 8, 2, 16, "bf16", "relu2")
+    r.gate_up_limit = 1.0
+    assert lib.moe_check_shape(r) == UNSUPPORTED  # the clamp belongs to SwiGLU experts
+
+
 def test_sizes_match_layouts():
     s = S(4096, 1408, 64, 6, 64, "bf16")
     # packed weights are a byte permutation of the canonical tensors

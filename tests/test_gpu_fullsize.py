@@ -90,7 +90,7 @@ def _sorted_positions(off, n_hot=4, item_rows=(128, 256)):
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "bf16_decode", "mxfp8_decode", "nvfp4_decode_t8",
                                   "nvfp4_decode_t128", "bf16_mxfp8_decode", "relu2_nvfp4_decode_t128",
-                                  "nvfp4_folded_decode_t128",
+                                  "nvfp4_folded_decode_t128", "clamp_mxfp8_decode",
                                   "mxfp8_prefill"])
 def test_fullsize_parity(name, pool):
     w = W[name]
@@ -155,11 +155,12 @@ def test_fullsize_parity(name, pool):
             assert float(got["w13_a"][e]) == float(a13) and float(got["w2_a"][e]) == float(a2), e
     _log(f"{name}: library weight codes of {len(experts)} experts equal the oracle's")
     if w.dtype == "bf16":
-        Wo = omoe.Weights("bf16", ow["w13"], ow["w2"], act=w.act)
+        Wo = omoe.Weights("bf16", ow["w13"], ow["w2"], act=w.act, limit=w.limit)
     elif gh.weight_format(w.dtype) == "mxfp8":
-        Wo = omoe.Weights(w.dtype, ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"], act=w.act)
+        Wo = omoe.Weights(w.dtype, ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"], act=w.act, limit=w.limit)
     else:
-        Wo = omoe.Weights("nvfp4", ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"], ow["w13_a"], ow["w2_a"], act=w.act)
+        Wo = omoe.Weights("nvfp4", ow["w13"], ow["w2"], ow["w13_s"], ow["w2_s"], ow["w13_a"], ow["w2_a"], act=w.act,
+                          limit=w.limit)
     ref = omoe.moe_layer(x_bits, l_host, Wo, w.k, tokens=toks, keep=True)
     hc, hs = layer.hq_numpy(r, w.T)
     y = gh.bf16_numpy(r["y"])
@@ -187,14 +188,15 @@ def test_fullsize_parity(name, pool):
                                               w.dtype, w.fold) for e in hot]))
         Wh = omoe.Weights(w.dtype, {e: r_[0][0] for e, r_ in zip(hot, res)}, {e: r_[1][0] for e, r_ in zip(hot, res)},
                           {e: r_[0][1] for e, r_ in zip(hot, res)}, {e: r_[1][1] for e, r_ in zip(hot, res)},
-                          {e: r_[0][2] for e, r_ in zip(hot, res)}, {e: r_[1][2] for e, r_ in zip(hot, res)}, act=w.act)
+                          {e: r_[0][2] for e, r_ in zip(hot, res)}, {e: r_[1][2] for e, r_ in zip(hot, res)}, act=w.act,
+                          limit=w.limit)
         worst = 0.0
         for e in hot:
             w13d, w2d = Wh.dequant(e)
             for row in sample[e]:
                 p = int(sp[row])
                 _, _, xh = omoe.quantize_x(x_bits[p // w.k: p // w.k + 1], w.dtype)
-                (_, _, h_ref), y_ref = omoe.expert_mlp(xh[0], w13d, w2d, w.act, w.dtype)
+                (_, _, h_ref), y_ref = omoe.expert_mlp(xh[0], w13d, w2d, w.act, w.dtype, w.limit)
                 h_got = oquant.dequantize_act(hc[row:row + 1], None if hs is None else hs[row:row + 1],
                                               gh.act_format(w.dtype))[0]
                 y_got = (y[p].astype(np.uint32) << 16).view(np.float32)

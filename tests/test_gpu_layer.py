@@ -60,6 +60,15 @@ SMALL = {
     "relu2_bf16_mxfp8_nt2": W["bf16_mxfp8_decode"].scaled(T=96, H=512, I=256, E=8, k=3, act="relu2"),
     # squared-ReLU experts of bf16 weights on the prefill-shaped GEMM
     "relu2_bf16_prefill_tiles": W["bf16_decode"].scaled(T=300, H=384, I=256, E=4, k=2, act="relu2"),
+    # SwiGLU experts with a gate/up clamp (pre-activations have std ~0.02 sqrt(H),
+    # ~0.45 at H = 512: limits of 0.3 - 0.5 clamp a large share), every format
+    # and GEMM shape
+    "clamp_bf16_decode": W["bf16_decode"].scaled(T=33, H=512, I=384, E=16, limit=0.4),
+    "clamp_mxfp8_decode": W["mxfp8_decode"].scaled(T=40, H=640, I=256, E=32, limit=0.5),
+    "clamp_nvfp4_nt2": W["nvfp4_decode_t8"].scaled(T=96, H=512, I=256, E=8, k=3, limit=0.3),
+    "clamp_mxfp8_prefill": W["mxfp8_prefill"].scaled(T=300, H=512, I=256, E=16, k=4, limit=0.4),
+    "clamp_nvfp4_prefill": W["nvfp4_decode_t128"].scaled(T=200, H=384, I=128, E=4, k=2, limit=0.3),
+    "clamp_bf16_mxfp8_prefill": W["bf16_mxfp8_prefill"].scaled(T=520, H=256, I=384, E=8, k=2, limit=0.25),
     # NVFP4 with the weight alpha folded into the block scales
     "nvfp4_folded_decode_small": W["nvfp4_decode_t8"].scaled(T=13, H=512, I=256, E=48, fold=True),
     "nvfp4_folded_prefill_tiles": W["nvfp4_decode_t128"].scaled(T=200, H=384, I=128, E=4, k=2, fold=True),
@@ -72,7 +81,7 @@ SMALL = {
 def _setup(w):
     cw, w13f, w2f = gh.canonical_from_host_master(w)
     Wo = omoe.quantize_weights({e: w13f[e] for e in range(w.E)}, {e: w2f[e] for e in range(w.E)}, w.dtype, w.act,
-                               w.fold)
+                               w.fold, w.limit)
     return cw, Wo
 
 
