@@ -227,6 +227,31 @@ def expert_mlp(xh: np.ndarray, w13: np.ndarray, w2: np.ndarray, act: str, dtype:
     return (hc[0], None if hsc is None else hsc[0], hh[0]), y
 
 
+def batched_experts(x_bits: np.ndarray, counts, W: Weights):
+    """The expert MLPs on tokens that arrive already bucketed per expert (the
+    batched activation format of the CuteDSL batched-experts class [vLLM PR
+    38050 report, "Implementation": FlashInferCuteDSLBatchedExperts, batched
+    activation format, workspace_shapes]): no routing and no combine.
+
+    x_bits bf16 [E, M, H]; counts [E] (values clamped to [0, M]).  Row r of
+    expert e (r < counts[e]) is quantised, run through expert e's MLP (gate/up
+    product, activation, requantisation, down product) and returned as
+    y float64 [E, M, H]; the other rows of y are zero.
+    """
+    x_bits = np.asarray(x_bits, np.uint16)
+    E, M, H = x_bits.shape
+    y = np.zeros((E, M, H), np.float64)
+    for e in range(E):
+        c = int(min(max(int(counts[e]), 0), M))
+        if c == 0:
+            continue
+        w13, w2 = W.dequant(e)
+        _, _, xh = quantize_x(x_bits[e, :c], W.dtype)
+        for r in range(c):
+            _, y[e, r] = expert_mlp(xh[r], w13, w2, W.act, W.dtype, W.limit)
+    return y
+
+
 @dataclasses.dataclass
 class LayerResult:
     out: np.ndarray            # bf16 bits [T, H] (rows of the requested tokens)
