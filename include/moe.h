@@ -268,6 +268,29 @@ MOE_API moe_status moe_forward_fused(const moe_shape* shape, int32_t T, const vo
                                      const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace of moe_batched_experts for up to max_rows rows per expert
+ * (0 for an unsupported shape or num_experts * max_rows > 2^24). */
+MOE_API size_t moe_batched_workspace_bytes(const moe_shape* shape, int32_t max_rows);
+
+/* The expert MLPs on tokens that arrive already bucketed per expert -- the
+ * batched activation format of the CuteDSL batched-experts class [vLLM PR
+ * 38050 report, "Implementation": FlashInferCuteDSLBatchedExperts, batched
+ * activation format with workspace_shapes] -- with no routing and no
+ * combine (the dispatch and the weighted combine live outside, e.g. in an
+ * expert-parallel exchange).
+ *   x      bf16 [E, max_rows, H]: row r of expert e is valid for r < counts[e];
+ *   counts int32 [E] on the device (values clamped to [0, max_rows]);
+ *   y      bf16 [E, max_rows, H]: y[e, r] = W2[e] . requant(act(W13[e] . quant(x[e, r])))
+ *          for the valid rows (the same arithmetic as moe_forward's expert
+ *          outputs); other rows of y are not written.
+ * The weights are those of moe_prepare_weights for `shape` (top_k and
+ * max_tokens are not used).  ws: moe_batched_workspace_bytes(shape,
+ * max_rows) bytes.  The GEMM shapes (decode- or prefill-shaped) follow
+ * max_rows as the expected rows per expert. */
+MOE_API moe_status moe_batched_experts(const moe_shape* shape, int32_t max_rows, const int32_t* counts,
+                                       const uint16_t* x, const void* packed, uint16_t* y, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
 /* Size of the device scratch array behind moe_forward_noalloc (64 MiB per
  * device, held until the process ends). */
 #define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)

@@ -46,6 +46,8 @@ EXPORTED = [
     "moe_forward_fused",
     "moe_forward_noalloc",
     "moe_workspace_init",
+    "moe_batched_workspace_bytes",
+    "moe_batched_experts",
 ]
 
 
@@ -105,6 +107,8 @@ def _load():
         "moe_forward": (I32, [S, I32, P, P, P, P, P, P, P, SZ, P]),
         "moe_forward_fused": (I32, [S, I32, P, P, P, P, P, P, P, SZ, P]),
         "moe_forward_noalloc": (I32, [S, I32, P, P, P, P, P, P, P]),
+        "moe_batched_workspace_bytes": (SZ, [S, I32]),
+        "moe_batched_experts": (I32, [S, I32, P, P, P, P, P, SZ, P]),
         "moe_workspace_init": (I32, [S, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -272,3 +276,14 @@ def moe_forward_noalloc(shape, T, packed, logits, x, out, topk_ids=None, topk_w=
 def moe_workspace_init(shape, ws, ws_bytes=None, stream=None):
     nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
     _check(_lib.moe_workspace_init(ctypes.byref(shape), _ptr(ws), nbytes, _stream(stream)), "moe_workspace_init")
+
+
+def moe_batched_workspace_bytes(shape: moe_shape, max_rows: int) -> int:
+    return _lib.moe_batched_workspace_bytes(ctypes.byref(shape), max_rows)
+
+
+def moe_batched_experts(shape, max_rows, counts, x, packed, y, ws, ws_bytes=None, stream=None):
+    """Expert MLPs on tokens bucketed per expert: x, y bf16 [E, max_rows, H], counts int32 [E]."""
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(_lib.moe_batched_experts(ctypes.byref(shape), max_rows, _ptr(counts), _ptr(x), _ptr(packed), _ptr(y),
+                                    _ptr(ws), nbytes, _stream(stream)), "moe_batched_experts")

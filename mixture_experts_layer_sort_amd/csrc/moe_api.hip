@@ -340,6 +340,36 @@ moe_status moe_forward_noalloc(const moe_shape* s, int32_t T, const void* packed
   return forward_staged(s, T, T, packed, logits, x, out, topk_ids, topk_w, base, stream);
 }
 
+size_t moe_batched_workspace_bytes(const moe_shape* s, int32_t max_rows) {
+  if (check_shape(s) != MOE_OK || max_rows < 1 || (long long)s->num_experts * max_rows > (1LL << 24)) return 0;
+  return batched_layout(s->dtype, s->num_experts, s->hidden, s->inter, max_rows).total;
+}
+
+moe_status moe_batched_experts(const moe_shape* s, int32_t max_rows, const int32_t* counts, const uint16_t* x,
+                               const void* packed, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (max_rows < 1 || (long long)s->num_experts * max_rows > (1LL << 24)) return MOE_ERR_INVALID_ARG;
+  if (!counts || !x || !packed || !y || !ws) return MOE_ERR_INVALID_ARG;
+  const int dt = s->dtype, E = s->num_experts, H = s->hidden, I = s->inter, R = E * max_rows;
+  const BatchedLayout B = batched_layout(dt, E, H, I, max_rows);
+  if (ws_bytes < B.total) return MOE_ERR_WORKSPACE;
+  uint8_t* base = (uint8_t*)ws;
+  int32_t* offsets = (int32_t*)(base + B.offsets);
+  int32_t* rows = (int32_t*)(base + B.rows);
+  uint8_t* xq = act_dt(dt) == DT_BF16 ? (uint8_t*)x : base + B.xq;  // bf16 activations are used in place
+  uint8_t* hq = base + B.hq;
+  // one "pair" per valid row (k = 1, R rows of capacity): the GEMM variants follow the rows per expert
+  hipError_t e = launch_batched_prep(dt, counts, E, max_rows, H, offsets, rows, x, xq, stream);
+  if (e == hipSuccess)
+    e = launch_gemm13(dt, gated(s), E, H, I, 1, R, (const uint8_t*)packed, offsets, rows, xq, hq,
+                      gemm_grid(dt, true, R, 1, E), stream, s->gate_up_limit);
+  if (e == hipSuccess)
+    e = launch_gemm2(dt, gated(s), E, H, I, 1, R, (const uint8_t*)packed, offsets, rows, hq, y,
+                     gemm_grid(dt, false, R, 1, E), stream);
+  return launched(e);
+}
+
 moe_status moe_forward_fused(const moe_shape* s, int32_t T, const void* packed, const float* logits,
                              const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w, void* ws,
                              size_t ws_bytes, hipStream_t stream) {

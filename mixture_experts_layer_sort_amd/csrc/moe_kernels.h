@@ -15,6 +15,12 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, floa
 hipError_t launch_permute(int dt, const int* ids, int T, int k, int E, int H, int* offsets, int* sorted_pairs,
                           int* pair_pos, const uint16_t* x, uint8_t* xq, hipStream_t s);
 
+// Batched activation format: offsets and rows of the valid rows of x [E, M, H]
+// (counts clamped to [0, M]), and x quantised into xq (all E M rows; BF16
+// activations are used in place and xq is ignored).
+hipError_t launch_batched_prep(int dt, const int* counts, int E, int M, int H, int* offsets, int* rows,
+                               const uint16_t* x, uint8_t* xq, hipStream_t s);
+
 hipError_t launch_quantize_weights(int dt, int count, int rows, int K, const float* w, void* codes, void* scales,
                                    float* alpha, hipStream_t s);
 

@@ -151,4 +151,21 @@ MOE_HD WorkspaceLayout workspace_layout(int dt, int E, int H, int I, int k, int 
   return W;
 }
 
+// moe_batched_experts workspace: E experts of up to M rows each.
+struct BatchedLayout {
+  size_t offsets, rows, xq, hq, total;
+};
+
+MOE_HD BatchedLayout batched_layout(int dt, int E, int H, int I, int M) {
+  BatchedLayout B;
+  const size_t R = (size_t)E * M;
+  size_t off = 0;
+  B.offsets = off; off = align256(off + (size_t)(E + 1) * 4);
+  B.rows = off; off = align256(off + R * 4);
+  B.xq = off; off = align256(off + (act_dt(dt) == DT_BF16 ? 0 : act_bytes(dt, (int)R, H)));
+  B.hq = off; off = align256(off + act_bytes(dt, (int)R, I));
+  B.total = off;
+  return B;
+}
+
 }  // namespace moe

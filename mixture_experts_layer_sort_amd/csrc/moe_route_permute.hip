@@ -38,6 +38,70 @@ __global__ __launch_bounds__(kPermThreads) void permute_quant_kernel(const int* 
   quantize_x_blocks<DT>(x, n_elem, xq_codes, xq_scales, xq_deq, gtid, gstride);
 }
 
+// ------------------------------------------------------------------ batched activation format
+// Tokens arrive bucketed per expert, x [E, M, H] with counts[e] valid rows
+// (clamped to [0, M]).  The grouped GEMMs then run with one "pair" per valid
+// row: offsets = exclusive prefix of the clamped counts, rows[offsets[e] + r]
+// = e M + r (the row of the batched buffer), so the gate/up GEMM reads
+// activation row rows[i] and the down GEMM writes y row rows[i] in place.
+
+// One block of 1024 threads: offsets[0..E] (E <= 1024).
+__global__ __launch_bounds__(1024) void batched_offsets_kernel(const int* __restrict__ counts, int E, int M,
+                                                               int* __restrict__ offsets) {
+  __shared__ int sc[1024];
+  const int t = threadIdx.x;
+  const int c = t < E ? min(max(counts[t], 0), M) : 0;
+  sc[t] = c;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // Hillis-Steele inclusive scan
+    const int v = t >= d ? sc[t - d] : 0;
+    __syncthreads();
+    sc[t] += v;
+    __syncthreads();
+  }
+  if (t < E) offsets[t] = sc[t] - c;
+  if (t == E - 1) offsets[E] = sc[t];
+}
+
+// rows[] of every valid row, and (unless the activations are used in place)
+// the quantisation of all E M rows of x.
+template <int DT>
+__global__ __launch_bounds__(kPermThreads) void batched_rows_quant_kernel(
+    const int* __restrict__ counts, const int* __restrict__ offsets, int E, int M, int* __restrict__ rows,
+    const uint16_t* __restrict__ x, long long n_elem, uint8_t* __restrict__ xq_codes, uint8_t* __restrict__ xq_scales,
+    uint16_t* __restrict__ xq_deq, int do_quant) {
+  const long long gtid = (long long)blockIdx.x * kPermThreads + threadIdx.x;
+  const long long gstride = (long long)gridDim.x * kPermThreads;
+  for (long long i = gtid; i < (long long)E * M; i += gstride) {
+    const int e = (int)(i / M), r = (int)(i % M);
+    if (r < min(max(counts[e], 0), M)) rows[offsets[e] + r] = (int)i;
+  }
+  if (do_quant) quantize_x_blocks<DT>(x, n_elem, xq_codes, xq_scales, xq_deq, gtid, gstride);
+}
+
+hipError_t launch_batched_prep(int dt, const int* counts, int E, int M, int H, int* offsets, int* rows,
+                               const uint16_t* x, uint8_t* xq, hipStream_t s) {
+  dt = act_dt(dt);
+  const int R = E * M;
+  hipLaunchKernelGGL(batched_offsets_kernel, dim3(1), dim3(1024), 0, s, counts, E, M, offsets);
+  const long long n_elem = (long long)R * H;
+  const int do_quant = dt != DT_BF16;
+  uint8_t* xq_scales = do_quant ? xq + act_scale_offset(dt, R, H) : nullptr;
+  uint16_t* xq_deq = do_quant ? reinterpret_cast<uint16_t*>(xq + act_dequant_offset(dt, R, H)) : nullptr;
+  const long long work = do_quant ? n_elem / 4 : (long long)R;
+  const int blocks = (int)min((work + kPermThreads - 1) / kPermThreads, (long long)4096);
+  if (dt == DT_MXFP8)
+    hipLaunchKernelGGL(batched_rows_quant_kernel<DT_MXFP8>, dim3(blocks), dim3(kPermThreads), 0, s, counts, offsets,
+                       E, M, rows, x, n_elem, xq, xq_scales, xq_deq, do_quant);
+  else if (dt == DT_NVFP4)
+    hipLaunchKernelGGL(batched_rows_quant_kernel<DT_NVFP4>, dim3(blocks), dim3(kPermThreads), 0, s, counts, offsets,
+                       E, M, rows, x, n_elem, xq, xq_scales, xq_deq, do_quant);
+  else
+    hipLaunchKernelGGL(batched_rows_quant_kernel<DT_BF16>, dim3(blocks), dim3(kPermThreads), 0, s, counts, offsets,
+                       E, M, rows, x, n_elem, xq, xq_scales, xq_deq, 0);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ weight quantisation
 // fp32 master weights -> canonical codes (the load-time preprocessing step).
 

@@ -64,6 +64,17 @@ def test_gate_up_limit_validation():
     assert lib.moe_check_shape(r) == UNSUPPORTED  # the clamp belongs to SwiGLU experts
 
 
+def test_batched_workspace_size():
+    s = S(512, 256, 8, 2, 16, "mxfp8")
+    n = lib.moe_batched_workspace_bytes(s, 24)
+    R = 8 * 24
+    xq = ((R * 512 + 255) // 256) * 256 + ((R * 16 + 255) // 256) * 256 + ((R * 512 * 2 + 255) // 256) * 256
+    hq = ((R * 256 + 255) // 256) * 256 + ((R * 8 + 255) // 256) * 256 + ((R * 256 * 2 + 255) // 256) * 256
+    assert n == 256 + ((R * 4 + 255) // 256) * 256 + xq + hq
+    assert lib.moe_batched_workspace_bytes(s, 0) == 0
+    assert lib.moe_batched_workspace_bytes(S(512, 256, 1024, 2, 16, "bf16"), 1 << 15) == 0  # E * rows > 2^24
+
+
 def test_sizes_match_layouts():
     s = S(4096, 1408, 64, 6, 64, "bf16")
     # packed weights are a byte permutation of the canonical tensors
