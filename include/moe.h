@@ -291,6 +291,29 @@ MOE_API moe_status moe_batched_experts(const moe_shape* shape, int32_t max_rows,
                                        const uint16_t* x, const void* packed, uint16_t* y, void* ws, size_t ws_bytes,
                                        hipStream_t stream);
 
+/* Dense NVFP4 linear layer, the pages' second b12x kernel: bf16 activations
+ * quantised to NVFP4 inside and multiplied by NVFP4 weights [vLLM PR 40082
+ * report, "Implementation" item 2: FlashInferB12xNvFp4LinearKernel quantises
+ * the input (scaled_fp4_quant) and calls the scaled fp4 matrix product].
+ *   out[m, n] = bf16( alpha * sum_k xq[m, k] * w[n, k] )  (fp32 accumulation),
+ * xq = the NVFP4 quantisation of x's rows (per 16, global scale 1: the
+ * layer's activation rule), w = e2m1 codes [N, K/2] (element 2i in the low
+ * nibble) times e4m3 scales [N, K/16] (moe_quantize_weights(MOE_NVFP4, 1, N,
+ * K, ...) produces them and alpha).  N % 64 == 0, K % 128 == 0 (else
+ * MOE_ERR_UNSUPPORTED).  The weights are repacked once by
+ * moe_nvfp4_linear_prepare into moe_nvfp4_linear_packed_bytes(N, K) bytes;
+ * a call on M rows needs moe_nvfp4_linear_workspace_bytes(M, K) bytes of
+ * workspace (sizes are 0 for unsupported arguments).  x bf16 [M, K],
+ * out bf16 [M, N]; M == 0 is a no-op.  It runs the MoE down-GEMM kernels
+ * with one expert holding all M rows. */
+MOE_API size_t moe_nvfp4_linear_packed_bytes(int32_t N, int32_t K);
+MOE_API size_t moe_nvfp4_linear_workspace_bytes(int32_t max_M, int32_t K);
+MOE_API moe_status moe_nvfp4_linear_prepare(int32_t N, int32_t K, const void* codes, const void* scales,
+                                            const float* alpha, void* packed, size_t packed_bytes,
+                                            hipStream_t stream);
+MOE_API moe_status moe_nvfp4_linear(int32_t M, int32_t N, int32_t K, const void* packed, const uint16_t* x,
+                                    uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Size of the device scratch array behind moe_forward_noalloc (64 MiB per
  * device, held until the process ends). */
 #define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)

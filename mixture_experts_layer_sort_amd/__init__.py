@@ -48,6 +48,10 @@ EXPORTED = [
     "moe_workspace_init",
     "moe_batched_workspace_bytes",
     "moe_batched_experts",
+    "moe_nvfp4_linear_packed_bytes",
+    "moe_nvfp4_linear_workspace_bytes",
+    "moe_nvfp4_linear_prepare",
+    "moe_nvfp4_linear",
 ]
 
 
@@ -109,6 +113,10 @@ def _load():
         "moe_forward_noalloc": (I32, [S, I32, P, P, P, P, P, P, P]),
         "moe_batched_workspace_bytes": (SZ, [S, I32]),
         "moe_batched_experts": (I32, [S, I32, P, P, P, P, P, SZ, P]),
+        "moe_nvfp4_linear_packed_bytes": (SZ, [I32, I32]),
+        "moe_nvfp4_linear_workspace_bytes": (SZ, [I32, I32]),
+        "moe_nvfp4_linear_prepare": (I32, [I32, I32, P, P, P, P, SZ, P]),
+        "moe_nvfp4_linear": (I32, [I32, I32, I32, P, P, P, P, SZ, P]),
         "moe_workspace_init": (I32, [S, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -287,3 +295,24 @@ def moe_batched_experts(shape, max_rows, counts, x, packed, y, ws, ws_bytes=None
     nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
     _check(_lib.moe_batched_experts(ctypes.byref(shape), max_rows, _ptr(counts), _ptr(x), _ptr(packed), _ptr(y),
                                     _ptr(ws), nbytes, _stream(stream)), "moe_batched_experts")
+
+
+def moe_nvfp4_linear_packed_bytes(N: int, K: int) -> int:
+    return _lib.moe_nvfp4_linear_packed_bytes(N, K)
+
+
+def moe_nvfp4_linear_workspace_bytes(max_M: int, K: int) -> int:
+    return _lib.moe_nvfp4_linear_workspace_bytes(max_M, K)
+
+
+def moe_nvfp4_linear_prepare(N, K, codes, scales, alpha, packed, packed_bytes=None, stream=None):
+    nbytes = packed_bytes if packed_bytes is not None else packed.numel() * packed.element_size()
+    _check(_lib.moe_nvfp4_linear_prepare(N, K, _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(packed), nbytes,
+                                         _stream(stream)), "moe_nvfp4_linear_prepare")
+
+
+def moe_nvfp4_linear(M, N, K, packed, x, out, ws, ws_bytes=None, stream=None):
+    """out bf16 [M, N] = NVFP4(x bf16 [M, K]) . W^T (dense NVFP4 linear layer)."""
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(_lib.moe_nvfp4_linear(M, N, K, _ptr(packed), _ptr(x), _ptr(out), _ptr(ws), nbytes, _stream(stream)),
+           "moe_nvfp4_linear")

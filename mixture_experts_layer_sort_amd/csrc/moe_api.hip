@@ -370,6 +370,47 @@ moe_status moe_batched_experts(const moe_shape* s, int32_t max_rows, const int32
   return launched(e);
 }
 
+static bool dense_shape_ok(int32_t N, int32_t K) {
+  return N >= 64 && K >= 128 && N % 64 == 0 && K % 128 == 0 && N <= (1 << 20) && K <= (1 << 20);
+}
+
+size_t moe_nvfp4_linear_packed_bytes(int32_t N, int32_t K) {
+  return dense_shape_ok(N, K) ? dense_layout(N, K).total : 0;
+}
+
+size_t moe_nvfp4_linear_workspace_bytes(int32_t max_M, int32_t K) {
+  if (max_M < 1 || max_M > (1 << 24) || K < 128 || K % 128 || K > (1 << 20)) return 0;
+  return dense_workspace(max_M, K).total;
+}
+
+moe_status moe_nvfp4_linear_prepare(int32_t N, int32_t K, const void* codes, const void* scales, const float* alpha,
+                                    void* packed, size_t packed_bytes, hipStream_t stream) {
+  if (!dense_shape_ok(N, K)) return MOE_ERR_UNSUPPORTED;
+  if (!codes || !scales || !alpha || !packed) return MOE_ERR_INVALID_ARG;
+  if (packed_bytes < dense_layout(N, K).total) return MOE_ERR_WORKSPACE;
+  return launched(launch_dense_prepare(N, K, (const uint8_t*)codes, (const uint8_t*)scales, alpha, (uint8_t*)packed,
+                                       stream));
+}
+
+moe_status moe_nvfp4_linear(int32_t M, int32_t N, int32_t K, const void* packed, const uint16_t* x, uint16_t* out,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dense_shape_ok(N, K)) return MOE_ERR_UNSUPPORTED;
+  if (M < 0 || M > (1 << 24)) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  if (!packed || !x || !out || !ws) return MOE_ERR_INVALID_ARG;
+  const DenseWorkspace W = dense_workspace(M, K);
+  if (ws_bytes < W.total) return MOE_ERR_WORKSPACE;
+  uint8_t* base = (uint8_t*)ws;
+  int32_t* offsets = (int32_t*)(base + W.offsets);
+  int32_t* rows = (int32_t*)(base + W.rows);
+  uint8_t* xq = base + W.xq;
+  hipError_t e = launch_dense_prep(M, K, offsets, rows, x, xq, stream);
+  if (e == hipSuccess)
+    e = launch_dense_gemm(M, N, K, (const uint8_t*)packed, offsets, rows, xq, out,
+                          gemm_grid(MOE_NVFP4, false, M, 1, 1), stream);
+  return launched(e);
+}
+
 moe_status moe_forward_fused(const moe_shape* s, int32_t T, const void* packed, const float* logits,
                              const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w, void* ws,
                              size_t ws_bytes, hipStream_t stream) {

@@ -227,6 +227,41 @@ hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, c
   return dispatch_gemm<false>(weight_dt(dt), gemm_nt(T, k, E), a, grid, s);
 }
 
+hipError_t launch_dense_prepare(int N, int K, const uint8_t* codes, const uint8_t* scales, const float* alpha,
+                                uint8_t* packed, hipStream_t s) {
+  const DenseLayout D = dense_layout(N, K);
+  const long long n = (long long)D.G * D.KG * 4 * 64;
+  const int threads = 256;
+  const int blocks = (int)std::min((n + threads - 1) / threads, 1LL << 20);
+  // the W2 arrangement: 64-row groups, rows 64 g + 16 t + i
+  hipLaunchKernelGGL(prepare_kernel<DT_NVFP4>, dim3(blocks), dim3(threads), 0, s, codes, scales, 1, N, K, D.G, D.KG,
+                     K, 0, packed + D.codes, packed + D.scales);
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(1), dim3(64), 0, s, alpha, reinterpret_cast<float*>(packed + D.alpha), 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_gemm(int M, int N, int K, const uint8_t* packed, const int* offsets, const int* rows,
+                             const uint8_t* xq, uint16_t* out, int grid, hipStream_t s) {
+  const DenseLayout D = dense_layout(N, K);
+  GemmArgs a;
+  a.wcodes = packed + D.codes;
+  a.wscales = packed + D.scales;
+  a.walpha = reinterpret_cast<const float*>(packed + D.alpha);
+  a.offsets = offsets;
+  a.sorted_pairs = rows;
+  a.act = xq + act_operand_offset(DT_NVFP4, M, K);
+  a.act_scales = nullptr;
+  a.out = reinterpret_cast<uint8_t*>(out);
+  a.out_scales = nullptr;
+  a.out_deq = nullptr;
+  a.act_bf16 = 0;
+  a.gated = 0;
+  a.limit = 0.f;
+  a.E = 1; a.K = K; a.G = D.G; a.KG = D.KG; a.k = 1; a.n_out = N;
+  if (gemm_prefill(M, 1, 1)) return launch_prefill(DT_NVFP4, false, a, grid, s);
+  return dispatch_gemm<false>(DT_NVFP4, gemm_nt(M, 1, 1), a, grid, s);
+}
+
 hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t* w13, const uint8_t* w13s,
                           const float* w13a, const uint8_t* w2, const uint8_t* w2s, const float* w2a, uint8_t* packed,
                           hipStream_t s) {

@@ -21,6 +21,15 @@ hipError_t launch_permute(int dt, const int* ids, int T, int k, int E, int H, in
 hipError_t launch_batched_prep(int dt, const int* counts, int E, int M, int H, int* offsets, int* rows,
                                const uint16_t* x, uint8_t* xq, hipStream_t s);
 
+// Dense NVFP4 linear layer: repack weights [N, K] (W2 arrangement) and alpha;
+// offsets / identity rows / NVFP4 quantisation of x [M, K]; the down-GEMM kernels
+// with one expert of M rows writing out [M, N].
+hipError_t launch_dense_prepare(int N, int K, const uint8_t* codes, const uint8_t* scales, const float* alpha,
+                                uint8_t* packed, hipStream_t s);
+hipError_t launch_dense_prep(int M, int K, int* offsets, int* rows, const uint16_t* x, uint8_t* xq, hipStream_t s);
+hipError_t launch_dense_gemm(int M, int N, int K, const uint8_t* packed, const int* offsets, const int* rows,
+                             const uint8_t* xq, uint16_t* out, int grid, hipStream_t s);
+
 hipError_t launch_quantize_weights(int dt, int count, int rows, int K, const float* w, void* codes, void* scales,
                                    float* alpha, hipStream_t s);
 

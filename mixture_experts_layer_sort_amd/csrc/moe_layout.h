@@ -151,6 +151,41 @@ MOE_HD WorkspaceLayout workspace_layout(int dt, int E, int H, int I, int k, int 
   return W;
 }
 
+// Dense NVFP4 linear layer: weights [N, K] in the W2 tile layout (row groups
+// of 64, 128-wide kgroups), then the fp32 alpha.
+struct DenseLayout {
+  int G, KG;
+  size_t codes, scales, alpha, total;
+};
+
+MOE_HD DenseLayout dense_layout(int N, int K) {
+  DenseLayout D;
+  D.G = N / 64;
+  D.KG = K / kKGroup;
+  const size_t n = (size_t)D.G * D.KG * kTilesPerGroup;
+  size_t off = 0;
+  D.codes = off; off = align256(off + n * tile_code_bytes(DT_NVFP4));
+  D.scales = off; off = align256(off + n * tile_scale_bytes(DT_NVFP4));
+  D.alpha = off; off = align256(off + 4);
+  D.total = off;
+  return D;
+}
+
+// Its workspace for M rows: offsets {0, M}, the identity row map, the NVFP4-quantised rows of x.
+struct DenseWorkspace {
+  size_t offsets, rows, xq, total;
+};
+
+MOE_HD DenseWorkspace dense_workspace(int M, int K) {
+  DenseWorkspace W;
+  size_t off = 0;
+  W.offsets = off; off = align256(off + 8);
+  W.rows = off; off = align256(off + (size_t)M * 4);
+  W.xq = off; off = align256(off + act_bytes(DT_NVFP4, M, K));
+  W.total = off;
+  return W;
+}
+
 // moe_batched_experts workspace: E experts of up to M rows each.
 struct BatchedLayout {
   size_t offsets, rows, xq, hq, total;

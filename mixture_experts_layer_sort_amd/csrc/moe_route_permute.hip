@@ -102,6 +102,34 @@ hipError_t launch_batched_prep(int dt, const int* counts, int E, int M, int H, i
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ dense NVFP4 linear
+// One "expert" holding all M rows: offsets {0, M}, rows[i] = i, and the
+// NVFP4 quantisation of x [M, K] (per 16, global scale 1).
+__global__ __launch_bounds__(kPermThreads) void dense_prep_kernel(int M, int* __restrict__ offsets,
+                                                                  int* __restrict__ rows,
+                                                                  const uint16_t* __restrict__ x, long long n_elem,
+                                                                  uint8_t* __restrict__ xq_codes,
+                                                                  uint8_t* __restrict__ xq_scales,
+                                                                  uint16_t* __restrict__ xq_deq) {
+  const long long gtid = (long long)blockIdx.x * kPermThreads + threadIdx.x;
+  const long long gstride = (long long)gridDim.x * kPermThreads;
+  if (gtid == 0) {
+    offsets[0] = 0;
+    offsets[1] = M;
+  }
+  for (long long i = gtid; i < M; i += gstride) rows[i] = (int)i;
+  quantize_x_blocks<DT_NVFP4>(x, n_elem, xq_codes, xq_scales, xq_deq, gtid, gstride);
+}
+
+hipError_t launch_dense_prep(int M, int K, int* offsets, int* rows, const uint16_t* x, uint8_t* xq, hipStream_t s) {
+  const long long n_elem = (long long)M * K;
+  const int blocks = (int)min((n_elem / 4 + kPermThreads - 1) / kPermThreads, (long long)4096);
+  hipLaunchKernelGGL(dense_prep_kernel, dim3(max(blocks, 1)), dim3(kPermThreads), 0, s, M, offsets, rows, x, n_elem,
+                     xq, xq + act_scale_offset(DT_NVFP4, M, K),
+                     reinterpret_cast<uint16_t*>(xq + act_dequant_offset(DT_NVFP4, M, K)));
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ weight quantisation
 // fp32 master weights -> canonical codes (the load-time preprocessing step).
 

@@ -75,6 +75,16 @@ def test_batched_workspace_size():
     assert lib.moe_batched_workspace_bytes(S(512, 256, 1024, 2, 16, "bf16"), 1 << 15) == 0  # E * rows > 2^24
 
 
+def test_nvfp4_linear_sizes():
+    N, K = 384, 512
+    tiles = (N // 64) * (K // 128) * 4
+    assert lib.moe_nvfp4_linear_packed_bytes(N, K) == tiles * 1024 + tiles * 128 + 256
+    M = 5
+    xq = ((M * K // 2 + 255) // 256) * 256 + ((M * K // 16 + 255) // 256) * 256 + ((M * K * 2 + 255) // 256) * 256
+    assert lib.moe_nvfp4_linear_workspace_bytes(M, K) == 256 + 256 + xq
+    assert lib.moe_nvfp4_linear_packed_bytes(96, 512) == 0 and lib.moe_nvfp4_linear_workspace_bytes(0, K) == 0
+
+
 def test_sizes_match_layouts():
     s = S(4096, 1408, 64, 6, 64, "bf16")
     # packed weights are a byte permutation of the canonical tensors
