@@ -4,22 +4,24 @@
 
 One step = one pass of the whole layer over one batch (route -> permute +
 activation quantisation -> gate/up GEMM + SwiGLU + requant -> down GEMM ->
-combine), i.e. one moe_forward call, with inputs and prepared weights already
-resident in HBM.  The default workload is the MXFP8 prefill layer (T=8192,
-H=7168, I=2048, E=256, top-8, Zipf(1.1)-skewed routing); --workload picks any
-other (e.g. bf16_decode, mxfp8_decode, nvfp4_decode_t8, nvfp4_decode_t128).
-Prints one JSON line with tokens/s (K steps of moe_forward, the five stage
-kernels back to back on torch's stream, each step between HIP events, with
-the L2 and the Infinity Cache flushed by reading 1 GiB before every step
-outside the timed intervals), the roofline of the dominant kernel (the
-gate/up GEMM, timed with HIP events on its launch stream over a second
-region of K steps through the staged entry points, flushed the same way),
-whole-layer HBM / MFMA fractions, the back-to-back (unflushed) step time,
-the step time when the same moe_forward call is captured into a HIP graph
-and replayed,
-the single-launch entry's step time, a measured device copy (GB/s) for
-context, and the CPU oracle (its expert-grouped BLAS form) timed on a bounded
-sample of the same workload.
+combine), i.e. one moe_forward_knobs call with the knobs the package's knob
+cache holds for the shape (else the defaults; reported in config.knobs),
+with inputs and prepared weights already resident in HBM.  The default
+workload is the MXFP8 prefill layer (T=8192, H=7168, I=2048, E=256, top-8,
+Zipf(1.1)-skewed routing); --workload picks any other (e.g. bf16_decode,
+mxfp8_decode, nvfp4_decode_t8, nvfp4_decode_t128).
+
+Prints one JSON line with tokens/s (K steps, the five stage kernels back to
+back on torch's stream, each step between HIP events, with the L2 and the
+Infinity Cache flushed by reading 1 GiB before every step outside the timed
+intervals), the roofline of the dominant kernel (the gate/up GEMM, timed with
+HIP events on its launch stream over a second region of K steps through the
+staged entry points, flushed the same way), whole-layer HBM / MFMA
+fractions, the back-to-back (unflushed) step time, the step time when the
+same call is captured into a HIP graph and replayed, the step time with the
+in-kernel fc2 reduce, the single-launch entry's step time, a measured device
+copy (GB/s) for context, and the CPU oracle (its expert-grouped BLAS form)
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -45,7 +47,9 @@ MFMA_PEAK_TFLOPS = {"bf16": BF16_PEAK_TFLOPS, "mxfp8": FP8_PEAK_TFLOPS, "nvfp4":
                     "bf16_mxfp8": BF16_PEAK_TFLOPS}
 # the arithmetic type of the contractions per layer format ("bf16_mxfp8": bf16
 # activations over MXFP8 weights)
-ARITH_DTYPE = {"bf16": "bf16", "mxfp8": "bf16", "nvfp4": "f16", "bf16_mxfp8": "bf16"}
+# (MXFP8 layers: gate/up on bf16 products of the exact codes, the prefill-shaped
+# down GEMM on the e4m3 block-scaled instruction)
+ARITH_DTYPE = {"bf16": "bf16", "mxfp8": "bf16/e4m3", "nvfp4": "f16", "bf16_mxfp8": "bf16"}
 DEFAULT_WORKLOAD = "mxfp8_prefill"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mixture_experts_layer_sort_amd", "csrc")
@@ -86,63 +90,6 @@ def load_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-class Layer:
-    """One layer on the device: canonical weights quantised from the seeded
-    fp32 masters by the library (expert by expert), the packed weights and the
-    forward workspace."""
-
-    def __init__(self, lib, w, device):
-        import torch
-
-        E, H, I, R = w.E, w.H, w.I, w.R13
-        wf = "mxfp8" if w.dtype == "bf16_mxfp8" else w.dtype
-        u8 = torch.uint8
-        if wf == "bf16":
-            c13, c2 = (torch.empty(E, R, H, dtype=torch.bfloat16, device=device),
-                       torch.empty(E, H, I, dtype=torch.bfloat16, device=device))
-            s13 = s2 = a13 = a2 = None
-        elif wf == "mxfp8":
-            c13, c2 = torch.empty(E, R, H, dtype=u8, device=device), torch.empty(E, H, I, dtype=u8, device=device)
-            s13, s2 = (torch.empty(E, R, H // 32, dtype=u8, device=device),
-                       torch.empty(E, H, I // 32, dtype=u8, device=device))
-            a13 = a2 = None
-        else:
-            c13, c2 = (torch.empty(E, R, H // 2, dtype=u8, device=device),
-                       torch.empty(E, H, I // 2, dtype=u8, device=device))
-            s13, s2 = (torch.empty(E, R, H // 16, dtype=u8, device=device),
-                       torch.empty(E, H, I // 16, dtype=u8, device=device))
-            a13, a2 = torch.empty(E, dtype=torch.float32, device=device), torch.empty(E, dtype=torch.float32,
-                                                                                       device=device)
-
-        def sub(t, e):
-            return None if t is None else t[e:e + 1]
-
-        import moe_inputs as mi
-
-        for e in range(E):
-            m13, m2 = mi.device_master_weights(w, e, device)
-            lib.moe_quantize_weights(w.dtype, 1, R, H, m13, c13[e:e + 1], sub(s13, e), sub(a13, e))
-            lib.moe_quantize_weights(w.dtype, 1, H, I, m2, c2[e:e + 1], sub(s2, e), sub(a2, e))
-            if w.fold:
-                lib.moe_nvfp4_fold_global_scale(1, R, H, sub(s13, e), sub(a13, e))
-                lib.moe_nvfp4_fold_global_scale(1, H, I, sub(s2, e), sub(a2, e))
-            del m13, m2
-        self.w = w
-        self.shape = lib.make_shape(H, I, E, w.k, w.T, w.dtype, w.act, w.limit)
-        self.packed = torch.empty(lib.moe_packed_weight_bytes(self.shape), dtype=u8, device=device)
-        lib.moe_prepare_weights(self.shape, c13, s13, a13, c2, s2, a2, self.packed)
-        self.ws = torch.empty(lib.moe_workspace_bytes(self.shape), dtype=u8, device=device)
-        lib.moe_workspace_init(self.shape, self.ws)
-        torch.cuda.synchronize()
-        del c13, c2, s13, s2, a13, a2
-
-    def sync_words(self):
-        """The single-launch kernel's synchronisation words (word 2: spin timeout)."""
-        import numpy as np
-
-        return self.ws[: 4 * (4 + self.w.E)].cpu().numpy().view(np.uint32)
-
-
 def build_layer(w, device):
     """Device inputs (seeded generators) and the layer with library-quantised,
     prepared weights."""
@@ -150,6 +97,7 @@ def build_layer(w, device):
 
     import mixture_experts_layer_sort_amd as lib
     import moe_inputs as mi
+    from mixture_experts_layer_sort_amd.device import Layer
 
     layer = Layer(lib, w, device)
     x = mi.device_x(w, device)
@@ -369,8 +317,12 @@ def main():
     ids_t = torch.empty(w.T, w.k, dtype=torch.int32, device=device)
     wts_t = torch.empty(w.T, w.k, dtype=torch.float32, device=device)
 
+    # knobs resolved once, as a serving engine would: the package's knob cache, else the defaults
+    knobs, cache_hit = lib.moe_knob_cache_lookup(layer.shape, w.T)
+
     def forward():
-        lib.moe_forward(layer.shape, w.T, layer.packed, logits, x, out, layer.ws, topk_ids=ids_t, topk_w=wts_t)
+        lib.moe_forward_knobs(layer.shape, w.T, layer.packed, logits, x, out, layer.ws, knobs, topk_ids=ids_t,
+                              topk_w=wts_t)
 
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=device)  # 1 GiB
     flush_sink = torch.empty((), dtype=torch.float32, device=device)
@@ -424,6 +376,26 @@ def main():
     g_ms = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
     graph_ms_step = g_ms[len(g_ms) // 2]
     del graph
+
+    # the in-kernel fc2 reduce (a correctness knob: outputs not bitwise
+    # reproducible), flushed and timed like the eager steps (context)
+    fc2_ms_step = None
+    if w.k >= 2:
+        fc2_knobs = lib.make_knobs(knobs.gemm, knobs.down_fp8, knobs.band_rows, 1)
+
+        def forward_fc2():
+            lib.moe_forward_knobs(layer.shape, w.T, layer.packed, logits, x, out, layer.ws, fc2_knobs)
+
+        for _ in range(3):
+            forward_fc2()
+        for i in range(args.steps):
+            flush(i)
+            starts[i].record()
+            forward_fc2()
+            ends[i].record()
+        torch.cuda.synchronize()
+        f_ms = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+        fc2_ms_step = f_ms[len(f_ms) // 2]
 
     # back to back, unflushed (context): one event pair around K steps
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -501,7 +473,7 @@ def main():
         "data": "synthetic (seeded N(0,1) x and logits, N(0,0.02) weights; random init)",
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.k,
                    "weights": w.dtype, "activation": w.act, "weight_alpha_folded": w.fold, "routing_skew": w.bias,
-                   "active_experts": n_active},
+                   "active_experts": n_active, "knobs": knobs.as_dict(), "knob_cache_hit": cache_hit},
         "roofline": roof,
         "layer": {"algorithmic_bytes": B, "flops": F, "gpu_ms_per_step": gpu_ms_step, "hbm_gbs": layer_gbs,
                   "hbm_frac": layer_gbs / HBM_PEAK_GBS, "mfma_tflops": tflops,
@@ -511,7 +483,11 @@ def main():
                   "step_ms_min_median_max": [step_ms[0], ms_step, step_ms[-1]],
                   "back_to_back_unflushed_ms_per_step": b2b_ms_step,
                   "graph_replay_ms_per_step": graph_ms_step,
-                  "single_launch_ms_per_step": fused_ms},
+                  "fc2_reduce_ms_per_step": fc2_ms_step,
+                  "single_launch_ms_per_step": fused_ms,
+                  # the staged entry points run the default knobs; the roofline kernel is the step's
+                  # own kernel when the resolved knobs are the defaults
+                  "staged_knobs_are_step_knobs": knobs.as_dict() == lib.moe_default_knobs().as_dict()},
         "achievable": achievable,
     }
     if not args.no_cpu_baseline:

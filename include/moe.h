@@ -336,6 +336,66 @@ MOE_API moe_status moe_forward_noalloc(const moe_shape* shape, int32_t T, const 
                                        const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
                                        hipStream_t stream);
 
+/* Knobs of one layer call: how the grouped GEMMs run (the pages separate
+ * correctness knobs, which change the code path or the output bits, from
+ * performance knobs, which leave the output unchanged, and resolve knobs once
+ * per buffer capacity from a persistent knob cache with a default heuristic
+ * as fallback, a plain lookup with no compilation [MegaMoE drop workflow,
+ * §4 step 3 (the knob split of the tuner) and §6 (knob resolution, the fc2
+ * reduce)]).  Every kernel variant is compiled into the library; knobs only
+ * choose among them.
+ *   gemm       0: by the rows per expert (T k / E; the default heuristic);
+ *              1: decode-shaped items with 16-row token tiles; 2: decode-shaped
+ *              items with 32-row token tiles; 3: prefill-shaped items (128
+ *              rows, LDS-staged; 256 rows on the fp8 instruction).
+ *              Correctness knob: the fp32 accumulation order of the
+ *              contractions differs between variants.
+ *   down_fp8   MXFP8 layers, prefill-shaped down GEMM: 1 (default) on the
+ *              block-scaled fp8 matrix instruction, 0 on bf16 products of the
+ *              widened codes.  Correctness knob (accumulation order); ignored
+ *              by other formats.
+ *   band_rows  prefill-shaped items: token rows of one band of the item order
+ *              (consecutive items share weight tiles within a band); 0 = 1024.
+ *              Performance knob: the output bits do not change.
+ *   fc2_reduce 1: the down GEMM adds w * y into an fp32 accumulator of the
+ *              token's output row with atomics and no y rows are written; the
+ *              summation order then depends on scheduling, so outputs are
+ *              not bitwise reproducible.  0 (default): y rows and the
+ *              deterministic slot-order combine.  Needs top_k >= 2 (the
+ *              accumulator lives in the y region of the workspace). */
+typedef struct moe_knobs {
+  int32_t gemm;
+  int32_t down_fp8;
+  int32_t band_rows;
+  int32_t fc2_reduce;
+} moe_knobs;
+
+/* The default knobs: {0, 1, 0, 0}. */
+MOE_API void moe_default_knobs(moe_knobs* knobs);
+
+/* moe_forward with explicit knobs (NULL = the defaults).  Same arguments and
+ * workspace as moe_forward; with the default knobs the results are bitwise
+ * those of moe_forward.  MOE_ERR_INVALID_ARG for a knob out of range (gemm
+ * outside [0, 3], down_fp8 / fc2_reduce outside {0, 1}, band_rows outside
+ * [0, 2^20]); MOE_ERR_UNSUPPORTED for fc2_reduce with top_k == 1. */
+MOE_API moe_status moe_forward_knobs(const moe_shape* shape, int32_t T, const void* packed, const float* logits,
+                                     const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
+                                     void* ws, size_t ws_bytes, const moe_knobs* knobs, hipStream_t stream);
+
+/* Persistent knob cache lookup (host only, no device work).  The cache is a
+ * text file of lines
+ *     dtype act hidden inter experts top_k t_min t_max : gemm down_fp8 band_rows fc2_reduce
+ * (dtype: bf16 | mxfp8 | nvfp4 | bf16_mxfp8; act: swiglu | relu2; '#' starts
+ * a comment).  The first line whose shape matches `shape` and whose token
+ * range t_min <= T <= t_max holds T fills *knobs and sets *found = 1;
+ * otherwise *knobs = the defaults and *found = 0.  Pass T = the buffer
+ * capacity (max_tokens) to resolve knobs once per workspace, as the pages
+ * do, or the call's own T.  A missing file is no error (*found = 0);
+ * MOE_ERR_INVALID_ARG for NULL arguments or a malformed line (*found = 0,
+ * *knobs = the defaults). */
+MOE_API moe_status moe_knob_cache_lookup(const char* path, const moe_shape* shape, int32_t T, moe_knobs* knobs,
+                                         int32_t* found);
+
 /* Zero the synchronisation words at the start of a workspace (enqueued on
  * `stream`); needed once per workspace before moe_forward_fused. */
 MOE_API moe_status moe_workspace_init(const moe_shape* shape, void* ws, size_t ws_bytes, hipStream_t stream);

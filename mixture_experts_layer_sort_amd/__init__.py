@@ -45,6 +45,9 @@ EXPORTED = [
     "moe_forward",
     "moe_forward_fused",
     "moe_forward_noalloc",
+    "moe_default_knobs",
+    "moe_forward_knobs",
+    "moe_knob_cache_lookup",
     "moe_workspace_init",
     "moe_batched_workspace_bytes",
     "moe_batched_experts",
@@ -75,6 +78,30 @@ class moe_shape(ctypes.Structure):
         return (f"moe_shape(H={self.hidden}, I={self.inter}, E={self.num_experts}, k={self.top_k}, "
                 f"max_tokens={self.max_tokens}, dtype={self.dtype}, activation={self.activation}, "
                 f"gate_up_limit={self.gate_up_limit})")
+
+
+class moe_knobs(ctypes.Structure):
+    """How the grouped GEMMs of one call run (gemm variant 0 auto / 1 decode
+    16-row / 2 decode 32-row / 3 prefill; MXFP8 fp8 down GEMM; prefill band
+    rows; in-kernel fc2 reduce)."""
+
+    _fields_ = [
+        ("gemm", ctypes.c_int32),
+        ("down_fp8", ctypes.c_int32),
+        ("band_rows", ctypes.c_int32),
+        ("fc2_reduce", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+    def __repr__(self):
+        return "moe_knobs(" + ", ".join(f"{k}={v}" for k, v in self.as_dict().items()) + ")"
+
+
+# the knob cache shipped with the package (written by mixture_experts_layer_sort_amd.tune);
+# the environment variable MOE_KNOB_CACHE names another file
+KNOB_CACHE_PATH = os.path.join(_PKG_DIR, "knob_cache.txt")
 
 
 def make_shape(hidden, inter, num_experts, top_k, max_tokens, dtype, activation="swiglu",
@@ -111,6 +138,10 @@ def _load():
         "moe_forward": (I32, [S, I32, P, P, P, P, P, P, P, SZ, P]),
         "moe_forward_fused": (I32, [S, I32, P, P, P, P, P, P, P, SZ, P]),
         "moe_forward_noalloc": (I32, [S, I32, P, P, P, P, P, P, P]),
+        "moe_default_knobs": (None, [ctypes.POINTER(moe_knobs)]),
+        "moe_forward_knobs": (I32, [S, I32, P, P, P, P, P, P, P, SZ, ctypes.POINTER(moe_knobs), P]),
+        "moe_knob_cache_lookup": (I32, [ctypes.c_char_p, S, I32, ctypes.POINTER(moe_knobs),
+                                        ctypes.POINTER(ctypes.c_int32)]),
         "moe_batched_workspace_bytes": (SZ, [S, I32]),
         "moe_batched_experts": (I32, [S, I32, P, P, P, P, P, SZ, P]),
         "moe_nvfp4_linear_packed_bytes": (SZ, [I32, I32]),
@@ -279,6 +310,36 @@ def moe_forward_noalloc(shape, T, packed, logits, x, out, topk_ids=None, topk_w=
     """moe_forward with its intermediates in the library's static device scratch (no workspace)."""
     _check(_lib.moe_forward_noalloc(ctypes.byref(shape), T, _ptr(packed), _ptr(logits), _ptr(x), _ptr(out),
                                     _ptr(topk_ids), _ptr(topk_w), _stream(stream)), "moe_forward_noalloc")
+
+
+def moe_default_knobs() -> moe_knobs:
+    kn = moe_knobs()
+    _lib.moe_default_knobs(ctypes.byref(kn))
+    return kn
+
+
+def make_knobs(gemm=0, down_fp8=1, band_rows=0, fc2_reduce=0) -> moe_knobs:
+    return moe_knobs(gemm, down_fp8, band_rows, fc2_reduce)
+
+
+def moe_forward_knobs(shape, T, packed, logits, x, out, ws, knobs=None, ws_bytes=None, topk_ids=None, topk_w=None,
+                      stream=None):
+    """moe_forward with explicit knobs (None: the defaults)."""
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    kp = ctypes.byref(knobs) if knobs is not None else None
+    _check(_lib.moe_forward_knobs(ctypes.byref(shape), T, _ptr(packed), _ptr(logits), _ptr(x), _ptr(out),
+                                  _ptr(topk_ids), _ptr(topk_w), _ptr(ws), nbytes, kp, _stream(stream)),
+           "moe_forward_knobs")
+
+
+def moe_knob_cache_lookup(shape, T, path=None):
+    """(knobs, found) for `shape` at T tokens from the knob cache at `path`
+    (default: $MOE_KNOB_CACHE, else the package's knob_cache.txt)."""
+    path = path or os.environ.get("MOE_KNOB_CACHE") or KNOB_CACHE_PATH
+    kn, found = moe_knobs(), ctypes.c_int32(0)
+    _check(_lib.moe_knob_cache_lookup(os.fsencode(path), ctypes.byref(shape), T, ctypes.byref(kn),
+                                      ctypes.byref(found)), "moe_knob_cache_lookup")
+    return kn, bool(found.value)
 
 
 def moe_workspace_init(shape, ws, ws_bytes=None, stream=None):

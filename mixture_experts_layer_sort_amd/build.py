@@ -9,6 +9,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
@@ -37,16 +39,30 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the MoE library)")
 
 
-def _compile(srcs, out, verbose):
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(PKG_DIR, "..", "include"), "-o", tmp, *srcs]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed with status {r.returncode}")
-    os.replace(tmp, out)
+
+
+def _compile(srcs, out, verbose):
+    """Each source to an object in parallel (the translation units share no
+    device code), then one link."""
+    inc = ["-I", os.path.join(PKG_DIR, "..", "include")]
+    cflags = [f for f in FLAGS if f not in ("-shared",)]
+    with tempfile.TemporaryDirectory(prefix="moe_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in srcs]
+        jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(jobs) as pool:
+            for f in [pool.submit(_run, [hipcc(), *cflags, *inc, "-c", "-o", o, src], verbose)
+                      for src, o in zip(srcs, objs)]:
+                f.result()
+        tmp = out + ".tmp"
+        _run([hipcc(), *FLAGS, "-o", tmp, *objs], verbose)
+        os.replace(tmp, out)
 
 
 def build(verbose: bool = False) -> str:

@@ -3,6 +3,9 @@
 // reads device data.
 #include <atomic>
 #include <climits>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "../../include/moe.h"
 #include "moe_kernels.h"
@@ -30,12 +33,13 @@ int device_cu_count() {
 // occupancy of each GEMM variant, per device: [dev][dt][g13][variant], variant 3 = the fp8 prefill GEMM
 std::atomic<int> g_occ[kMaxDevices][3][2][4];
 
-int gemm_grid(int layer_dt, bool g13, int T, int k, int E) {
+// Persistent grid of one grouped GEMM under plan p.
+int gemm_grid(int layer_dt, bool g13, const GemmPlan& p) {
   const int dt = weight_dt(layer_dt);  // the kernels are those of the weight format
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  int v = gemm_variant(T, k, E);
-  if (v == 2 && has_fp8_gemm(layer_dt)) v = 3;
+  int v = p.variant;
+  if (v == 2 && !g13 && p.down_fp8 && has_fp8_gemm(layer_dt)) v = 3;
   int occ = 1;
   if (dev >= 0 && dev < kMaxDevices) {
     occ = g_occ[dev][dt][g13][v].load(std::memory_order_relaxed);
@@ -46,6 +50,15 @@ int gemm_grid(int layer_dt, bool g13, int T, int k, int E) {
     }
   }
   return device_cu_count() * occ;
+}
+
+// The plan of the default knobs for R routed rows (T tokens x k slots): the
+// GEMM variant follows the rows per expert, the fp8 down GEMM is on.
+GemmPlan default_plan(int T, int k, int E, float limit) {
+  GemmPlan p;
+  p.variant = gemm_variant(T, k, E);
+  p.limit = limit;
+  return p;
 }
 
 // co-resident blocks of the fused kernel, per device: [dev][dt][variant]; -1 = unusable
@@ -251,9 +264,10 @@ moe_status moe_gemm13_swiglu_quant(const moe_shape* s, int32_t T, const void* pa
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!packed || !offsets || !sorted_pairs || !xq || !hq) return MOE_ERR_INVALID_ARG;
+  const GemmPlan p = default_plan(T, s->top_k, s->num_experts, s->gate_up_limit);
   return launched(launch_gemm13(s->dtype, gated(s), s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
-                                offsets, sorted_pairs, (const uint8_t*)xq, (uint8_t*)hq,
-                                gemm_grid(s->dtype, true, T, s->top_k, s->num_experts), stream, s->gate_up_limit));
+                                offsets, sorted_pairs, (const uint8_t*)xq, (uint8_t*)hq, gemm_grid(s->dtype, true, p),
+                                stream, p));
 }
 
 moe_status moe_gemm2(const moe_shape* s, int32_t T, const void* packed, const int32_t* offsets,
@@ -265,9 +279,9 @@ moe_status moe_gemm2(const moe_shape* s, int32_t T, const void* packed, const in
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!packed || !offsets || !sorted_pairs || !hq || !y) return MOE_ERR_INVALID_ARG;
+  const GemmPlan p = default_plan(T, s->top_k, s->num_experts, s->gate_up_limit);
   return launched(launch_gemm2(s->dtype, gated(s), s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
-                               offsets, sorted_pairs, (const uint8_t*)hq, y,
-                               gemm_grid(s->dtype, false, T, s->top_k, s->num_experts), stream));
+                               offsets, sorted_pairs, (const uint8_t*)hq, y, gemm_grid(s->dtype, false, p), stream, p));
 }
 
 moe_status moe_combine(const moe_shape* s, int32_t T, const uint16_t* y, const float* topk_w, uint16_t* out,
@@ -291,10 +305,13 @@ static moe_status check_forward(const moe_shape* s, int32_t T, const void* packe
 }
 
 // The five stage kernels of the layer on `stream`, intermediates in the
-// workspace at `base` laid out for `cap` tokens (cap >= T).
+// workspace at `base` laid out for `cap` tokens (cap >= T), the GEMMs as plan
+// p says.  With fc2 (the in-kernel fc2 reduce, top_k >= 2) the down GEMM
+// adds w * y into an fp32 [T, H] accumulator in the y region (T H 4 bytes <=
+// cap k H 2 bytes), zeroed first, and the combine becomes a conversion to bf16.
 static moe_status forward_staged(const moe_shape* s, int32_t T, int cap, const void* packed, const float* logits,
                                  const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w, uint8_t* base,
-                                 hipStream_t stream) {
+                                 GemmPlan p, bool fc2, hipStream_t stream) {
   const int dt = s->dtype, E = s->num_experts, H = s->hidden, I = s->inter, k = s->top_k;
   const WorkspaceLayout W = workspace_layout(dt, E, H, I, k, cap);
   int32_t* ids = topk_ids ? topk_ids : (int32_t*)(base + W.ids);
@@ -305,16 +322,21 @@ static moe_status forward_staged(const moe_shape* s, int32_t T, int cap, const v
   uint8_t* xq = act_dt(dt) == DT_BF16 ? (uint8_t*)x : base + W.xq;  // bf16 activations are used in place
   uint8_t* hq = base + W.hq;
   uint16_t* y = (uint16_t*)(base + W.y);
+  float* acc = fc2 ? (float*)(base + W.y) : nullptr;
+  p.red = acc;
+  p.wts = acc ? wts : nullptr;
   hipError_t e = launch_route(logits, T, E, k, ids, wts, stream);
   if (e == hipSuccess)
     e = launch_permute(dt, ids, T, k, E, H, offsets, sorted_pairs, pair_pos, x, xq, stream);
   if (e == hipSuccess)
     e = launch_gemm13(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, xq, hq,
-                      gemm_grid(dt, true, T, k, E), stream, s->gate_up_limit);
+                      gemm_grid(dt, true, p), stream, p);
+  if (e == hipSuccess && acc) e = launch_zero_f32(acc, (long long)T * H, stream);
   if (e == hipSuccess)
     e = launch_gemm2(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, hq, y,
-                     gemm_grid(dt, false, T, k, E), stream);
-  if (e == hipSuccess) e = launch_combine(T, H, k, y, wts, out, stream);
+                     gemm_grid(dt, false, p), stream, p);
+  if (e == hipSuccess) e = acc ? launch_f32_to_bf16(acc, out, (long long)T * H, stream)
+                               : launch_combine(T, H, k, y, wts, out, stream);
   return launched(e);
 }
 
@@ -323,7 +345,33 @@ moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const 
                        hipStream_t stream) {
   moe_status st = check_forward(s, T, packed, logits, x, out, ws, ws_bytes);
   if (st != MOE_OK || T == 0) return st;
-  return forward_staged(s, T, s->max_tokens, packed, logits, x, out, topk_ids, topk_w, (uint8_t*)ws, stream);
+  return forward_staged(s, T, s->max_tokens, packed, logits, x, out, topk_ids, topk_w, (uint8_t*)ws,
+                        default_plan(T, s->top_k, s->num_experts, s->gate_up_limit), false, stream);
+}
+
+void moe_default_knobs(moe_knobs* kn) {
+  if (kn) *kn = moe_knobs{0, 1, 0, 0};
+}
+
+moe_status moe_forward_knobs(const moe_shape* s, int32_t T, const void* packed, const float* logits,
+                             const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w, void* ws,
+                             size_t ws_bytes, const moe_knobs* knobs, hipStream_t stream) {
+  moe_knobs kn;
+  moe_default_knobs(&kn);
+  if (knobs) kn = *knobs;
+  if (kn.gemm < 0 || kn.gemm > 3 || (kn.down_fp8 | 1) != 1 || (kn.fc2_reduce | 1) != 1 || kn.band_rows < 0 ||
+      kn.band_rows > (1 << 20))
+    return MOE_ERR_INVALID_ARG;
+  moe_status st = check_forward(s, T, packed, logits, x, out, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (kn.fc2_reduce && s->top_k < 2) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  GemmPlan p = default_plan(T, s->top_k, s->num_experts, s->gate_up_limit);
+  if (kn.gemm > 0) p.variant = kn.gemm - 1;
+  p.down_fp8 = kn.down_fp8 != 0;
+  p.band = kn.band_rows;
+  return forward_staged(s, T, s->max_tokens, packed, logits, x, out, topk_ids, topk_w, (uint8_t*)ws, p,
+                        kn.fc2_reduce != 0, stream);
 }
 
 moe_status moe_forward_noalloc(const moe_shape* s, int32_t T, const void* packed, const float* logits,
@@ -337,7 +385,8 @@ moe_status moe_forward_noalloc(const moe_shape* s, int32_t T, const void* packed
   uint8_t* base = scratch_address();
   if (!base) return MOE_ERR_LAUNCH;
   // every intermediate is written before it is read: nothing needs clearing
-  return forward_staged(s, T, T, packed, logits, x, out, topk_ids, topk_w, base, stream);
+  return forward_staged(s, T, T, packed, logits, x, out, topk_ids, topk_w, base,
+                        default_plan(T, s->top_k, s->num_experts, s->gate_up_limit), false, stream);
 }
 
 size_t moe_batched_workspace_bytes(const moe_shape* s, int32_t max_rows) {
@@ -360,13 +409,14 @@ moe_status moe_batched_experts(const moe_shape* s, int32_t max_rows, const int32
   uint8_t* xq = act_dt(dt) == DT_BF16 ? (uint8_t*)x : base + B.xq;  // bf16 activations are used in place
   uint8_t* hq = base + B.hq;
   // one "pair" per valid row (k = 1, R rows of capacity): the GEMM variants follow the rows per expert
+  const GemmPlan p = default_plan(R, 1, E, s->gate_up_limit);
   hipError_t e = launch_batched_prep(dt, counts, E, max_rows, H, offsets, rows, x, xq, stream);
   if (e == hipSuccess)
     e = launch_gemm13(dt, gated(s), E, H, I, 1, R, (const uint8_t*)packed, offsets, rows, xq, hq,
-                      gemm_grid(dt, true, R, 1, E), stream, s->gate_up_limit);
+                      gemm_grid(dt, true, p), stream, p);
   if (e == hipSuccess)
     e = launch_gemm2(dt, gated(s), E, H, I, 1, R, (const uint8_t*)packed, offsets, rows, hq, y,
-                     gemm_grid(dt, false, R, 1, E), stream);
+                     gemm_grid(dt, false, p), stream, p);
   return launched(e);
 }
 
@@ -407,7 +457,7 @@ moe_status moe_nvfp4_linear(int32_t M, int32_t N, int32_t K, const void* packed,
   hipError_t e = launch_dense_prep(M, K, offsets, rows, x, xq, stream);
   if (e == hipSuccess)
     e = launch_dense_gemm(M, N, K, (const uint8_t*)packed, offsets, rows, xq, out,
-                          gemm_grid(MOE_NVFP4, false, M, 1, 1), stream);
+                          gemm_grid(MOE_NVFP4, false, default_plan(M, 1, 1, 0.f)), stream);
   return launched(e);
 }
 
@@ -425,6 +475,68 @@ moe_status moe_forward_fused(const moe_shape* s, int32_t T, const void* packed, 
   if (grid <= 0) return MOE_ERR_UNSUPPORTED;
   return launched(launch_fused(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, logits, x, out, ids, wts, base, ws_bytes,
                                s->max_tokens, grid, stream, s->gate_up_limit));
+}
+
+static int parse_dtype(const char* t) {
+  static const char* names[] = {"bf16", "mxfp8", "nvfp4", "bf16_mxfp8"};
+  for (int i = 0; i < 4; ++i)
+    if (!strcmp(t, names[i])) return i;
+  return -1;
+}
+
+moe_status moe_knob_cache_lookup(const char* path, const moe_shape* s, int32_t T, moe_knobs* knobs,
+                                 int32_t* found) {
+  if (!path || !s || !knobs || !found) return MOE_ERR_INVALID_ARG;
+  moe_default_knobs(knobs);
+  *found = 0;
+  FILE* f = fopen(path, "r");
+  if (!f) return MOE_OK;
+  char line[512];
+  moe_status st = MOE_OK;
+  while (fgets(line, sizeof line, f)) {
+    if (char* c = strchr(line, '#')) *c = 0;
+    char* tok[13];
+    int n = 0;
+    char* save = nullptr;
+    for (char* t = strtok_r(line, " \t\r\n", &save); t; t = strtok_r(nullptr, " \t\r\n", &save)) {
+      if (n == 13) { n = 14; break; }
+      tok[n++] = t;
+    }
+    if (n == 0) continue;
+    long v[12];
+    bool ok = n == 13 && !strcmp(tok[8], ":");
+    for (int i = 2; ok && i < 13; ++i) {
+      if (i == 8) continue;
+      char* end = nullptr;
+      v[i < 8 ? i : i - 1] = strtol(tok[i], &end, 10);
+      ok = end != tok[i] && *end == 0;
+    }
+    const int dt = ok ? parse_dtype(tok[0]) : -1;
+    const int act = ok ? (!strcmp(tok[1], "swiglu") ? MOE_SWIGLU : !strcmp(tok[1], "relu2") ? MOE_RELU2 : -1) : -1;
+    if (!ok || dt < 0 || act < 0) {
+      st = MOE_ERR_INVALID_ARG;
+      break;
+    }
+    // v[2..7]: hidden inter experts top_k t_min t_max; v[8..11]: the knobs
+    if (dt == s->dtype && act == s->activation && v[2] == s->hidden && v[3] == s->inter && v[4] == s->num_experts &&
+        v[5] == s->top_k && v[6] <= T && T <= v[7]) {
+      const moe_knobs kn{(int32_t)v[8], (int32_t)v[9], (int32_t)v[10], (int32_t)v[11]};
+      if (kn.gemm < 0 || kn.gemm > 3 || (kn.down_fp8 | 1) != 1 || (kn.fc2_reduce | 1) != 1 || kn.band_rows < 0 ||
+          kn.band_rows > (1 << 20) || v[8] != kn.gemm || v[10] != kn.band_rows) {
+        st = MOE_ERR_INVALID_ARG;
+        break;
+      }
+      *knobs = kn;
+      *found = 1;
+      break;
+    }
+  }
+  fclose(f);
+  if (st != MOE_OK) {
+    moe_default_knobs(knobs);
+    *found = 0;
+  }
+  return st;
 }
 
 }  // extern "C"

@@ -177,7 +177,7 @@ int gemm_blocks_per_cu(int dt, bool g13, int nt) {
 
 hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
                          const int* offsets, const int* sorted_pairs, const uint8_t* xq, uint8_t* hq, int grid,
-                         hipStream_t s, float limit) {
+                         hipStream_t s, const GemmPlan& plan) {
   const PackedLayout L = packed_layout(dt, E, H, I, gated);
   GemmArgs a;
   a.wcodes = packed + L.w13_codes;
@@ -192,15 +192,18 @@ hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, 
   a.act_scales = nullptr;
   a.act_bf16 = dt == DT_BF16_MXFP8;
   a.gated = gated;
-  a.limit = gated ? limit : 0.f;
+  a.limit = gated ? plan.limit : 0.f;
+  a.band = plan.band;
+  a.red = nullptr;
+  a.wts = nullptr;
   a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
-  if (gemm_prefill(T, k, E)) return launch_prefill(weight_dt(dt), true, a, grid, s);
-  return dispatch_gemm<true>(weight_dt(dt), gemm_nt(T, k, E), a, grid, s);
+  if (plan.variant == 2) return launch_prefill(weight_dt(dt), true, a, grid, s);
+  return dispatch_gemm<true>(weight_dt(dt), plan.variant + 1, a, grid, s);
 }
 
 hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
                         const int* offsets, const int* sorted_pairs, const uint8_t* hq, uint16_t* y, int grid,
-                        hipStream_t s) {
+                        hipStream_t s, const GemmPlan& plan) {
   const PackedLayout L = packed_layout(dt, E, H, I, gated);
   GemmArgs a;
   a.wcodes = packed + L.w2_codes;
@@ -216,15 +219,44 @@ hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, c
   a.act_bf16 = dt == DT_BF16_MXFP8;
   a.gated = gated;
   a.limit = 0.f;
+  a.band = plan.band;
+  a.red = plan.red;
+  a.wts = plan.wts;
   a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
-  if (gemm_prefill(T, k, E) && has_fp8_gemm(dt)) {
+  if (plan.variant == 2 && plan.down_fp8 && has_fp8_gemm(dt)) {
     a.wcodes = packed + L.w2_frag;
     a.act = hq;  // e4m3 codes
     a.act_scales = hq + act_scale_offset(dt, T * k, I);
     return launch_prefill_f8(false, a, grid, s);
   }
-  if (gemm_prefill(T, k, E)) return launch_prefill(weight_dt(dt), false, a, grid, s);
-  return dispatch_gemm<false>(weight_dt(dt), gemm_nt(T, k, E), a, grid, s);
+  if (plan.variant == 2) return launch_prefill(weight_dt(dt), false, a, grid, s);
+  return dispatch_gemm<false>(weight_dt(dt), plan.variant + 1, a, grid, s);
+}
+
+__global__ void zero_f32_kernel(float* __restrict__ p, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n / 4; i += (long long)gridDim.x * blockDim.x)
+    reinterpret_cast<float4*>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__global__ void f32_to_bf16_kernel(const float* __restrict__ acc, uint16_t* __restrict__ out, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n / 4; i += (long long)gridDim.x * blockDim.x) {
+    const float4 v = reinterpret_cast<const float4*>(acc)[i];
+    reinterpret_cast<uint2*>(out)[i] = make_uint2(f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                                                  f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16));
+  }
+}
+
+// (n is a multiple of 4: rows of H % 128 == 0 values)
+hipError_t launch_zero_f32(float* p, long long n, hipStream_t s) {
+  const int blocks = (int)std::min((n / 4 + 255) / 256, 65536LL);
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_to_bf16(const float* acc, uint16_t* out, long long n, hipStream_t s) {
+  const int blocks = (int)std::min((n / 4 + 255) / 256, 65536LL);
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, s, acc, out, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_dense_prepare(int N, int K, const uint8_t* codes, const uint8_t* scales, const float* alpha,
@@ -257,6 +289,9 @@ hipError_t launch_dense_gemm(int M, int N, int K, const uint8_t* packed, const i
   a.act_bf16 = 0;
   a.gated = 0;
   a.limit = 0.f;
+  a.band = 0;
+  a.red = nullptr;
+  a.wts = nullptr;
   a.E = 1; a.K = K; a.G = D.G; a.KG = D.KG; a.k = 1; a.n_out = N;
   if (gemm_prefill(M, 1, 1)) return launch_prefill(DT_NVFP4, false, a, grid, s);
   return dispatch_gemm<false>(DT_NVFP4, gemm_nt(M, 1, 1), a, grid, s);

@@ -23,6 +23,10 @@ struct GemmArgs {
   int act_bf16;               // MXFP8 weights with bf16 activations: the intermediate is rounded to bf16
   int gated;                  // gate/up GEMM: 1 SwiGLU (gate/up row pairs), 0 ReLU^2 (64 W1 rows per group)
   float limit;                // SwiGLU gate/up clamp L (0: none): gate = min(gate, L), up = clamp(up, -L, L)
+  int band;                   // prefill item order: token rows per band (0: the kernel's default, 1024)
+  float* red;                 // down GEMM, in-kernel fc2 reduce: fp32 out [T, H] += wts[p] * y[p] (atomics);
+                              // null: y rows are written
+  const float* wts;           // the router weights of the pairs (with red)
   int E, K, G, KG, k, n_out;
 };
 
@@ -386,13 +390,22 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
     } else {
       if (ok) {
         const int p = a.sorted_pairs[r];
-        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)p * a.n_out + 64 * g + 4 * q;
+        if (a.red) {  // in-kernel fc2 reduce: w * y added to the token's fp32 output row
+          const float wp = a.wts[p];
+          float* o = a.red + (size_t)(p / a.k) * a.n_out + 64 * g + 4 * q;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          uint2 v;
-          v.x = f32_to_bf16(acc[t][s][0] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][1] * alpha) << 16);
-          v.y = f32_to_bf16(acc[t][s][2] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][3] * alpha) << 16);
-          *reinterpret_cast<uint2*>(o + 16 * t) = v;
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) unsafeAtomicAdd(o + 16 * t + j, wp * (acc[t][s][j] * alpha));
+        } else {
+          uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)p * a.n_out + 64 * g + 4 * q;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            uint2 v;
+            v.x = f32_to_bf16(acc[t][s][0] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][1] * alpha) << 16);
+            v.y = f32_to_bf16(acc[t][s][2] * alpha) | ((uint32_t)f32_to_bf16(acc[t][s][3] * alpha) << 16);
+            *reinterpret_cast<uint2*>(o + 16 * t) = v;
+          }
         }
       }
     }

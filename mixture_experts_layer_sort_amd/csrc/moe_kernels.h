@@ -42,14 +42,34 @@ hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t
                           const float* w13a, const uint8_t* w2, const uint8_t* w2s, const float* w2a, uint8_t* packed,
                           hipStream_t s);
 
-// Grouped GEMMs.  `grid` is the persistent grid size (blocks).
+// How the grouped GEMMs of one call run: the kernel variant (0: decode items
+// with 16-row token tiles, 1: 32-row token tiles, 2: prefill items), whether
+// an MXFP8 layer's prefill-shaped down GEMM runs on the fp8 instruction, the
+// prefill item band (token rows per band of weight reuse; 0: the kernel's
+// default), the SwiGLU clamp and
+// the optional in-kernel fc2 reduce of the down GEMM (red: fp32 [T, H] output
+// rows, wts: the router weights of the pairs).
+struct GemmPlan {
+  int variant = 0;
+  bool down_fp8 = true;
+  int band = 0;
+  float limit = 0.f;
+  float* red = nullptr;
+  const float* wts = nullptr;
+};
+
+// Grouped GEMMs.  `grid` is the persistent grid size (blocks) of the plan's variant.
 hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
                          const int* offsets, const int* sorted_pairs, const uint8_t* xq, uint8_t* hq, int grid,
-                         hipStream_t s, float limit = 0.f);
+                         hipStream_t s, const GemmPlan& plan);
 
 hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, const uint8_t* packed,
                         const int* offsets, const int* sorted_pairs, const uint8_t* hq, uint16_t* y, int grid,
-                        hipStream_t s);
+                        hipStream_t s, const GemmPlan& plan);
+
+// fp32 rows [n] = 0 (a fill kernel: safe under graph capture); bf16 out [n] = rne(acc [n])
+hipError_t launch_zero_f32(float* p, long long n, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* acc, uint16_t* out, long long n, hipStream_t s);
 
 hipError_t launch_combine(int T, int H, int k, const uint16_t* y, const float* wts, uint16_t* out, hipStream_t s);
 

@@ -107,7 +107,14 @@ __device__ __forceinline__ void f8_down_epilogue(const GemmArgs& a, f32x16_t (&a
   const int hl = lane >> 5;
 #pragma unroll
   for (int S = 0; S < NSA; ++S) {
-    if (pidx[S] >= 0) {
+    if (pidx[S] >= 0 && a.red) {  // in-kernel fc2 reduce: w * y added to the token's fp32 output row
+      const float wp = a.wts[pidx[S]];
+      float* o = a.red + (size_t)(pidx[S] / a.k) * a.n_out + 64 * g + 4 * hl;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) unsafeAtomicAdd(o + 32 * f + 8 * (i >> 2) + (i & 3), wp * acc[f][S][i]);
+    } else if (pidx[S] >= 0) {
       uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)pidx[S] * a.n_out + 64 * g + 4 * hl;
 #pragma unroll
       for (int f = 0; f < 2; ++f)
@@ -131,7 +138,7 @@ __device__ __forceinline__ void f8_down_epilogue(const GemmArgs& a, f32x16_t (&a
 // free for reuse.
 template <bool G13>
 __device__ __forceinline__ int f8_item(const GemmArgs& a, long long w, const int* cum, const F8Stages& st) {
-  constexpr int kBand = pf_band<kF8Rows>();
+  const int kBand = a.band > 0 ? max(1, a.band / kF8Rows) : pf_band<kF8Rows>();
   const int tid = threadIdx.x, lane = tid & 63, m = lane & 31, hl = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NB = (a.G + kPfGroups - 1) / kPfGroups;

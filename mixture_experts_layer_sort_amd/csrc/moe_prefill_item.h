@@ -265,16 +265,27 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
     } else {
       if (ok) {
         const int p = a.sorted_pairs[r];
-        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)p * a.n_out + 64 * g + 4 * hl;
+        if (a.red) {  // in-kernel fc2 reduce: w * y added to the token's fp32 output row
+          const float wp = a.wts[p];
+          float* o = a.red + (size_t)(p / a.k) * a.n_out + 64 * g + 4 * hl;
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+          for (int f = 0; f < 2; ++f)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const f32x16_t& v = acc[f][S];
-            *reinterpret_cast<uint2*>(o + 32 * f + 8 * b) =
-                make_uint2(f32_to_bf16(v[4 * b] * alpha) | ((uint32_t)f32_to_bf16(v[4 * b + 1] * alpha) << 16),
-                           f32_to_bf16(v[4 * b + 2] * alpha) | ((uint32_t)f32_to_bf16(v[4 * b + 3] * alpha) << 16));
-          }
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) unsafeAtomicAdd(o + 32 * f + 8 * b + j, wp * (acc[f][S][4 * b + j] * alpha));
+        } else {
+          uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)p * a.n_out + 64 * g + 4 * hl;
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const f32x16_t& v = acc[f][S];
+              *reinterpret_cast<uint2*>(o + 32 * f + 8 * b) =
+                  make_uint2(f32_to_bf16(v[4 * b] * alpha) | ((uint32_t)f32_to_bf16(v[4 * b + 1] * alpha) << 16),
+                             f32_to_bf16(v[4 * b + 2] * alpha) | ((uint32_t)f32_to_bf16(v[4 * b + 3] * alpha) << 16));
+            }
+        }
       }
     }
   }
@@ -305,7 +316,7 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
   constexpr int kSW = kSub / TW;                    // token sub-tiles per wave
   constexpr int kDma = kSub / TW;                   // token loads per wave per K step (4 kSub per block)
   constexpr int kADma = 4 / TW;                     // LDS weights: code loads per wave per K step (16 per block)
-  constexpr int kBand = pf_band<ROWS>();
+  const int kBand = a.band > 0 ? max(1, a.band / ROWS) : pf_band<ROWS>();
   // vector-memory operations per wave per K step
   constexpr int kOps = kDma + (kALds ? kADma + 1 : pf_a_ops<DT>());
   constexpr int kPfStages = pf_stages<DT, ROWS>();

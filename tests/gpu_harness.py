@@ -163,6 +163,12 @@ class DeviceLayer:
         lib.moe_forward_fused(self.shape, T, self.packed, logits, x, out, self.ws, topk_ids=ids, topk_w=wts)
         return out
 
+    def forward_knobs(self, x: torch.Tensor, logits: torch.Tensor, knobs, out=None) -> torch.Tensor:
+        T = x.shape[0]
+        out = torch.empty(T, self.w.H, dtype=torch.bfloat16, device=dev()) if out is None else out
+        lib.moe_forward_knobs(self.shape, T, self.packed, logits, x, out, self.ws, knobs)
+        return out
+
     def sync_words(self) -> np.ndarray:
         """The fused kernel's synchronisation words (zero between launches;
         word 2 is its spin-timeout flag)."""

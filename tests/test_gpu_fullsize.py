@@ -20,6 +20,7 @@ import pytest
 import torch
 
 import gpu_harness as gh
+import mixture_experts_layer_sort_amd as lib
 import moe_inputs as mi
 from oracle import moe as omoe
 from oracle import quant as oquant
@@ -28,6 +29,9 @@ pytestmark = pytest.mark.gpu
 
 W = mi.WORKLOADS
 MAX_SAMPLE_EXPERTS = 16
+# knob settings (gemm, down_fp8, band_rows, fc2_reduce) checked at full size
+KNOB_CASES = {"mxfp8_prefill": [(3, 0, 0, 0), (0, 1, 0, 1), (0, 1, 256, 0), (0, 1, 4096, 0)],
+              "mxfp8_decode": [(3, 0, 512, 0), (2, 1, 0, 0), (0, 1, 0, 1)]}
 
 
 def _log(msg):
@@ -204,5 +208,21 @@ def test_fullsize_parity(name, pool):
                 assert rh <= tol and ry <= tol, (e, row, rh, ry)
                 worst = max(worst, rh, ry)
         _log(f"{name}: sorted-position rows within tolerance (worst relL2 {worst:.2e})")
+
+    if name in KNOB_CASES:
+        # knob settings at full size: every token's output against the default
+        # path's (tolerance), the sampled tokens against the oracle; a band
+        # change alone leaves the bits unchanged
+        base = gh.bf16_numpy(r["out"])
+        for kn in KNOB_CASES[name]:
+            got = gh.bf16_numpy(layer.forward_knobs(x, logits, lib.make_knobs(*kn)))
+            torch.cuda.synchronize()
+            rel, mad = gh.check_out(got[toks], ref.out, w.dtype, f"{name} knobs {kn}")
+            if kn[3] == 0 and kn[1] == 1 and kn[0] == 0:
+                assert np.array_equal(got, base), kn
+            d = gh.rel_l2((got.astype(np.uint32) << 16).view(np.float32),
+                          (base.astype(np.uint32) << 16).view(np.float32))
+            assert d <= gh.out_tolerance(w.dtype), (kn, d)
+            _log(f"{name}: knobs {kn}: sampled out relL2 {rel:.2e} max|d|/rms {mad:.2e}; all tokens vs default {d:.2e}")
     del layer, cw, r, out_fwd, out_fused
     torch.cuda.empty_cache()
