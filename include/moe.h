@@ -377,7 +377,8 @@ MOE_API void moe_default_knobs(moe_knobs* knobs);
  * workspace as moe_forward; with the default knobs the results are bitwise
  * those of moe_forward.  MOE_ERR_INVALID_ARG for a knob out of range (gemm
  * outside [0, 3], down_fp8 / fc2_reduce outside {0, 1}, band_rows outside
- * [0, 2^20]); MOE_ERR_UNSUPPORTED for fc2_reduce with top_k == 1. */
+ * [0, 2^20]); MOE_ERR_UNSUPPORTED for fc2_reduce with top_k == 1, and for
+ * gemm = 1 with more than 16 (65535 - num_experts) routed rows (T top_k). */
 MOE_API moe_status moe_forward_knobs(const moe_shape* shape, int32_t T, const void* packed, const float* logits,
                                      const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
                                      void* ws, size_t ws_bytes, const moe_knobs* knobs, hipStream_t stream);

@@ -365,6 +365,8 @@ moe_status moe_forward_knobs(const moe_shape* s, int32_t T, const void* packed, 
   moe_status st = check_forward(s, T, packed, logits, x, out, ws, ws_bytes);
   if (st != MOE_OK) return st;
   if (kn.fc2_reduce && s->top_k < 2) return MOE_ERR_UNSUPPORTED;
+  // the 16-row decode schedule packs two m-tile prefixes into 16-bit halves
+  if (kn.gemm == 1 && (long long)T * s->top_k > 16LL * (65535 - s->num_experts)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   GemmPlan p = default_plan(T, s->top_k, s->num_experts, s->gate_up_limit);
   if (kn.gemm > 0) p.variant = kn.gemm - 1;

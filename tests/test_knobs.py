@@ -124,6 +124,13 @@ def test_forward_knobs_host_checks():
     # the fc2 accumulator lives in the y region: top_k >= 2 only
     assert h.moe_forward_knobs(ctypes.byref(s1), 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, P(FAKE), ws,
                                ctypes.byref(fc2), None) == UNSUPPORTED
+    # the 16-row decode items' schedule holds at most 65535 m-tiles: forcing
+    # them on more than 16 (65535 - E) routed rows is refused
+    big = lib.make_shape(128, 128, 256, 8, 1 << 18, "bf16")
+    wsb = lib.moe_workspace_bytes(big)
+    T_over = 2 * (65535 - 256) + 1  # top-8: 8 T > 16 (65535 - 256)
+    assert h.moe_forward_knobs(ctypes.byref(big), T_over, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, P(FAKE),
+                               wsb, ctypes.byref(lib.moe_knobs(1, 1, 0, 0)), None) == UNSUPPORTED
     s = lib.make_shape(256, 512, 8, 2, 16, "bf16")
     ws = lib.moe_workspace_bytes(s)
     assert h.moe_forward_knobs(ctypes.byref(s), 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, P(FAKE), ws - 1,
