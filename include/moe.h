@@ -362,22 +362,27 @@ MOE_API moe_status moe_forward_noalloc(const moe_shape* shape, int32_t T, const 
  *              summation order then depends on scheduling, so outputs are
  *              not bitwise reproducible.  0 (default): y rows and the
  *              deterministic slot-order combine.  Needs top_k >= 2 (the
- *              accumulator lives in the y region of the workspace). */
+ *              accumulator lives in the y region of the workspace).
+ *   blocks_per_cu  persistent grid of the grouped GEMMs, blocks per compute
+ *              unit (0: as many as fit at once; 1..16 otherwise; blocks past
+ *              the resident capacity start as earlier ones finish).
+ *              Performance knob. */
 typedef struct moe_knobs {
   int32_t gemm;
   int32_t down_fp8;
   int32_t band_rows;
   int32_t fc2_reduce;
+  int32_t blocks_per_cu;
 } moe_knobs;
 
-/* The default knobs: {0, 1, 0, 0}. */
+/* The default knobs: {0, 1, 0, 0, 0}. */
 MOE_API void moe_default_knobs(moe_knobs* knobs);
 
 /* moe_forward with explicit knobs (NULL = the defaults).  Same arguments and
  * workspace as moe_forward; with the default knobs the results are bitwise
  * those of moe_forward.  MOE_ERR_INVALID_ARG for a knob out of range (gemm
  * outside [0, 3], down_fp8 / fc2_reduce outside {0, 1}, band_rows outside
- * [0, 2^20]); MOE_ERR_UNSUPPORTED for fc2_reduce with top_k == 1, and for
+ * [0, 2^20], blocks_per_cu outside [0, 16]); MOE_ERR_UNSUPPORTED for fc2_reduce with top_k == 1, and for
  * gemm = 1 with more than 16 (65535 - num_experts) routed rows (T top_k). */
 MOE_API moe_status moe_forward_knobs(const moe_shape* shape, int32_t T, const void* packed, const float* logits,
                                      const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
@@ -385,7 +390,7 @@ MOE_API moe_status moe_forward_knobs(const moe_shape* shape, int32_t T, const vo
 
 /* Persistent knob cache lookup (host only, no device work).  The cache is a
  * text file of lines
- *     dtype act hidden inter experts top_k t_min t_max : gemm down_fp8 band_rows fc2_reduce
+ *     dtype act hidden inter experts top_k t_min t_max : gemm down_fp8 band_rows fc2_reduce blocks_per_cu
  * (dtype: bf16 | mxfp8 | nvfp4 | bf16_mxfp8; act: swiglu | relu2; '#' starts
  * a comment).  The first line whose shape matches `shape` and whose token
  * range t_min <= T <= t_max holds T fills *knobs and sets *found = 1;

@@ -40,6 +40,7 @@ int gemm_grid(int layer_dt, bool g13, const GemmPlan& p) {
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
   int v = p.variant;
   if (v == 2 && !g13 && p.down_fp8 && has_fp8_gemm(layer_dt)) v = 3;
+  if (p.blocks_per_cu > 0) return device_cu_count() * p.blocks_per_cu;
   int occ = 1;
   if (dev >= 0 && dev < kMaxDevices) {
     occ = g_occ[dev][dt][g13][v].load(std::memory_order_relaxed);
@@ -350,7 +351,12 @@ moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const 
 }
 
 void moe_default_knobs(moe_knobs* kn) {
-  if (kn) *kn = moe_knobs{0, 1, 0, 0};
+  if (kn) *kn = moe_knobs{0, 1, 0, 0, 0};
+}
+
+static bool knobs_valid(const moe_knobs& kn) {
+  return kn.gemm >= 0 && kn.gemm <= 3 && (kn.down_fp8 | 1) == 1 && (kn.fc2_reduce | 1) == 1 && kn.band_rows >= 0 &&
+         kn.band_rows <= (1 << 20) && kn.blocks_per_cu >= 0 && kn.blocks_per_cu <= 16;
 }
 
 moe_status moe_forward_knobs(const moe_shape* s, int32_t T, const void* packed, const float* logits,
@@ -359,9 +365,7 @@ moe_status moe_forward_knobs(const moe_shape* s, int32_t T, const void* packed, 
   moe_knobs kn;
   moe_default_knobs(&kn);
   if (knobs) kn = *knobs;
-  if (kn.gemm < 0 || kn.gemm > 3 || (kn.down_fp8 | 1) != 1 || (kn.fc2_reduce | 1) != 1 || kn.band_rows < 0 ||
-      kn.band_rows > (1 << 20))
-    return MOE_ERR_INVALID_ARG;
+  if (!knobs_valid(kn)) return MOE_ERR_INVALID_ARG;
   moe_status st = check_forward(s, T, packed, logits, x, out, ws, ws_bytes);
   if (st != MOE_OK) return st;
   if (kn.fc2_reduce && s->top_k < 2) return MOE_ERR_UNSUPPORTED;
@@ -372,6 +376,7 @@ moe_status moe_forward_knobs(const moe_shape* s, int32_t T, const void* packed, 
   if (kn.gemm > 0) p.variant = kn.gemm - 1;
   p.down_fp8 = kn.down_fp8 != 0;
   p.band = kn.band_rows;
+  p.blocks_per_cu = kn.blocks_per_cu;
   return forward_staged(s, T, s->max_tokens, packed, logits, x, out, topk_ids, topk_w, (uint8_t*)ws, p,
                         kn.fc2_reduce != 0, stream);
 }
@@ -497,37 +502,33 @@ moe_status moe_knob_cache_lookup(const char* path, const moe_shape* s, int32_t T
   moe_status st = MOE_OK;
   while (fgets(line, sizeof line, f)) {
     if (char* c = strchr(line, '#')) *c = 0;
-    char* tok[13];
+    constexpr int kKeys = 8, kKnobs = 5, kTok = kKeys + 1 + kKnobs;
+    char* tok[kTok];
     int n = 0;
     char* save = nullptr;
     for (char* t = strtok_r(line, " \t\r\n", &save); t; t = strtok_r(nullptr, " \t\r\n", &save)) {
-      if (n == 13) { n = 14; break; }
+      if (n == kTok) { n = kTok + 1; break; }
       tok[n++] = t;
     }
     if (n == 0) continue;
-    long v[12];
-    bool ok = n == 13 && !strcmp(tok[8], ":");
-    for (int i = 2; ok && i < 13; ++i) {
-      if (i == 8) continue;
+    long v[kKeys + kKnobs] = {};  // v[2..7]: hidden inter experts top_k t_min t_max; v[8..]: the knobs
+    bool ok = n == kTok && !strcmp(tok[kKeys], ":");
+    for (int i = 2; ok && i < kTok; ++i) {
+      if (i == kKeys) continue;
       char* end = nullptr;
-      v[i < 8 ? i : i - 1] = strtol(tok[i], &end, 10);
-      ok = end != tok[i] && *end == 0;
+      const long x = strtol(tok[i], &end, 10);
+      ok = end != tok[i] && *end == 0 && x >= INT_MIN && x <= INT_MAX;
+      v[i < kKeys ? i : i - 1] = x;
     }
     const int dt = ok ? parse_dtype(tok[0]) : -1;
     const int act = ok ? (!strcmp(tok[1], "swiglu") ? MOE_SWIGLU : !strcmp(tok[1], "relu2") ? MOE_RELU2 : -1) : -1;
-    if (!ok || dt < 0 || act < 0) {
+    const moe_knobs kn{(int32_t)v[8], (int32_t)v[9], (int32_t)v[10], (int32_t)v[11], (int32_t)v[12]};
+    if (!ok || dt < 0 || act < 0 || !knobs_valid(kn)) {
       st = MOE_ERR_INVALID_ARG;
       break;
     }
-    // v[2..7]: hidden inter experts top_k t_min t_max; v[8..11]: the knobs
     if (dt == s->dtype && act == s->activation && v[2] == s->hidden && v[3] == s->inter && v[4] == s->num_experts &&
         v[5] == s->top_k && v[6] <= T && T <= v[7]) {
-      const moe_knobs kn{(int32_t)v[8], (int32_t)v[9], (int32_t)v[10], (int32_t)v[11]};
-      if (kn.gemm < 0 || kn.gemm > 3 || (kn.down_fp8 | 1) != 1 || (kn.fc2_reduce | 1) != 1 || kn.band_rows < 0 ||
-          kn.band_rows > (1 << 20) || v[8] != kn.gemm || v[10] != kn.band_rows) {
-        st = MOE_ERR_INVALID_ARG;
-        break;
-      }
       *knobs = kn;
       *found = 1;
       break;

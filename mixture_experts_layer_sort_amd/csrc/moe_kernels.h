@@ -46,13 +46,14 @@ hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t
 // with 16-row token tiles, 1: 32-row token tiles, 2: prefill items), whether
 // an MXFP8 layer's prefill-shaped down GEMM runs on the fp8 instruction, the
 // prefill item band (token rows per band of weight reuse; 0: the kernel's
-// default), the SwiGLU clamp and
+// default), the persistent blocks per compute unit (0: the occupancy limit), the SwiGLU clamp and
 // the optional in-kernel fc2 reduce of the down GEMM (red: fp32 [T, H] output
 // rows, wts: the router weights of the pairs).
 struct GemmPlan {
   int variant = 0;
   bool down_fp8 = true;
   int band = 0;
+  int blocks_per_cu = 0;
   float limit = 0.f;
   float* red = nullptr;
   const float* wts = nullptr;

@@ -7,16 +7,17 @@ For every workload (a synthetic layer shape from moe_inputs) and token count,
 each candidate knob setting runs the whole layer (moe_forward_knobs) for
 `steps` timed steps, each between its own HIP event pair with the L2 and the
 Infinity Cache flushed before it; the candidate with the lowest median step
-time wins (the default knobs win ties within 1 %).  The pages sweep a knob
+time wins (the default knobs win ties within 2 %, about the run-to-run
+spread of the step times).  The pages sweep a knob
 candidate list per shape, keep the winner in a persistent cache keyed by
 shape, and resolve knobs from that cache before a default heuristic
 [MegaMoE drop workflow, §4 step 3 and §6]; here every candidate is already
 compiled into the library, so a sweep costs only the timed runs.
 
 Candidates: the GEMM variant (decode-shaped 16- or 32-row token tiles,
-prefill-shaped items), for prefill-shaped items the band of the item order
-(token rows sharing weight tiles) and, for MXFP8 layers, the fp8 or bf16 down
-GEMM.  The in-kernel fc2 reduce makes outputs non-reproducible; it is a
+prefill-shaped items); for decode-shaped items the persistent blocks per
+compute unit; for prefill-shaped items the band of the item order (token
+rows sharing weight tiles) and, for MXFP8 layers, the fp8 or bf16 down GEMM.  The in-kernel fc2 reduce makes outputs non-reproducible; it is a
 candidate only with --fc2.
 
 Lines of the cache cover token ranges: between two swept token counts of one
@@ -36,19 +37,23 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DEFAULT_WORKLOADS = ("bf16_decode", "mxfp8_decode", "nvfp4_decode_t8", "nvfp4_decode_t128", "mxfp8_prefill")
 BANDS = (0, 256, 512, 2048, 4096, 8192)
+DECODE_BLOCKS = (0, 2, 4, 5, 6, 8)
 MAX_T = 1 << 24
+TIE = 1.02  # the default knobs win unless another setting is faster by more than this factor
 
 
 def candidates(w, T, fc2):
-    """Knob tuples (gemm, down_fp8, band_rows, fc2_reduce) for workload w at T tokens."""
+    """Knob tuples (gemm, down_fp8, band_rows, fc2_reduce, blocks_per_cu) for workload w at T tokens."""
     mx = w.dtype == "mxfp8"
     out = []
     for red in ((0, 1) if fc2 and w.k >= 2 else (0,)):
         for gemm in (1, 2):
-            out.append((gemm, 1, 0, red))
+            for blocks in DECODE_BLOCKS:
+                out.append((gemm, 1, 0, red, blocks))
         for down in ((1, 0) if mx else (1,)):
             for band in BANDS:
-                out.append((3, down, band, red))
+                out.append((3, down, band, red, 0))
+        out.append((3, 1, 0, red, 2))
     return out
 
 
@@ -119,12 +124,41 @@ def sweep(lib, w, tokens, steps, warmup, fc2, device, log):
 
 
 def pick(w, T, rows):
-    default = (auto_gemm(T, w.k, w.E), 1, 0, 0)
+    default = (auto_gemm(T, w.k, w.E), 1, 0, 0, 0)
     best = min(rows, key=lambda r: r[1])
     d = [r for r in rows if r[0] == default]
-    if d and d[0][1] <= 1.01 * best[1]:
+    if d and d[0][1] <= TIE * best[1]:
         return d[0], d[0]
     return best, (d[0] if d else None)
+
+
+def sweep_all(lib, mi, args, device, by_shape, record, log):
+    """Sweep every requested shape; fills by_shape {key: {T: (knobs, ms, default_ms, label)}} and record."""
+    # workloads of one layer shape are swept together, on one set of weights
+    groups = {}
+    for item in args.workloads.split(","):
+        name, _, own = item.partition(":")
+        w = mi.WORKLOADS[name]
+        g = groups.setdefault(shape_key(w), [w, set(), []])
+        if own:
+            g[1].update(int(t) for t in own.split("+"))
+        elif args.tokens:
+            g[1].update(int(t) for t in args.tokens.split(","))
+        else:
+            g[1].add(w.T)
+        g[2].append(name)
+    for key, (w, tokens, names) in groups.items():
+        tokens = sorted(tokens)
+        label = "+".join(names)
+        log(f"sweeping {label} at T = {tokens}")
+        res = sweep(lib, w, tokens, args.steps, args.warmup, args.fc2, device, log)
+        for T, rows in res.items():
+            (kn, ms), dflt = pick(w, T, rows)
+            by_shape.setdefault(key, {})[T] = (kn, ms, dflt[1] if dflt else None, label)
+            record.append({"workloads": names, "shape": list(key), "T": T, "winner": list(kn), "ms": ms,
+                           "default_ms": dflt[1] if dflt else None,
+                           "candidates": [{"knobs": list(k), "ms": m} for k, m in rows]})
+            log(f"{label} T={T}: knobs {kn} {ms:.4f} ms (default {dflt[1] if dflt else float('nan'):.4f} ms)")
 
 
 def main(argv=None):
@@ -139,50 +173,39 @@ def main(argv=None):
     ap.add_argument("--fc2", action="store_true", help="also try the in-kernel fc2 reduce (non-deterministic)")
     ap.add_argument("--out", default=None, help="cache file to write (default: the package's knob_cache.txt)")
     ap.add_argument("--json", default=None, help="also write every measurement to this JSON file")
+    ap.add_argument("--from-json", default=None,
+                    help="write the cache from the measurements of an earlier run's --json file (no GPU work)")
     args = ap.parse_args(argv)
 
     sys.path.insert(0, ROOT)
-    import torch
-
     import mixture_experts_layer_sort_amd as lib
     import moe_inputs as mi
-
-    device = torch.device("cuda:0")
 
     def log(msg):
         print(msg, flush=True)
 
-    # workloads of one layer shape are swept together, on one set of weights
-    groups = {}
-    for item in args.workloads.split(","):
-        name, _, own = item.partition(":")
-        w = mi.WORKLOADS[name]
-        g = groups.setdefault(shape_key(w), [w, set(), []])
-        if own:
-            g[1].update(int(t) for t in own.split("+"))
-        elif args.tokens:
-            g[1].update(int(t) for t in args.tokens.split(","))
-        else:
-            g[1].add(w.T)
-        g[2].append(name)
     by_shape = {}
     record = []
-    for key, (w, tokens, names) in groups.items():
-        tokens = sorted(tokens)
-        label = "+".join(names)
-        log(f"sweeping {label} at T = {tokens}")
-        res = sweep(lib, w, tokens, args.steps, args.warmup, args.fc2, device, log)
-        for T, rows in res.items():
-            (kn, ms), dflt = pick(w, T, rows)
-            by_shape.setdefault(key, {})[T] = (kn, ms, dflt[1] if dflt else None, label)
-            record.append({"workloads": names, "shape": list(key), "T": T, "winner": list(kn), "ms": ms,
-                           "default_ms": dflt[1] if dflt else None,
-                           "candidates": [{"knobs": list(k), "ms": m} for k, m in rows]})
-            log(f"{label} T={T}: knobs {kn} {ms:.4f} ms (default {dflt[1] if dflt else float('nan'):.4f} ms)")
+    if args.from_json:
+        with open(args.from_json) as f:
+            data = json.load(f)
+            for rec in data["sweeps"] if isinstance(data, dict) else data:
+                key = tuple(rec["shape"])
+                w = mi.WORKLOADS[rec["workloads"][0]]
+                rows = [(tuple(c["knobs"]), c["ms"]) for c in rec["candidates"]]
+                (kn, ms), dflt = pick(w, rec["T"], rows)
+                by_shape.setdefault(key, {})[rec["T"]] = (kn, ms, dflt[1] if dflt else None,
+                                                          "+".join(rec["workloads"]))
+                record.append(rec)
+    else:
+        import torch
+
+        device = torch.device("cuda:0")
+        sweep_all(lib, mi, args, device, by_shape, record, log)
 
     cmd = "python -m mixture_experts_layer_sort_amd.tune " + " ".join(argv if argv is not None else sys.argv[1:])
     lines = ["# Knob cache of the MoE layer library (moe_knob_cache_lookup).",
-             "# dtype act hidden inter experts top_k t_min t_max : gemm down_fp8 band_rows fc2_reduce",
+             "# dtype act hidden inter experts top_k t_min t_max : gemm down_fp8 band_rows fc2_reduce blocks_per_cu",
              f"# written by: {cmd.strip()}",
              "# each line: the fastest knobs at the swept token count (median of flushed steps on one MI355X)"]
     for key in sorted(by_shape):
@@ -193,7 +216,7 @@ def main(argv=None):
             # a winning variant that the heuristic picks anyway is written as 0 (auto), so calls of other
             # sizes in the line's range keep the per-call choice
             gemm = 0 if kn[0] == auto_gemm(T, k, E) else kn[0]
-            lines.append(f"{dtype} {act} {H} {I} {E} {k} {lo} {hi} : {gemm} {kn[1]} {kn[2]} {kn[3]}  # {note}")
+            lines.append(f"{dtype} {act} {H} {I} {E} {k} {lo} {hi} : {gemm} {kn[1]} {kn[2]} {kn[3]} {kn[4]}  # {note}")
     path = args.out or lib.KNOB_CACHE_PATH
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
