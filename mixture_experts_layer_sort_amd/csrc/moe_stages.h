@@ -12,6 +12,41 @@ namespace moe {
 // (logit descending, id ascending) pick the experts; slot j is the j-th pick.
 // Weights: softmax over the k picked logits [vLLM PR 40082 report,
 // "Implementation" item 1: routing inside the fused call].
+
+// (v, i) <- the better of (v, i) and (ov, oi): larger value, then smaller id
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
+  const bool b = ov > v || (ov == v && oi < i);
+  v = b ? ov : v;
+  i = b ? oi : i;
+}
+
+// Row-local exchange through the DPP crossbar (a few cycles, no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& v, int& i) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false);
+  argmax_merge(v, i, ov, oi);
+}
+
+// Wave-wide arg-max; every lane receives the winner.  Within each row of 16
+// lanes: swaps of neighbours (quad_perm 1,0,3,2), of pairs (2,3,0,1), then
+// the half-row and row mirrors; the four row winners are then read from
+// lanes 0, 16, 32, 48 and merged in row order.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_dpp<0xB1>(v, i);   // quad_perm [1, 0, 3, 2]
+  argmax_dpp<0x4E>(v, i);   // quad_perm [2, 3, 0, 1]
+  argmax_dpp<0x141>(v, i);  // row_half_mirror
+  argmax_dpp<0x140>(v, i);  // row_mirror
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r)),
+                 __builtin_amdgcn_readlane(i, 16 * r));
+  v = bv;
+  i = bi;
+}
+
 template <int NV>
 __device__ __forceinline__ void route_token_n(const float* __restrict__ logits, int t, int E, int k,
                                               int* __restrict__ ids, float* __restrict__ wts, int lane) {
@@ -25,7 +60,7 @@ __device__ __forceinline__ void route_token_n(const float* __restrict__ logits, 
     v[i] = (x == x) ? x : -INFINITY;  // NaN never wins; results stay in range
     if (e >= E) taken |= 1u << i;
   }
-  float my_val = 0.f;
+  float my_val = 0.f, m0 = 0.f, sum = 0.f;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
@@ -37,28 +72,18 @@ __device__ __forceinline__ void route_token_n(const float* __restrict__ logits, 
       bv = better ? v[i] : bv;
       bi = better ? id : bi;
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      float ov = __shfl_xor(bv, m, 64);
-      int oi = __shfl_xor(bi, m, 64);
-      bool better = ov > bv || (ov == bv && oi < bi);
-      bv = better ? ov : bv;
-      bi = better ? oi : bi;
-    }
+    wave_argmax(bv, bi);  // uniform across the wave from here
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (j == 0) m0 = bv;
+    sum += expf(bv - m0);  // the softmax denominator, in pick order
     if (lane == j) {
       my_val = bv;
       my_id = bi;
     }
   }
-  const float m0 = __shfl(my_val, 0, 64);
-  float ex = lane < k ? expf(my_val - m0) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m, 64);
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
-    wts[(size_t)t * k + lane] = ex / sum;
+    wts[(size_t)t * k + lane] = expf(my_val - m0) / sum;
   }
 }
 
