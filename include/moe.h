@@ -382,8 +382,11 @@ MOE_API void moe_default_knobs(moe_knobs* knobs);
  * workspace as moe_forward; with the default knobs the results are bitwise
  * those of moe_forward.  MOE_ERR_INVALID_ARG for a knob out of range (gemm
  * outside [0, 3], down_fp8 / fc2_reduce outside {0, 1}, band_rows outside
- * [0, 2^20], blocks_per_cu outside [0, 16]); MOE_ERR_UNSUPPORTED for fc2_reduce with top_k == 1, and for
- * gemm = 1 with more than 16 (65535 - num_experts) routed rows (T top_k). */
+ * [0, 2^20], blocks_per_cu outside [0, 16]); MOE_ERR_UNSUPPORTED for fc2_reduce with top_k == 1, for
+ * gemm = 1 with more than 16 (65535 - num_experts) routed rows (T top_k), and
+ * for gemm = 3 where T hidden or T top_k inter reaches 2^30 (the prefill-shaped
+ * GEMMs address activation rows with 31-bit byte offsets; the default knobs
+ * then use the 32-row decode items). */
 MOE_API moe_status moe_forward_knobs(const moe_shape* shape, int32_t T, const void* packed, const float* logits,
                                      const uint16_t* x, uint16_t* out, int32_t* topk_ids, float* topk_w,
                                      void* ws, size_t ws_bytes, const moe_knobs* knobs, hipStream_t stream);

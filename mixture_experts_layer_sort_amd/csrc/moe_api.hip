@@ -53,11 +53,14 @@ int gemm_grid(int layer_dt, bool g13, const GemmPlan& p) {
   return device_cu_count() * occ;
 }
 
-// The plan of the default knobs for R routed rows (T tokens x k slots): the
-// GEMM variant follows the rows per expert, the fp8 down GEMM is on.
-GemmPlan default_plan(int T, int k, int E, float limit) {
+// The plan of the default knobs for T tokens x k slots: the GEMM variant
+// follows the rows per expert (32-row decode items where the prefill-shaped
+// ones do not fit), the fp8 down GEMM is on where its offsets fit.
+GemmPlan default_plan(int T, int k, int E, int H, int I, float limit) {
   GemmPlan p;
   p.variant = gemm_variant(T, k, E);
+  if (p.variant == 2 && !prefill_fits(T, H, (long long)T * k, I)) p.variant = 1;
+  p.down_fp8 = fp8_down_fits(T, k, I);
   p.limit = limit;
   return p;
 }
@@ -65,11 +68,11 @@ GemmPlan default_plan(int T, int k, int E, float limit) {
 // co-resident blocks of the fused kernel, per device: [dev][dt][variant]; -1 = unusable
 std::atomic<int> g_fused_occ[kMaxDevices][3][4];
 
-int fused_grid(int layer_dt, int T, int k, int E) {
+int fused_grid(int layer_dt, int T, int k, int E, int H, int I) {
   const int dt = weight_dt(layer_dt);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  const int v = fused_variant(layer_dt, T, k, E);
+  const int v = fused_variant(layer_dt, T, k, E, H, I);
   int occ = g_fused_occ[dev][dt][v].load(std::memory_order_relaxed);
   if (occ == 0) {
     occ = fused_blocks_per_cu(dt, v);
@@ -265,7 +268,7 @@ moe_status moe_gemm13_swiglu_quant(const moe_shape* s, int32_t T, const void* pa
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!packed || !offsets || !sorted_pairs || !xq || !hq) return MOE_ERR_INVALID_ARG;
-  const GemmPlan p = default_plan(T, s->top_k, s->num_experts, s->gate_up_limit);
+  const GemmPlan p = default_plan(T, s->top_k, s->num_experts, s->hidden, s->inter, s->gate_up_limit);
   return launched(launch_gemm13(s->dtype, gated(s), s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
                                 offsets, sorted_pairs, (const uint8_t*)xq, (uint8_t*)hq, gemm_grid(s->dtype, true, p),
                                 stream, p));
@@ -280,7 +283,7 @@ moe_status moe_gemm2(const moe_shape* s, int32_t T, const void* packed, const in
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!packed || !offsets || !sorted_pairs || !hq || !y) return MOE_ERR_INVALID_ARG;
-  const GemmPlan p = default_plan(T, s->top_k, s->num_experts, s->gate_up_limit);
+  const GemmPlan p = default_plan(T, s->top_k, s->num_experts, s->hidden, s->inter, s->gate_up_limit);
   return launched(launch_gemm2(s->dtype, gated(s), s->num_experts, s->hidden, s->inter, s->top_k, T, (const uint8_t*)packed,
                                offsets, sorted_pairs, (const uint8_t*)hq, y, gemm_grid(s->dtype, false, p), stream, p));
 }
@@ -347,7 +350,7 @@ moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const 
   moe_status st = check_forward(s, T, packed, logits, x, out, ws, ws_bytes);
   if (st != MOE_OK || T == 0) return st;
   return forward_staged(s, T, s->max_tokens, packed, logits, x, out, topk_ids, topk_w, (uint8_t*)ws,
-                        default_plan(T, s->top_k, s->num_experts, s->gate_up_limit), false, stream);
+                        default_plan(T, s->top_k, s->num_experts, s->hidden, s->inter, s->gate_up_limit), false, stream);
 }
 
 void moe_default_knobs(moe_knobs* kn) {
@@ -371,10 +374,11 @@ moe_status moe_forward_knobs(const moe_shape* s, int32_t T, const void* packed, 
   if (kn.fc2_reduce && s->top_k < 2) return MOE_ERR_UNSUPPORTED;
   // the 16-row decode schedule packs two m-tile prefixes into 16-bit halves
   if (kn.gemm == 1 && (long long)T * s->top_k > 16LL * (65535 - s->num_experts)) return MOE_ERR_UNSUPPORTED;
+  if (kn.gemm == 3 && !prefill_fits(T, s->hidden, (long long)T * s->top_k, s->inter)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  GemmPlan p = default_plan(T, s->top_k, s->num_experts, s->gate_up_limit);
+  GemmPlan p = default_plan(T, s->top_k, s->num_experts, s->hidden, s->inter, s->gate_up_limit);
   if (kn.gemm > 0) p.variant = kn.gemm - 1;
-  p.down_fp8 = kn.down_fp8 != 0;
+  p.down_fp8 = p.down_fp8 && kn.down_fp8 != 0;
   p.band = kn.band_rows;
   p.blocks_per_cu = kn.blocks_per_cu;
   return forward_staged(s, T, s->max_tokens, packed, logits, x, out, topk_ids, topk_w, (uint8_t*)ws, p,
@@ -393,7 +397,7 @@ moe_status moe_forward_noalloc(const moe_shape* s, int32_t T, const void* packed
   if (!base) return MOE_ERR_LAUNCH;
   // every intermediate is written before it is read: nothing needs clearing
   return forward_staged(s, T, T, packed, logits, x, out, topk_ids, topk_w, base,
-                        default_plan(T, s->top_k, s->num_experts, s->gate_up_limit), false, stream);
+                        default_plan(T, s->top_k, s->num_experts, s->hidden, s->inter, s->gate_up_limit), false, stream);
 }
 
 size_t moe_batched_workspace_bytes(const moe_shape* s, int32_t max_rows) {
@@ -416,7 +420,7 @@ moe_status moe_batched_experts(const moe_shape* s, int32_t max_rows, const int32
   uint8_t* xq = act_dt(dt) == DT_BF16 ? (uint8_t*)x : base + B.xq;  // bf16 activations are used in place
   uint8_t* hq = base + B.hq;
   // one "pair" per valid row (k = 1, R rows of capacity): the GEMM variants follow the rows per expert
-  const GemmPlan p = default_plan(R, 1, E, s->gate_up_limit);
+  const GemmPlan p = default_plan(R, 1, E, H, I, s->gate_up_limit);
   hipError_t e = launch_batched_prep(dt, counts, E, max_rows, H, offsets, rows, x, xq, stream);
   if (e == hipSuccess)
     e = launch_gemm13(dt, gated(s), E, H, I, 1, R, (const uint8_t*)packed, offsets, rows, xq, hq,
@@ -464,7 +468,7 @@ moe_status moe_nvfp4_linear(int32_t M, int32_t N, int32_t K, const void* packed,
   hipError_t e = launch_dense_prep(M, K, offsets, rows, x, xq, stream);
   if (e == hipSuccess)
     e = launch_dense_gemm(M, N, K, (const uint8_t*)packed, offsets, rows, xq, out,
-                          gemm_grid(MOE_NVFP4, false, default_plan(M, 1, 1, 0.f)), stream);
+                          gemm_grid(MOE_NVFP4, false, default_plan(M, 1, 1, K, K, 0.f)), stream);
   return launched(e);
 }
 
@@ -478,7 +482,7 @@ moe_status moe_forward_fused(const moe_shape* s, int32_t T, const void* packed, 
   uint8_t* base = (uint8_t*)ws;
   int32_t* ids = topk_ids ? topk_ids : (int32_t*)(base + W.ids);
   float* wts = topk_w ? topk_w : (float*)(base + W.wts);
-  const int grid = fused_grid(dt, T, k, E);
+  const int grid = fused_grid(dt, T, k, E, H, I);
   if (grid <= 0) return MOE_ERR_UNSUPPORTED;
   return launched(launch_fused(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, logits, x, out, ids, wts, base, ws_bytes,
                                s->max_tokens, grid, stream, s->gate_up_limit));

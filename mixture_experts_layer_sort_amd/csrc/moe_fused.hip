@@ -305,7 +305,7 @@ hipError_t launch_fused(int dt, bool gated, int E, int H, int I, int k, int T, c
   g.band = h.band = 0;
   g.red = h.red = nullptr;
   g.wts = h.wts = nullptr;
-  const int v = fused_variant(dt, T, k, E);
+  const int v = fused_variant(dt, T, k, E, H, I);
   if (v == 3) {  // the fp8 down items: fragment-order weights, e4m3 hq codes and e8m0 scales
     h.wcodes = packed + L.w2_frag;
     h.act = hq;

@@ -44,7 +44,8 @@ hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t
 
 // How the grouped GEMMs of one call run: the kernel variant (0: decode items
 // with 16-row token tiles, 1: 32-row token tiles, 2: prefill items), whether
-// an MXFP8 layer's prefill-shaped down GEMM runs on the fp8 instruction, the
+// an MXFP8 layer's prefill-shaped down GEMM runs on the fp8 instruction (only
+// where fp8_down_fits), the
 // prefill item band (token rows per band of weight reuse; 0: the kernel's
 // default), the persistent blocks per compute unit (0: the occupancy limit), the SwiGLU clamp and
 // the optional in-kernel fc2 reduce of the down GEMM (red: fp32 [T, H] output
@@ -85,11 +86,21 @@ inline int gemm_nt(int T, int k, int E) { return (long long)T * k > 16LL * E ? 2
 inline bool gemm_prefill(int T, int k, int E) { return (long long)T * k >= 64LL * E; }
 // GEMM variant index for caches: 0 decode NT=1, 1 decode NT=2, 2 prefill.
 inline int gemm_variant(int T, int k, int E) { return gemm_prefill(T, k, E) ? 2 : gemm_nt(T, k, E) - 1; }
-// GEMM variant of the single-launch kernel (layer format dt): as gemm_variant,
-// and 3 for the prefill-shaped GEMMs of MXFP8 layers (fp8 matrix instruction).
-inline int fused_variant(int dt, int T, int k, int E) {
-  const int v = gemm_variant(T, k, E);
-  return v == 2 && has_fp8_gemm(dt) ? 3 : v;
+// The prefill-shaped GEMMs load activation rows straight into LDS through
+// buffer resources with 32-bit offsets below 2^31: rows13 rows of the gate/up
+// GEMM's 16-bit activations (H wide) and rows2 rows of the down GEMM's (I
+// wide); the fp8 down GEMM reads the latter's I-byte codes.
+inline bool prefill_fits(long long rows13, int H, long long rows2, int I) {
+  return rows13 * H * 2 < (1LL << 31) && rows2 * I * 2 < (1LL << 31);
+}
+inline bool fp8_down_fits(int T, int k, int I) { return (long long)T * k * I < (1LL << 31); }
+// GEMM variant of the single-launch kernel (layer format dt): as gemm_variant
+// (the 32-row decode items where the prefill-shaped ones do not fit), and 3
+// for the prefill-shaped GEMMs of MXFP8 layers (fp8 matrix instruction).
+inline int fused_variant(int dt, int T, int k, int E, int H, int I) {
+  int v = gemm_variant(T, k, E);
+  if (v == 2 && !prefill_fits(T, H, (long long)T * k, I)) v = 1;
+  return v == 2 && has_fp8_gemm(dt) && fp8_down_fits(T, k, I) ? 3 : v;
 }
 int prefill_blocks_per_cu(int dt, bool g13);
 int prefill_f8_blocks_per_cu(bool g13);

@@ -159,7 +159,9 @@ __device__ __forceinline__ int f8_item(const GemmArgs& a, long long w, const int
   // .. 8 wv + 7 (sub-tiles 2 wv, 2 wv + 1).  Lane L loads row 16 half + L / 4
   // of the sub-tile, piece (L % 4) ^ swizzle.  Rows past the expert's end
   // load its last row (results discarded).
-  const uint8_t* tsrc[2][2];
+  // (byte offsets from a.act / a.act_scales: the loads go through buffer
+  // resources, see issue_t; the host keeps every offset below 2^31)
+  uint32_t toff[2][2];
 #pragma unroll
   for (int S2 = 0; S2 < 2; ++S2)
 #pragma unroll
@@ -167,15 +169,18 @@ __device__ __forceinline__ int f8_item(const GemmArgs& a, long long w, const int
       const int rl = 16 * half + (lane >> 2);
       const int r = min(r0 + 32 * (2 * wv + S2) + rl, r_end - 1);
       const int row = G13 ? a.sorted_pairs[r] / a.k : r;
-      tsrc[S2][half] = a.act + (size_t)row * a.K + 16 * ((lane & 3) ^ pf_swz(rl));
+      toff[S2][half] = (uint32_t)row * (uint32_t)a.K + 16 * ((lane & 3) ^ pf_swz(rl));
     }
   // token scale words: this wave loads tokens 64 wv .. +64 of the item, 4 bytes each
-  const uint8_t* ssrc;
+  uint32_t soff;
   {
     const int r = min(r0 + 64 * wv + lane, r_end - 1);
     const int row = G13 ? a.sorted_pairs[r] / a.k : r;
-    ssrc = a.act_scales + (size_t)row * (a.K / 32);
+    soff = (uint32_t)row * (uint32_t)(a.K / 32);
   }
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, 0x7FFFFFFF, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.act_scales, (short)0, 0x7FFFFFFF, 0x00020000);
   // down GEMM: the pair index of each of this lane's output rows, loaded now for the epilogue
   int pidx[kF8Sub];
   if constexpr (!G13) {
@@ -200,14 +205,20 @@ __device__ __forceinline__ int f8_item(const GemmArgs& a, long long w, const int
 #pragma unroll
     for (int f = 0; f < 2; ++f) A.s[f] = *reinterpret_cast<const uint32_t*>(wssrc + (size_t)kg * 256 + f * 128);
   };
+  // Token loads straight into LDS through buffer resources (the MUBUF form:
+  // the compiler then tracks them with the vector-memory counter alone; the
+  // global form is also counted as a possible LDS access, which made it wait
+  // for every LDS read before each MFMA while any of these were in flight).
   auto issue_t = [&](u32x4_t(&stage)[kF8StageSlots], int kg) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = 8 * wv + i, S = c >> 2, s = (c >> 1) & 1, half = c & 1;
-      __builtin_amdgcn_global_load_lds(tsrc[i >> 2][half] + kg * 128 + s * 64, &stage[((S * 2 + s) * 2 + half) * 64],
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          trs, (__attribute__((address_space(3))) void*)&stage[((S * 2 + s) * 2 + half) * 64], 16,
+          toff[i >> 2][half] + kg * 128 + s * 64, 0, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds(ssrc + 4 * kg, &stage[kF8TokSlots + 16 * wv], 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        srs, (__attribute__((address_space(3))) void*)&stage[kF8TokSlots + 16 * wv], 4, soff + 4 * kg, 0, 0, 0);
   };
 
   auto run = [&](auto nsa_tag) {
@@ -300,6 +311,7 @@ __device__ __forceinline__ int f8_item(const GemmArgs& a, long long w, const int
         const int nk = min(kg + u + 2, KG - 1);
         issue_a(A[(u + 2) % kF8ARing], nk);
         issue_t(*st.s[(u + 2) % kF8Stages], nk);
+        __builtin_amdgcn_sched_barrier(0);  // the direct-to-LDS loads stay ahead of the MFMAs
         body(A[u], *st.s[u]);
       }
     }
@@ -311,6 +323,7 @@ __device__ __forceinline__ int f8_item(const GemmArgs& a, long long w, const int
         const int nk = min(kg + u + 2, KG - 1);
         issue_a(A[(u + 2) % kF8ARing], nk);
         issue_t(*st.s[(u + 2) % kF8Stages], nk);
+        __builtin_amdgcn_sched_barrier(0);  // the direct-to-LDS loads stay ahead of the MFMAs
         body(A[u], *st.s[u]);
       }
     }
@@ -333,9 +346,6 @@ __device__ __forceinline__ int f8_item(const GemmArgs& a, long long w, const int
     case 7: run(std::integral_constant<int, 7>{}); break;
     default: run(std::integral_constant<int, 8>{}); break;
   }
-  // drain the epilogue's stores before the next item's loads (the shared
-  // vector-memory counter then counts only loads again)
-  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
   return e;
 }
 

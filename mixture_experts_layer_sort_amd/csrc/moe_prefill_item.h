@@ -340,20 +340,23 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
   // wv kDma .. + kDma, all in sub-tile dS.  Load lane: row 16 half + lane / 4, the
   // row's 16-byte piece (lane % 4) ^ swizzle.  Rows past the expert's end
   // load its last row, whose results are discarded.
+  // (byte offsets from a.act: the direct-to-LDS loads go through buffer
+  // resources, see issue_op; the host keeps every offset below 2^31)
   const int dS = (wv * kDma) >> 2;
-  const uint8_t* bsrc[2];
+  uint32_t boff[2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int rl = 16 * half + (lane >> 2);
     const int r = min(r0 + 32 * dS + rl, r_end - 1);
     const int row = G13 ? a.sorted_pairs[r] / a.k : r;
     const int piece = (lane & 3) ^ pf_swz(rl);
-    bsrc[half] = a.act + ((size_t)row * a.K + 8 * piece) * 2;
+    boff[half] = ((uint32_t)row * (uint32_t)a.K + 8 * piece) * 2;
   }
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, 0x7FFFFFFF, 0x00020000);
   // fragment reads: row l32 of a block, piece 2m + hl
-  int boff[2];
+  int fro[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) boff[m] = 4 * l32 + ((2 * m + hl) ^ pf_swz(l32));
+  for (int m = 0; m < 2; ++m) fro[m] = 4 * l32 + ((2 * m + hl) ^ pf_swz(l32));
 
   // weights: lane part of the gathered fragment address
   constexpr size_t tcode = DT == DT_BF16 ? 4096 : DT == DT_MXFP8 ? 2048 : 1024;
@@ -362,14 +365,25 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
   const size_t tile0 = (size_t)(e * a.G + gl) * a.KG * 4;  // tile index of (gl, kgroup 0, tile 0)
   const uint8_t* wc = a.wcodes + (tile0 + ltile) * tcode + lpos * 16;
   const uint8_t* ws = a.wscales + (tile0 + ltile) * tscale + i16 * (DT == DT_MXFP8 ? 4 : 8);
+  // LDS-staged weights: buffer resources based at this row group's first tile (offsets within one group)
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.wcodes + tile0 * tcode), (short)0, 0x7FFFFFFF, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wsrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.wscales + tile0 * tscale), (short)0, 0x7FFFFFFF, 0x00020000);
+  const uint32_t wlo = ltile * (uint32_t)tcode + lpos * 16;
 
   // Vector-memory operation k of K step `step`: k < kDma a token load into
-  // `stage`; k >= kDma a piece of the weights into A.
+  // `stage`; k >= kDma a piece of the weights into A.  The direct-to-LDS
+  // loads use the buffer (MUBUF) form: the compiler tracks those with the
+  // vector-memory counter alone, while the global form also counts as a
+  // possible LDS access and made it wait for every LDS read before each
+  // slice's MFMAs as long as one was in flight.
   auto issue_op = [&](int k, u32x4_t(&stage)[kSlots], PfA<DT>& A, int step) {
     if (k < kDma) {
       const int d = wv * kDma + k, cc = (d >> 1) & 1, half = k & 1;
-      __builtin_amdgcn_global_load_lds(bsrc[half] + step * 128 + cc * 64, &stage[((2 * dS + cc) * 2 + half) * 64], 16,
-                                       0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          brs, (__attribute__((address_space(3))) void*)&stage[((2 * dS + cc) * 2 + half) * 64], 16,
+          boff[half] + step * 128 + cc * 64, 0, 0, 0);
       return;
     }
     const int kg = step >> 1, h = step & 1, idx = k - kDma;
@@ -378,12 +392,14 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
       if (idx < kADma) {
         // codes of fragment pair (f, m) of this row group, in fragment-lane order
         const int f = TW == 2 ? th : (idx >> 1), m = TW == 2 ? idx : (idx & 1);
-        __builtin_amdgcn_global_load_lds(wc + (tk + 2 * f) * tcode + h * 1024 + m * 512,
-                                         &stage[kTokSlots + ((wg * 2 + f) * 2 + m) * 64], 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wrs, (__attribute__((address_space(3))) void*)&stage[kTokSlots + ((wg * 2 + f) * 2 + m) * 64], 16,
+            wlo + (uint32_t)((tk + 2 * f) * tcode + h * 1024 + m * 512), 0, 0, 0);
       } else {
         // this wave's copy of the group's 4 tile scale blocks (256 contiguous bytes)
-        __builtin_amdgcn_global_load_lds(a.wscales + (tile0 + tk) * tscale + lane * 4,
-                                         &stage[kTokSlots + 1024 + wv * 16], 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wsrs, (__attribute__((address_space(3))) void*)&stage[kTokSlots + 1024 + wv * 16], 4,
+            (uint32_t)(tk * tscale) + lane * 4, 0, 0, 0);
       }
       return;
     }
@@ -437,7 +453,7 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
     // token fragments of the active sub-tiles, K slice (chunk cc, m)
     auto read_b = [&](u32x4_t(&bf)[kSW], const u32x4_t(&stage)[kSlots], int cc, int m) {
 #pragma unroll
-      for (int S = 0; S < NSA; ++S) bf[S] = stage[(2 * (TW * S + th) + cc) * 128 + boff[m]];
+      for (int S = 0; S < NSA; ++S) bf[S] = stage[(2 * (TW * S + th) + cc) * 128 + fro[m]];
     };
 
     // Operands of slice 0 of a step, read ahead across the step boundary:

@@ -137,6 +137,11 @@ def test_forward_knobs_host_checks():
     T_over = 2 * (65535 - 256) + 1  # top-8: 8 T > 16 (65535 - 256)
     assert h.moe_forward_knobs(ctypes.byref(big), T_over, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, P(FAKE),
                                wsb, ctypes.byref(lib.moe_knobs(1, 1, 0, 0, 0)), None) == UNSUPPORTED
+    # the prefill-shaped items address activation rows with 31-bit byte offsets
+    huge = lib.make_shape(128, 128, 8, 1, 1 << 23, "bf16")
+    wsh = lib.moe_workspace_bytes(huge)
+    assert h.moe_forward_knobs(ctypes.byref(huge), 1 << 23, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None,
+                               P(FAKE), wsh, ctypes.byref(lib.moe_knobs(3, 1, 0, 0, 0)), None) == UNSUPPORTED
     s = lib.make_shape(256, 512, 8, 2, 16, "bf16")
     ws = lib.moe_workspace_bytes(s)
     assert h.moe_forward_knobs(ctypes.byref(s), 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, P(FAKE), ws - 1,
