@@ -288,8 +288,12 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-single-launch", action="store_true", help="do not time moe_forward_fused")
+    ap.add_argument("--skip-fc2", action="store_true", help="do not time the in-kernel fc2 reduce")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--dma-probe", action="store_true",
+                    help="only run the layer on a single-expert MXFP8 prefill shape whose gate/up GEMM fetches "
+                         "each operand byte once through its direct-to-LDS loads (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
@@ -309,6 +313,23 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": a.numel() * 4}))
+        return
+
+    if args.dma_probe:
+        # E = 1, T = 256 routed rows, I = 256: the gate/up GEMM (prefill-shaped, 128-row items) runs
+        # 2 m-tiles x 2 blocks of 256 weight rows as four items side by side on one XCD (the
+        # XCD-contiguous item order); they stream K in near lockstep, so the L2 misses are the unique
+        # operand bytes: the W13 codes and scales and the 16-bit copy of the 256 token rows.
+        w = mi.WORKLOADS["mxfp8_prefill"].scaled(T=256, I=256, E=1, k=1, bias="none", name="dma_probe")
+        lib, layer, x, logits = build_layer(w, device)
+        step = StagedStep(lib, layer, x, logits)
+        for _ in range(3):
+            step.run()
+        torch.cuda.synchronize()
+        w13 = w.R13 * w.H * (1 + 1 / 32)
+        toks = w.T * w.H * 2
+        print(json.dumps({"dma_probe_gemm13_unique_fetch_bytes": w13 + toks, "w13_bytes": w13,
+                          "token_copy_bytes": toks, "launches": 3}))
         return
 
     w = mi.WORKLOADS[args.workload]
@@ -380,7 +401,7 @@ def main():
     # the in-kernel fc2 reduce (a correctness knob: outputs not bitwise
     # reproducible), flushed and timed like the eager steps (context)
     fc2_ms_step = None
-    if w.k >= 2:
+    if w.k >= 2 and not args.skip_fc2:
         fc2_knobs = lib.make_knobs(knobs.gemm, knobs.down_fp8, knobs.band_rows, 1)
 
         def forward_fc2():
