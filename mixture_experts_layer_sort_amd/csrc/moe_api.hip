@@ -329,6 +329,8 @@ static moe_status forward_staged(const moe_shape* s, int32_t T, int cap, const v
   float* acc = fc2 ? (float*)(base + W.y) : nullptr;
   p.red = acc;
   p.wts = acc ? wts : nullptr;
+  // the fp8 down GEMM reads the hq codes: the gate/up GEMM skips hq's 16-bit copy
+  p.skip_hq_deq = p.variant == 2 && p.down_fp8 && has_fp8_gemm(dt);
   hipError_t e = launch_route(logits, T, E, k, ids, wts, stream);
   if (e == hipSuccess)
     e = launch_permute(dt, ids, T, k, E, H, offsets, sorted_pairs, pair_pos, x, xq, stream);

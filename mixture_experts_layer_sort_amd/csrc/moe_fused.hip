@@ -307,6 +307,7 @@ hipError_t launch_fused(int dt, bool gated, int E, int H, int I, int k, int T, c
   g.wts = h.wts = nullptr;
   const int v = fused_variant(dt, T, k, E, H, I);
   if (v == 3) {  // the fp8 down items: fragment-order weights, e4m3 hq codes and e8m0 scales
+    g.out_deq = nullptr;  // (hq's 16-bit copy is not read)
     h.wcodes = packed + L.w2_frag;
     h.act = hq;
     h.act_scales = hq + act_scale_offset(dt, T * k, I);

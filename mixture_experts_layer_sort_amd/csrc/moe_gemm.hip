@@ -188,7 +188,7 @@ hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, 
   a.act = xq + act_operand_offset(dt, T, H);
   a.out = hq;
   a.out_scales = hq + act_scale_offset(dt, T * k, I);
-  a.out_deq = reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
+  a.out_deq = plan.skip_hq_deq ? nullptr : reinterpret_cast<uint16_t*>(hq + act_dequant_offset(dt, T * k, I));
   a.act_scales = nullptr;
   a.act_bf16 = dt == DT_BF16_MXFP8;
   a.gated = gated;

@@ -19,7 +19,8 @@ struct GemmArgs {
   const uint8_t* act_scales;  // the fp8 prefill GEMM: the e8m0 scales of those rows
   uint8_t* out;               // hq codes (gemm13) or y (gemm2)
   uint8_t* out_scales;        // hq scales (gemm13)
-  uint16_t* out_deq;          // hq dequantised 16-bit copy (gemm13; MXFP8, NVFP4)
+  uint16_t* out_deq;          // hq dequantised 16-bit copy (gemm13; MXFP8, NVFP4; null: not written, which
+                              // only the prefill-shaped MXFP8 epilogue allows)
   int act_bf16;               // MXFP8 weights with bf16 activations: the intermediate is rounded to bf16
   int gated;                  // gate/up GEMM: 1 SwiGLU (gate/up row pairs), 0 ReLU^2 (64 W1 rows per group)
   float limit;                // SwiGLU gate/up clamp L (0: none): gate = min(gate, L), up = clamp(up, -L, L)

@@ -49,10 +49,13 @@ hipError_t launch_prepare(int dt, bool gated, int E, int H, int I, const uint8_t
 // prefill item band (token rows per band of weight reuse; 0: the kernel's
 // default), the persistent blocks per compute unit (0: the occupancy limit), the SwiGLU clamp and
 // the optional in-kernel fc2 reduce of the down GEMM (red: fp32 [T, H] output
-// rows, wts: the router weights of the pairs).
+// rows, wts: the router weights of the pairs), and whether the gate/up GEMM
+// may leave out the 16-bit copy of hq (only the bf16-product down GEMMs read
+// it; the fp8 one reads the codes).
 struct GemmPlan {
   int variant = 0;
   bool down_fp8 = true;
+  bool skip_hq_deq = false;
   int band = 0;
   int blocks_per_cu = 0;
   float limit = 0.f;

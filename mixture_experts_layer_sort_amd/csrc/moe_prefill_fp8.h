@@ -63,6 +63,12 @@ __device__ __forceinline__ u32x4_t (*f8_stage())[kF8StageSlots] {
   return &buf;
 }
 
+// Pair index of each routed row of the item (down GEMM epilogue).
+__device__ __forceinline__ int (*f8_pidx())[kF8Rows] {
+  __shared__ int buf[kF8Rows];
+  return &buf;
+}
+
 struct F8Stages {
   u32x4_t (*s[kF8Stages])[kF8StageSlots];
 };
@@ -96,36 +102,79 @@ __device__ __forceinline__ void f8_wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Down-GEMM epilogue: bf16 y rows of the pairs; pidx[S] is the pair index of
-// this lane's row r0 + 32 S + (lane & 31) (loaded at the start of the item so
-// the loads' latency hides behind the K loop), -1 past the expert's rows.
-// Lane l, element i of acc[f][S] is weight row 32 f + (i & 3) + 8 (i >> 2) +
-// 4 (l >> 5) of row group g (the 32x32 accumulator layout).
+// Down-GEMM epilogue: bf16 y rows of the pairs of the item's `nrows` routed
+// rows; pidx (LDS, filled at the start of the item so the loads' latency
+// hides behind the K loop) holds the pair index of each.  Lane l, element i
+// of acc[f][S] is weight row 32 f + (i & 3) + 8 (i >> 2) + 4 (l >> 5) of row
+// group g, routed row 32 S + (l & 31) (the 32x32 accumulator layout).
+//
+// The accumulator layout gives each lane 16-byte pieces of 32 different y
+// rows per store; written straight out, every store instruction touches 32
+// cache lines.  Instead each wave turns its 64-column slice around in LDS
+// (the token stages are free once the K loop is done): up to 4 sub-tiles at
+// a time, 128 rows x 128 bytes in the wave's own 16 KB, 16-byte chunk j of
+// row r at slot j ^ (r & 7) (conflict-free writes of 8-byte pieces and reads
+// of whole rows), then each store instruction writes 8 whole 128-byte row
+// segments (one cache line each).  The caller ends the item with a block
+// barrier before the next item's loads refill the stages.
 template <int NSA>
-__device__ __forceinline__ void f8_down_epilogue(const GemmArgs& a, f32x16_t (&acc)[2][kF8Sub], const int (&pidx)[kF8Sub],
-                                                 int g, int lane) {
-  const int hl = lane >> 5;
+__device__ __forceinline__ void f8_down_epilogue(const GemmArgs& a, f32x16_t (&acc)[2][kF8Sub], const int* pidx,
+                                                 int nrows, int g, int lane, int wv, const F8Stages& st) {
+  const int hl = lane >> 5, m = lane & 31;
+  if (a.red) {  // in-kernel fc2 reduce: w * y added to the token's fp32 output row
 #pragma unroll
-  for (int S = 0; S < NSA; ++S) {
-    if (pidx[S] >= 0 && a.red) {  // in-kernel fc2 reduce: w * y added to the token's fp32 output row
-      const float wp = a.wts[pidx[S]];
-      float* o = a.red + (size_t)(pidx[S] / a.k) * a.n_out + 64 * g + 4 * hl;
+    for (int S = 0; S < NSA; ++S) {
+      if (32 * S + m < nrows) {
+        const int p = pidx[32 * S + m];
+        const float wp = a.wts[p];
+        float* o = a.red + (size_t)(p / a.k) * a.n_out + 64 * g + 4 * hl;
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) unsafeAtomicAdd(o + 32 * f + 8 * (i >> 2) + (i & 3), wp * acc[f][S][i]);
-    } else if (pidx[S] >= 0) {
-      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (size_t)pidx[S] * a.n_out + 64 * g + 4 * hl;
+          for (int i = 0; i < 16; ++i) unsafeAtomicAdd(o + 32 * f + 8 * (i >> 2) + (i & 3), wp * acc[f][S][i]);
+      }
+    }
+    return;
+  }
+  // (a select, not an indexed load: indexing st would place it in memory)
+  u32x4_t* buf = &(*(wv < 2 ? st.s[0] : st.s[1]))[(wv & 1) * 1024];  // 1024 slots of 16 bytes
+  uint2* b64 = reinterpret_cast<uint2*>(buf);
+  // Lane-dependent address parts, opaque to the compiler here so that the
+  // per-store addresses are formed in place rather than hoisted out of the
+  // item loop (dozens of loop-invariant registers, spilled across the K loop)
+  int xm = m & 7, rl = lane >> 3, c8 = lane & 7;
+  asm volatile("" : "+v"(xm), "+v"(rl), "+v"(c8));
+  const int rslot = rl * 8 + (c8 ^ rl);  // read slot of chunk c8 of row rl
+  uint16_t* y = reinterpret_cast<uint16_t*>(a.out) + 64 * g + 8 * c8;
+#pragma unroll
+  for (int p = 0; p < (NSA + 3) / 4; ++p) {
+    constexpr int kPass = 4;
+#pragma unroll
+    for (int S = kPass * p; S < NSA && S < kPass * p + kPass; ++S) {
+      uint2* wrow = b64 + (256 * (S - kPass * p) + 8 * m) * 2 + hl;  // row 32 (S - kPass p) + m
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const f32x16_t& v = acc[f][S];
-          *reinterpret_cast<uint2*>(o + 32 * f + 8 * b) =
+          wrow[((4 * f + b) ^ xm) * 2] =
               make_uint2(f32_to_bf16(v[4 * b]) | ((uint32_t)f32_to_bf16(v[4 * b + 1]) << 16),
                          f32_to_bf16(v[4 * b + 2]) | ((uint32_t)f32_to_bf16(v[4 * b + 3]) << 16));
         }
     }
+    // 8 rows per store: lane l reads chunk l % 8 of row 8 j + l / 8 (all
+    // reads first, so their latencies overlap; then the stores)
+    const int nj = 4 * (NSA - kPass * p < kPass ? NSA - kPass * p : kPass);  // a constant once unrolled
+    u32x4_t v[4 * kPass];
+    int pid[4 * kPass];
+#pragma unroll
+    for (int j = 0; j < nj; ++j) {
+      v[j] = buf[64 * j + rslot];
+      pid[j] = pidx[32 * kPass * p + 8 * j + rl];
+    }
+#pragma unroll
+    for (int j = 0; j < nj; ++j)
+      if (32 * kPass * p + 8 * j + rl < nrows) *reinterpret_cast<u32x4_t*>(y + (size_t)pid[j] * a.n_out) = v[j];
   }
 }
 
@@ -181,14 +230,15 @@ __device__ __forceinline__ int f8_item(const GemmArgs& a, long long w, const int
   const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, 0x7FFFFFFF, 0x00020000);
   const __amdgpu_buffer_rsrc_t srs =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.act_scales, (short)0, 0x7FFFFFFF, 0x00020000);
-  // down GEMM: the pair index of each of this lane's output rows, loaded now for the epilogue
-  int pidx[kF8Sub];
+  // down GEMM: the pair index of each routed row of the item, straight into
+  // LDS for the epilogue (issued before the kgroup loads, so the K loop's
+  // waits cover it); rows past the expert's end repeat its last row
+  int* pidx = *f8_pidx();
   if constexpr (!G13) {
-#pragma unroll
-    for (int S = 0; S < kF8Sub; ++S) {
-      const int r = r0 + 32 * S + m;
-      pidx[S] = r < r_end ? a.sorted_pairs[r] : -1;
-    }
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.sorted_pairs, (short)0, 0x7FFFFFFF, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (__attribute__((address_space(3))) void*)&pidx[64 * wv], 4,
+                                             (uint32_t)min(r0 + 64 * wv + lane, r_end - 1) * 4u, 0, 0, 0);
   }
   // weights: this lane's unit of (gl, step 0, f 0, q 0), and its scale word of (gl, kgroup 0, f 0)
   const uint8_t* wsrc = a.wcodes + f8_unit_offset(e, a.G, gl, KS, 0, 0, 0, lane);
@@ -327,13 +377,18 @@ __device__ __forceinline__ int f8_item(const GemmArgs& a, long long w, const int
         body(A[u], *st.s[u]);
       }
     }
-    // drain the clamped loads; every wave done with the stages before the next item refills them
+    // drain the clamped loads (L2 hits of the last kgroup, issued a kgroup of
+    // matrix work ago); every wave done with the stages before the epilogue
+    // and the next item reuse them
     f8_wait_barrier<0>();
     if constexpr (NSA > 0)
       if (g < a.G) {
         if constexpr (G13) pf_epilogue<DT_MXFP8, G13, NSA, kF8Sub, 32>(a, acc, r0, r_end, g, e, lane);
-        else f8_down_epilogue<NSA>(a, acc, pidx, g, lane);
+        else f8_down_epilogue<NSA>(a, acc, pidx, r_end - r0, g, lane, wv, st);
       }
+    // every wave done reading its staged rows (the stores may stay in flight:
+    // a full __syncthreads would wait for all of them)
+    if constexpr (!G13) f8_wait_barrier<63>();
   };
   const int nsa = min(kF8Sub, (r_end - r0 + 31) >> 5);
   switch (nsa) {

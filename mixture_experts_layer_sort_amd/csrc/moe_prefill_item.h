@@ -198,7 +198,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
               uint2 dq;
               const uint32_t v = mx_encode4(h[4 * b], h[4 * b + 1], h[4 * b + 2], h[4 * b + 3], sx, dq);
               *reinterpret_cast<uint32_t*>(o + 8 * b) = v;
-              *reinterpret_cast<uint2*>(od + 8 * b) = dq;
+              if (a.out_deq) *reinterpret_cast<uint2*>(od + 8 * b) = dq;  // null: the copy is not read
             }
             if (hl == 0) a.out_scales[(size_t)r * (I / 32) + gg] = (uint8_t)(sx + 127);
           }
