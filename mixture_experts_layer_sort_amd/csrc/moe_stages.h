@@ -12,78 +12,99 @@ namespace moe {
 // (logit descending, id ascending) pick the experts; slot j is the j-th pick.
 // Weights: softmax over the k picked logits [vLLM PR 40082 report,
 // "Implementation" item 1: routing inside the fused call].
+//
+// The order is carried by one 64-bit key per expert: the logit mapped to an
+// unsigned integer of the same order (its high half; -0 counts as +0, NaN as
+// -inf) and the complement of the id (low half, so the smaller id of two
+// equal logits has the larger key); experts past E get key 0, below every
+// real one.  Each lane sorts its own keys once; a round is then one
+// wave-wide maximum of the lanes' first keys (DPP exchanges, no LDS), after
+// which the winning lane drops its first key.
 
-// (v, i) <- the better of (v, i) and (ov, oi): larger value, then smaller id
-__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
-  const bool b = ov > v || (ov == v && oi < i);
-  v = b ? ov : v;
-  i = b ? oi : i;
+__device__ __forceinline__ uint64_t route_key(float v, int id) {
+  v = (v == v) ? v + 0.0f : -INFINITY;  // NaN never wins; -0 -> +0 (equal logits tie on the id)
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)id;
+}
+__device__ __forceinline__ float route_key_value(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+__device__ __forceinline__ int route_key_id(uint64_t key) { return (int)~(uint32_t)key; }
+
+// x = max(x, the value DPP control CTRL brings from another lane); lanes
+// outside ROW_MASK keep their own value
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void max_dpp_u64(uint64_t& x) {
+  const uint32_t hi = (uint32_t)(x >> 32), lo = (uint32_t)x;
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  x = o > x ? o : x;
 }
 
-// Row-local exchange through the DPP crossbar (a few cycles, no LDS round trip)
-template <int CTRL>
-__device__ __forceinline__ void argmax_dpp(float& v, int& i) {
-  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-  const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false);
-  argmax_merge(v, i, ov, oi);
+// Wave-wide maximum of a 64-bit key; every lane receives it.  Within each row
+// of 16 lanes: swaps of neighbours (quad_perm 1,0,3,2), of pairs (2,3,0,1),
+// then the half-row and row mirrors; across rows: row 0's lane 15 into row 1
+// and row 2's into row 3 (row_bcast:15), then row 1's lane 31 into rows 2
+// and 3 (row_bcast:31); lane 63 then holds the wave's maximum.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  max_dpp_u64<0xB1, 0xF>(x);   // quad_perm [1, 0, 3, 2]
+  max_dpp_u64<0x4E, 0xF>(x);   // quad_perm [2, 3, 0, 1]
+  max_dpp_u64<0x141, 0xF>(x);  // row_half_mirror
+  max_dpp_u64<0x140, 0xF>(x);  // row_mirror
+  max_dpp_u64<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  max_dpp_u64<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// Wave-wide arg-max; every lane receives the winner.  Within each row of 16
-// lanes: swaps of neighbours (quad_perm 1,0,3,2), of pairs (2,3,0,1), then
-// the half-row and row mirrors; the four row winners are then read from
-// lanes 0, 16, 32, 48 and merged in row order.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_dpp<0xB1>(v, i);   // quad_perm [1, 0, 3, 2]
-  argmax_dpp<0x4E>(v, i);   // quad_perm [2, 3, 0, 1]
-  argmax_dpp<0x141>(v, i);  // row_half_mirror
-  argmax_dpp<0x140>(v, i);  // row_mirror
-  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r)
-    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r)),
-                 __builtin_amdgcn_readlane(i, 16 * r));
-  v = bv;
-  i = bi;
+// Descending compare-exchange of keys a, b (a keeps the larger)
+__device__ __forceinline__ void route_cx(uint64_t& a, uint64_t& b) {
+  const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+  a = hi;
+  b = lo;
 }
 
 template <int NV>
 __device__ __forceinline__ void route_token_n(const float* __restrict__ logits, int t, int E, int k,
                                               int* __restrict__ ids, float* __restrict__ wts, int lane) {
   const float* row = logits + (size_t)t * E;
-  float v[NV];
-  uint32_t taken = 0;
+  uint64_t key[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    int e = lane + 64 * i;
-    float x = e < E ? row[e] : -INFINITY;
-    v[i] = (x == x) ? x : -INFINITY;  // NaN never wins; results stay in range
-    if (e >= E) taken |= 1u << i;
+    const int e = lane + 64 * i;
+    key[i] = e < E ? route_key(row[e], e) : 0ull;
   }
-  float my_val = 0.f, m0 = 0.f, sum = 0.f;
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+  // this lane's keys in descending order (Batcher's odd-even merge sort network)
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int id = lane + 64 * i;
-      bool better = !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && id < bi));
-      bv = better ? v[i] : bv;
-      bi = better ? id : bi;
-    }
-    wave_argmax(bv, bi);  // uniform across the wave from here
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (j == 0) m0 = bv;
-    sum += expf(bv - m0);  // the softmax denominator, in pick order
-    if (lane == j) {
-      my_val = bv;
-      my_id = bi;
-    }
+  for (int p = 1; p < NV; p <<= 1)
+#pragma unroll
+    for (int q = p; q >= 1; q >>= 1)
+#pragma unroll
+      for (int j = q % p; j + q < NV; j += 2 * q)
+#pragma unroll
+        for (int i = 0; i < q && i + j + q < NV; ++i)
+          if ((i + j) / (2 * p) == (i + j + q) / (2 * p)) route_cx(key[i + j], key[i + j + q]);
+  uint64_t mine = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint64_t w = wave_max_u64(key[0]);  // uniform: pick j
+    const bool win = key[0] == w;              // the one lane that held it drops it
+#pragma unroll
+    for (int i = 0; i + 1 < NV; ++i) key[i] = win ? key[i + 1] : key[i];
+    key[NV - 1] = win ? 0ull : key[NV - 1];
+    mine = lane == j ? w : mine;
   }
+  // slot `lane` < k: softmax over the picks, the denominator summed in pick order
+  const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(route_key_value(mine)), 0));
+  const float ex = expf(route_key_value(mine) - m0);
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    wts[(size_t)t * k + lane] = expf(my_val - m0) / sum;
+    ids[(size_t)t * k + lane] = route_key_id(mine);
+    wts[(size_t)t * k + lane] = ex / sum;
   }
 }
 

@@ -194,6 +194,34 @@ def _check_layer(w, name, x, logits):
     assert not layer.sync_words().any()
 
 
+@pytest.mark.parametrize("dtype,E,k", [("bf16", 8, 2), ("mxfp8", 64, 6), ("nvfp4", 256, 8), ("mxfp8", 384, 8),
+                                        ("bf16", 1024, 32)])
+def test_forward_routing_matches_staged(dtype, E, k):
+    """At token counts around the routing kernel's 4-token blocks and the
+    sorting block's 8-wave segments, moe_forward's routing, weights and output
+    equal those of the separate moe_route / moe_permute chain bit for bit,
+    and the routing equals the oracle's (ties and E up to 1024, k up to 32)."""
+    base = {"bf16": W["bf16_decode"], "mxfp8": W["mxfp8_decode"], "nvfp4": W["nvfp4_decode_t8"]}[dtype]
+    w = base.scaled(T=33, H=128, I=128, E=E, k=k)
+    cw, _ = _setup(w)
+    layer = gh.DeviceLayer(w, cw)
+    x_all = mi.host_x(w)
+    rng = np.random.default_rng(E * 31 + k)
+    for T in (1, 7, 8, 9, 16, 17, 25, 31, 32, 33):
+        l = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+        l[:, : min(E, 3)] = 0.25  # exact ties, broken by the smaller id
+        xd, ld = gh.to_device_x(x_all[:T]), torch.from_numpy(l).to(gh.dev())
+        r = layer.staged(xd, ld)
+        ids = torch.empty(T, k, dtype=torch.int32, device=gh.dev())
+        wts = torch.empty(T, k, dtype=torch.float32, device=gh.dev())
+        o = layer.forward(xd, ld, ids=ids, wts=wts)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, r["ids"]) and torch.equal(wts, r["wts"]), T
+        assert np.array_equal(gh.bf16_numpy(o), gh.bf16_numpy(r["out"])), T
+        rid, _ = omoe.route(l, k)
+        assert np.array_equal(ids.cpu().numpy(), rid), T
+
+
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (7, 8, 2), (64, 64, 6), (33, 256, 8), (5, 384, 8), (3, 1024, 32),
                                    (200, 1000, 9), (4, 32, 32)])
 def test_route_parity(T, E, k):
