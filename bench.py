@@ -402,7 +402,8 @@ def main():
     # reproducible), flushed and timed like the eager steps (context)
     fc2_ms_step = None
     if w.k >= 2 and not args.skip_fc2:
-        fc2_knobs = lib.make_knobs(knobs.gemm, knobs.down_fp8, knobs.band_rows, 1)
+        fc2_knobs = lib.make_knobs(knobs.gemm, knobs.down_fp8, knobs.band_rows, 1, knobs.blocks_per_cu,
+                                   knobs.load_balance)
 
         def forward_fc2():
             lib.moe_forward_knobs(layer.shape, w.T, layer.packed, logits, x, out, layer.ws, fc2_knobs)

@@ -366,23 +366,36 @@ MOE_API moe_status moe_forward_noalloc(const moe_shape* shape, int32_t T, const 
  *   blocks_per_cu  persistent grid of the grouped GEMMs, blocks per compute
  *              unit (0: as many as fit at once; 1..16 otherwise; blocks past
  *              the resident capacity start as earlier ones finish).
- *              Performance knob. */
+ *              Performance knob.
+ *   load_balance  prefill-shaped items: how the persistent blocks deal the
+ *              item order, chunk by chunk of (grid) consecutive items, each
+ *              XCD taking one slice of 1/8 of a chunk.  0 (default): XCD x
+ *              always takes slice x (its L2 keeps the same weight n-blocks
+ *              from chunk to chunk); 1: the slice rotates over the XCDs every
+ *              chunk and each block's place in it every chunk (item costs
+ *              follow the expert-major order, so a fixed slice can leave one
+ *              XCD the costlier places chunk after chunk); 2: the slice
+ *              rotates every fourth chunk, the place every chunk.
+ *              Performance knob (each item is computed the same way wherever
+ *              it runs); ignored by the decode-shaped items. */
 typedef struct moe_knobs {
   int32_t gemm;
   int32_t down_fp8;
   int32_t band_rows;
   int32_t fc2_reduce;
   int32_t blocks_per_cu;
+  int32_t load_balance;
 } moe_knobs;
 
-/* The default knobs: {0, 1, 0, 0, 0}. */
+/* The default knobs: {0, 1, 0, 0, 0, 0}. */
 MOE_API void moe_default_knobs(moe_knobs* knobs);
 
 /* moe_forward with explicit knobs (NULL = the defaults).  Same arguments and
  * workspace as moe_forward; with the default knobs the results are bitwise
  * those of moe_forward.  MOE_ERR_INVALID_ARG for a knob out of range (gemm
  * outside [0, 3], down_fp8 / fc2_reduce outside {0, 1}, band_rows outside
- * [0, 2^20], blocks_per_cu outside [0, 16]); MOE_ERR_UNSUPPORTED for fc2_reduce with top_k == 1, for
+ * [0, 2^20], blocks_per_cu outside [0, 16], load_balance outside [0, 2]);
+ * MOE_ERR_UNSUPPORTED for fc2_reduce with top_k == 1, for
  * gemm = 1 with more than 16 (65535 - num_experts) routed rows (T top_k), and
  * for gemm = 3 where T hidden or T top_k inter reaches 2^30 (the prefill-shaped
  * GEMMs address activation rows with 31-bit byte offsets; the default knobs
@@ -394,6 +407,7 @@ MOE_API moe_status moe_forward_knobs(const moe_shape* shape, int32_t T, const vo
 /* Persistent knob cache lookup (host only, no device work).  The cache is a
  * text file of lines
  *     dtype act hidden inter experts top_k t_min t_max : gemm down_fp8 band_rows fc2_reduce blocks_per_cu
+ *                                                         load_balance
  * (dtype: bf16 | mxfp8 | nvfp4 | bf16_mxfp8; act: swiglu | relu2; '#' starts
  * a comment).  The first line whose shape matches `shape` and whose token
  * range t_min <= T <= t_max holds T fills *knobs and sets *found = 1;

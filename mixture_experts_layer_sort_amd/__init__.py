@@ -83,7 +83,8 @@ class moe_shape(ctypes.Structure):
 class moe_knobs(ctypes.Structure):
     """How the grouped GEMMs of one call run (gemm variant 0 auto / 1 decode
     16-row / 2 decode 32-row / 3 prefill; MXFP8 fp8 down GEMM; prefill band
-    rows; in-kernel fc2 reduce; persistent blocks per compute unit)."""
+    rows; in-kernel fc2 reduce; persistent blocks per compute unit; prefill
+    item deal over the XCDs and blocks)."""
 
     _fields_ = [
         ("gemm", ctypes.c_int32),
@@ -91,6 +92,7 @@ class moe_knobs(ctypes.Structure):
         ("band_rows", ctypes.c_int32),
         ("fc2_reduce", ctypes.c_int32),
         ("blocks_per_cu", ctypes.c_int32),
+        ("load_balance", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -319,8 +321,8 @@ def moe_default_knobs() -> moe_knobs:
     return kn
 
 
-def make_knobs(gemm=0, down_fp8=1, band_rows=0, fc2_reduce=0, blocks_per_cu=0) -> moe_knobs:
-    return moe_knobs(gemm, down_fp8, band_rows, fc2_reduce, blocks_per_cu)
+def make_knobs(gemm=0, down_fp8=1, band_rows=0, fc2_reduce=0, blocks_per_cu=0, load_balance=0) -> moe_knobs:
+    return moe_knobs(gemm, down_fp8, band_rows, fc2_reduce, blocks_per_cu, load_balance)
 
 
 def moe_forward_knobs(shape, T, packed, logits, x, out, ws, knobs=None, ws_bytes=None, topk_ids=None, topk_w=None,

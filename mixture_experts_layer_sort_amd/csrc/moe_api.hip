@@ -356,12 +356,13 @@ moe_status moe_forward(const moe_shape* s, int32_t T, const void* packed, const 
 }
 
 void moe_default_knobs(moe_knobs* kn) {
-  if (kn) *kn = moe_knobs{0, 1, 0, 0, 0};
+  if (kn) *kn = moe_knobs{0, 1, 0, 0, 0, 0};
 }
 
 static bool knobs_valid(const moe_knobs& kn) {
   return kn.gemm >= 0 && kn.gemm <= 3 && (kn.down_fp8 | 1) == 1 && (kn.fc2_reduce | 1) == 1 && kn.band_rows >= 0 &&
-         kn.band_rows <= (1 << 20) && kn.blocks_per_cu >= 0 && kn.blocks_per_cu <= 16;
+         kn.band_rows <= (1 << 20) && kn.blocks_per_cu >= 0 && kn.blocks_per_cu <= 16 && kn.load_balance >= 0 &&
+         kn.load_balance <= 2;
 }
 
 moe_status moe_forward_knobs(const moe_shape* s, int32_t T, const void* packed, const float* logits,
@@ -383,6 +384,7 @@ moe_status moe_forward_knobs(const moe_shape* s, int32_t T, const void* packed, 
   p.down_fp8 = p.down_fp8 && kn.down_fp8 != 0;
   p.band = kn.band_rows;
   p.blocks_per_cu = kn.blocks_per_cu;
+  p.balance = kn.load_balance;
   return forward_staged(s, T, s->max_tokens, packed, logits, x, out, topk_ids, topk_w, (uint8_t*)ws, p,
                         kn.fc2_reduce != 0, stream);
 }
@@ -508,7 +510,7 @@ moe_status moe_knob_cache_lookup(const char* path, const moe_shape* s, int32_t T
   moe_status st = MOE_OK;
   while (fgets(line, sizeof line, f)) {
     if (char* c = strchr(line, '#')) *c = 0;
-    constexpr int kKeys = 8, kKnobs = 5, kTok = kKeys + 1 + kKnobs;
+    constexpr int kKeys = 8, kKnobs = 6, kTok = kKeys + 1 + kKnobs;
     char* tok[kTok];
     int n = 0;
     char* save = nullptr;
@@ -528,7 +530,8 @@ moe_status moe_knob_cache_lookup(const char* path, const moe_shape* s, int32_t T
     }
     const int dt = ok ? parse_dtype(tok[0]) : -1;
     const int act = ok ? (!strcmp(tok[1], "swiglu") ? MOE_SWIGLU : !strcmp(tok[1], "relu2") ? MOE_RELU2 : -1) : -1;
-    const moe_knobs kn{(int32_t)v[8], (int32_t)v[9], (int32_t)v[10], (int32_t)v[11], (int32_t)v[12]};
+    const moe_knobs kn{(int32_t)v[8],  (int32_t)v[9],  (int32_t)v[10],
+                       (int32_t)v[11], (int32_t)v[12], (int32_t)v[13]};
     if (!ok || dt < 0 || act < 0 || !knobs_valid(kn)) {
       st = MOE_ERR_INVALID_ARG;
       break;

@@ -303,6 +303,7 @@ hipError_t launch_fused(int dt, bool gated, int E, int H, int I, int k, int T, c
   g.limit = gated ? limit : 0.f;
   h.limit = 0.f;
   g.band = h.band = 0;
+  g.balance = h.balance = 0;
   g.red = h.red = nullptr;
   g.wts = h.wts = nullptr;
   const int v = fused_variant(dt, T, k, E, H, I);

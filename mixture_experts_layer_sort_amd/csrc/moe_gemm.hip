@@ -194,6 +194,7 @@ hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, 
   a.gated = gated;
   a.limit = gated ? plan.limit : 0.f;
   a.band = plan.band;
+  a.balance = plan.balance;
   a.red = nullptr;
   a.wts = nullptr;
   a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
@@ -220,6 +221,7 @@ hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, c
   a.gated = gated;
   a.limit = 0.f;
   a.band = plan.band;
+  a.balance = plan.balance;
   a.red = plan.red;
   a.wts = plan.wts;
   a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
@@ -292,6 +294,7 @@ hipError_t launch_dense_gemm(int M, int N, int K, const uint8_t* packed, const i
   a.band = 0;
   a.red = nullptr;
   a.wts = nullptr;
+  a.balance = 0;
   a.E = 1; a.K = K; a.G = D.G; a.KG = D.KG; a.k = 1; a.n_out = N;
   if (gemm_prefill(M, 1, 1)) return launch_prefill(DT_NVFP4, false, a, grid, s);
   return dispatch_gemm<false>(DT_NVFP4, gemm_nt(M, 1, 1), a, grid, s);

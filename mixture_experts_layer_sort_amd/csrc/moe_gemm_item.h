@@ -25,6 +25,7 @@ struct GemmArgs {
   int gated;                  // gate/up GEMM: 1 SwiGLU (gate/up row pairs), 0 ReLU^2 (64 W1 rows per group)
   float limit;                // SwiGLU gate/up clamp L (0: none): gate = min(gate, L), up = clamp(up, -L, L)
   int band;                   // prefill item order: token rows per band (0: the kernel's default, 1024)
+  int balance;                // prefill item deal over the blocks (pf_chunk_slot)
   float* red;                 // down GEMM, in-kernel fc2 reduce: fp32 out [T, H] += wts[p] * y[p] (atomics);
                               // null: y rows are written
   const float* wts;           // the router weights of the pairs (with red)

@@ -58,6 +58,7 @@ struct GemmPlan {
   bool skip_hq_deq = false;
   int band = 0;
   int blocks_per_cu = 0;
+  int balance = 0;  // prefill item deal (moe_knobs.load_balance)
   float limit = 0.f;
   float* red = nullptr;
   const float* wts = nullptr;

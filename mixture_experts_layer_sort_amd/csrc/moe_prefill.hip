@@ -28,7 +28,10 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmArgs a) {
   const auto st = pf_make_stages<DT, ROWS>();
   const int total_mt = build_schedule(a.offsets, a.E, ROWS, cum, wsum);
   const long long total = (long long)total_mt * ((a.G + kPfGroups - 1) / kPfGroups);
-  for (long long w = xcd_logical_block(); w < total; w += gridDim.x) prefill_item<DT, G13, 2, ROWS>(a, w, cum, st);
+  for (long long n = 0; n * gridDim.x < total; ++n) {
+    const long long w = n * gridDim.x + pf_chunk_slot(n, a.balance);
+    if (w < total) prefill_item<DT, G13, 2, ROWS>(a, w, cum, st);
+  }
 }
 
 template <int DT, bool G13>
@@ -50,7 +53,10 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   const F8Stages st = f8_make_stages();
   const int total_mt = build_schedule(a.offsets, a.E, kF8Rows, cum, wsum);
   const long long total = (long long)total_mt * ((a.G + kPfGroups - 1) / kPfGroups);
-  for (long long w = xcd_logical_block(); w < total; w += gridDim.x) f8_item<G13>(a, w, cum, st);
+  for (long long n = 0; n * gridDim.x < total; ++n) {
+    const long long w = n * gridDim.x + pf_chunk_slot(n, a.balance);
+    if (w < total) f8_item<G13>(a, w, cum, st);
+  }
 }
 
 static const void* prefill_f8_ptr(bool g13) {

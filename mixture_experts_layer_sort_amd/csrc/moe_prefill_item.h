@@ -92,6 +92,24 @@ __device__ __forceinline__ int xcd_logical_block() {
   return g % 8 == 0 ? (b % 8) * (g / 8) + b / 8 : b;
 }
 
+// Slot of this block in chunk n of the persistent item order (chunks of
+// gridDim.x consecutive items; the block takes item n gridDim.x + slot).
+// The blocks of XCD x (b % 8 == x) take one contiguous slice of C =
+// gridDim.x / 8 items of each chunk, so items that share weight or token
+// tiles meet in one L2 (grids that are not a multiple of 8: block b takes
+// place b).  `balance` (moe_knobs.load_balance) picks the slice and place:
+// 0: slice x, place b / 8 every chunk (xcd_logical_block); 1: slice
+// (x + n) % 8, place (b / 8 + n) % C; 2: slice (x + n / 4) % 8, place
+// (b / 8 + n) % C.  Each is a permutation of the chunk's places.
+__device__ __forceinline__ int pf_chunk_slot(long long n, int balance) {
+  const int b = blockIdx.x, g = gridDim.x;
+  if (g % 8 != 0) return b;
+  const int C = g / 8, x = b % 8, j = b / 8, r = (int)(n % (32LL * C));
+  if (balance == 1) return ((x + r) % 8) * C + (j + r) % C;
+  if (balance == 2) return ((x + r / 4) % 8) * C + (j + r) % C;
+  return x * C + j;
+}
+
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding and all its LDS reads are done, then barrier.  No fence: the
 // direct-to-LDS loads of later stages stay in flight across it.

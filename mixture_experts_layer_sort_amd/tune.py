@@ -7,8 +7,9 @@ For every workload (a synthetic layer shape from moe_inputs) and token count,
 each candidate knob setting runs the whole layer (moe_forward_knobs) for
 `steps` timed steps, each between its own HIP event pair with the L2 and the
 Infinity Cache flushed before it; the candidate with the lowest median step
-time wins (the default knobs win ties within 2 %, about the run-to-run
-spread of the step times).  The pages sweep a knob
+time wins, where settings within 5 % of the fastest (about the spread of
+repeated runs of one setting) count as tied and of those the one closest to
+the default knobs is kept.  The pages sweep a knob
 candidate list per shape, keep the winner in a persistent cache keyed by
 shape, and resolve knobs from that cache before a default heuristic
 [MegaMoE drop workflow, §4 step 3 and §6]; here every candidate is already
@@ -38,23 +39,39 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DEFAULT_WORKLOADS = ("bf16_decode", "mxfp8_decode", "nvfp4_decode_t8", "nvfp4_decode_t128", "mxfp8_prefill")
 BANDS = (0, 256, 512, 2048, 4096, 8192)
 DECODE_BLOCKS = (0, 2, 4, 5, 6, 8)
+LOAD_BALANCE = (0, 1, 2)
 MAX_T = 1 << 24
-TIE = 1.02  # the default knobs win unless another setting is faster by more than this factor
+# Settings within this factor of the fastest count as tied (above the spread of single sweep runs:
+# repeated runs of one setting differ by up to ~4 %); of the tied settings the one with the fewest
+# knobs away from the defaults wins, so the defaults win whenever they are tied.
+TIE = 1.05
+
+
+KNOBS = 6  # gemm, down_fp8, band_rows, fc2_reduce, blocks_per_cu, load_balance
 
 
 def candidates(w, T, fc2):
-    """Knob tuples (gemm, down_fp8, band_rows, fc2_reduce, blocks_per_cu) for workload w at T tokens."""
+    """Knob tuples (gemm, down_fp8, band_rows, fc2_reduce, blocks_per_cu, load_balance) for workload w at T
+    tokens."""
     mx = w.dtype == "mxfp8"
     out = []
     for red in ((0, 1) if fc2 and w.k >= 2 else (0,)):
         for gemm in (1, 2):
             for blocks in DECODE_BLOCKS:
-                out.append((gemm, 1, 0, red, blocks))
+                out.append((gemm, 1, 0, red, blocks, 0))
         for down in ((1, 0) if mx else (1,)):
             for band in BANDS:
-                out.append((3, down, band, red, 0))
-        out.append((3, 1, 0, red, 2))
+                out.append((3, down, band, red, 0, 0))
+            for balance in LOAD_BALANCE[1:]:
+                out.append((3, down, 0, red, 0, balance))
+        out.append((3, 1, 0, red, 2, 0))
     return out
+
+
+def full_knobs(kn):
+    """A recorded knob tuple with the knobs added since it was recorded at their defaults (0)."""
+    kn = tuple(kn)
+    return kn + (0,) * (KNOBS - len(kn))
 
 
 def auto_gemm(T, k, E):
@@ -124,41 +141,47 @@ def sweep(lib, w, tokens, steps, warmup, fc2, device, log):
 
 
 def pick(w, T, rows):
-    default = (auto_gemm(T, w.k, w.E), 1, 0, 0, 0)
-    best = min(rows, key=lambda r: r[1])
+    """(the chosen (knobs, ms), the default knobs' (knobs, ms) or None)."""
+    default = (auto_gemm(T, w.k, w.E), 1, 0, 0, 0, 0)
+    best = min(r[1] for r in rows)
+    tied = [r for r in rows if r[1] <= TIE * best]
+    chosen = min(tied, key=lambda r: (sum(a != b for a, b in zip(r[0], default)), r[1]))
     d = [r for r in rows if r[0] == default]
-    if d and d[0][1] <= TIE * best[1]:
-        return d[0], d[0]
-    return best, (d[0] if d else None)
+    return chosen, (d[0] if d else None)
 
 
 def sweep_all(lib, mi, args, device, by_shape, record, log):
-    """Sweep every requested shape; fills by_shape {key: {T: (knobs, ms, default_ms, label)}} and record."""
-    # workloads of one layer shape are swept together, on one set of weights
+    """Sweep every requested shape; fills by_shape {key: {T: (knobs, ms, default_ms, label)}} and record.
+    Workloads of one layer shape write one set of cache lines; each token count is timed with the routing
+    of the workload that asks for it (a skewed prefill batch and a decode batch of the same shape route
+    differently)."""
     groups = {}
     for item in args.workloads.split(","):
         name, _, own = item.partition(":")
         w = mi.WORKLOADS[name]
-        g = groups.setdefault(shape_key(w), [w, set(), []])
         if own:
-            g[1].update(int(t) for t in own.split("+"))
+            tokens = {int(t) for t in own.split("+")}
         elif args.tokens:
-            g[1].update(int(t) for t in args.tokens.split(","))
+            tokens = {int(t) for t in args.tokens.split(",")}
         else:
-            g[1].add(w.T)
-        g[2].append(name)
-    for key, (w, tokens, names) in groups.items():
-        tokens = sorted(tokens)
-        label = "+".join(names)
-        log(f"sweeping {label} at T = {tokens}")
-        res = sweep(lib, w, tokens, args.steps, args.warmup, args.fc2, device, log)
-        for T, rows in res.items():
-            (kn, ms), dflt = pick(w, T, rows)
-            by_shape.setdefault(key, {})[T] = (kn, ms, dflt[1] if dflt else None, label)
-            record.append({"workloads": names, "shape": list(key), "T": T, "winner": list(kn), "ms": ms,
-                           "default_ms": dflt[1] if dflt else None,
-                           "candidates": [{"knobs": list(k), "ms": m} for k, m in rows]})
-            log(f"{label} T={T}: knobs {kn} {ms:.4f} ms (default {dflt[1] if dflt else float('nan'):.4f} ms)")
+            tokens = {w.T}
+        groups.setdefault(shape_key(w), []).append((w, tokens))
+    for key, members in groups.items():
+        taken = set()
+        for w, tokens in members:
+            tokens = sorted(tokens - taken)  # a token count two workloads ask for: the first one's routing
+            taken.update(tokens)
+            if not tokens:
+                continue
+            log(f"sweeping {w.name} at T = {tokens}")
+            res = sweep(lib, w, tokens, args.steps, args.warmup, args.fc2, device, log)
+            for T, rows in res.items():
+                (kn, ms), dflt = pick(w, T, rows)
+                by_shape.setdefault(key, {})[T] = (kn, ms, dflt[1] if dflt else None, w.name)
+                record.append({"workloads": [w.name], "shape": list(key), "T": T, "winner": list(kn), "ms": ms,
+                               "default_ms": dflt[1] if dflt else None,
+                               "candidates": [{"knobs": list(k), "ms": m} for k, m in rows]})
+                log(f"{w.name} T={T}: knobs {kn} {ms:.4f} ms (default {dflt[1] if dflt else float('nan'):.4f} ms)")
 
 
 def main(argv=None):
@@ -192,7 +215,7 @@ def main(argv=None):
             for rec in data["sweeps"] if isinstance(data, dict) else data:
                 key = tuple(rec["shape"])
                 w = mi.WORKLOADS[rec["workloads"][0]]
-                rows = [(tuple(c["knobs"]), c["ms"]) for c in rec["candidates"]]
+                rows = [(full_knobs(c["knobs"]), c["ms"]) for c in rec["candidates"]]
                 (kn, ms), dflt = pick(w, rec["T"], rows)
                 by_shape.setdefault(key, {})[rec["T"]] = (kn, ms, dflt[1] if dflt else None,
                                                           "+".join(rec["workloads"]))
@@ -205,7 +228,8 @@ def main(argv=None):
 
     cmd = "python -m mixture_experts_layer_sort_amd.tune " + " ".join(argv if argv is not None else sys.argv[1:])
     lines = ["# Knob cache of the MoE layer library (moe_knob_cache_lookup).",
-             "# dtype act hidden inter experts top_k t_min t_max : gemm down_fp8 band_rows fc2_reduce blocks_per_cu",
+             "# dtype act hidden inter experts top_k t_min t_max : gemm down_fp8 band_rows fc2_reduce blocks_per_cu"
+             " load_balance",
              f"# written by: {cmd.strip()}",
              "# each line: the fastest knobs at the swept token count (median of flushed steps on one MI355X)"]
     for key in sorted(by_shape):
@@ -216,7 +240,8 @@ def main(argv=None):
             # a winning variant that the heuristic picks anyway is written as 0 (auto), so calls of other
             # sizes in the line's range keep the per-call choice
             gemm = 0 if kn[0] == auto_gemm(T, k, E) else kn[0]
-            lines.append(f"{dtype} {act} {H} {I} {E} {k} {lo} {hi} : {gemm} {kn[1]} {kn[2]} {kn[3]} {kn[4]}  # {note}")
+            lines.append(f"{dtype} {act} {H} {I} {E} {k} {lo} {hi} : {gemm} {kn[1]} {kn[2]} {kn[3]} {kn[4]} {kn[5]}"
+                         f"  # {note}")
     path = args.out or lib.KNOB_CACHE_PATH
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")

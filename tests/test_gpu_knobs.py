@@ -4,8 +4,9 @@ Knobs choose among compiled kernel variants [MegaMoE drop workflow, §4 step 3
 and §6]: the GEMM variant (decode-shaped 16/32-row token tiles or the
 prefill-shaped items) and the MXFP8 fp8 down GEMM change the fp32
 accumulation order (correctness knobs: the output must meet the oracle
-tolerance); the prefill band and the persistent grid size only reorder work
-items (performance knobs: the output bits must not change); the in-kernel fc2 reduce sums w * y with
+tolerance); the prefill band, the persistent grid size and the load-balance
+deal only reorder work items (performance knobs: the output bits must not
+change); the in-kernel fc2 reduce sums w * y with
 fp32 atomics in scheduling order (tolerance only, not reproducible bitwise).
 Each case forces every variant on shapes the oracle finishes in seconds,
 including variants the default heuristic would not pick for that shape.
@@ -42,10 +43,11 @@ def _knob_grid(w):
     for gemm, d, fc2 in itertools.product((1, 2, 3), down, (0, 1)):
         if fc2 and w.k < 2:
             continue
-        # performance knobs: the band (prefill-shaped items) and the persistent grid
-        perf = [(0, 0), (128, 0), (4096, 0), (0, 2)] if gemm == 3 else [(0, 0), (0, 1), (0, 5)]
-        for band, blocks in perf:
-            out.append((gemm, d, band, fc2, blocks))
+        # performance knobs: the band and the item deal (prefill-shaped items) and the persistent grid
+        perf = ([(0, 0, 0), (128, 0, 0), (4096, 0, 0), (0, 2, 0), (0, 0, 1), (0, 2, 2), (128, 0, 2)] if gemm == 3
+                else [(0, 0, 0), (0, 1, 0), (0, 5, 0), (0, 0, 1)])
+        for band, blocks, balance in perf:
+            out.append((gemm, d, band, fc2, blocks, balance))
     return out
 
 
@@ -69,9 +71,9 @@ def test_forward_knobs_parity(name):
         got = gh.bf16_numpy(layer.forward_knobs(xd, ld, lib.make_knobs(*kn)))
         rel, mad = gh.check_out(got, ref.out, w.dtype, f"{name} knobs {kn}")
         print(f"  knobs {kn}: out relL2 {rel:.2e} max|d|/rms {mad:.2e}", flush=True)
-        gemm, d, band, fc2, blocks = kn
+        gemm, d, band, fc2, blocks, balance = kn
         if not fc2:
-            # the band and the grid reorder items only: the same bits
+            # the band, the grid and the item deal reorder items only: the same bits
             key = (gemm, d)
             if key in by_plan:
                 assert np.array_equal(got, by_plan[key]), kn

@@ -13,7 +13,7 @@ import mixture_experts_layer_sort_amd as lib
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
 FAKE = 0x1000  # never dereferenced: every call below returns before enqueueing
 
-LINE = "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 5\n"
+LINE = "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 5 2\n"
 
 
 def _shape(H=7168, I=2048, E=256, k=8, T=8192, dt="mxfp8", act="swiglu"):
@@ -28,7 +28,7 @@ def _write(tmp_path, text, name="knobs.txt"):
 
 def test_default_knobs():
     assert lib.moe_default_knobs().as_dict() == {"gemm": 0, "down_fp8": 1, "band_rows": 0, "fc2_reduce": 0,
-                                                 "blocks_per_cu": 0}
+                                                 "blocks_per_cu": 0, "load_balance": 0}
 
 
 def test_missing_file_gives_defaults(tmp_path):
@@ -42,7 +42,8 @@ def test_matching_line_and_token_range(tmp_path):
         kn, found = lib.moe_knob_cache_lookup(_shape(), T, path=path)
         assert found == hit, T
         if hit:
-            assert kn.as_dict() == {"gemm": 3, "down_fp8": 1, "band_rows": 2048, "fc2_reduce": 0, "blocks_per_cu": 5}
+            assert kn.as_dict() == {"gemm": 3, "down_fp8": 1, "band_rows": 2048, "fc2_reduce": 0, "blocks_per_cu": 5,
+                                    "load_balance": 2}
         else:
             assert kn.as_dict() == lib.moe_default_knobs().as_dict()
 
@@ -59,37 +60,39 @@ def test_every_shape_field_is_part_of_the_key(tmp_path, field, value):
 
 
 def test_first_matching_line_wins_and_comments_are_ignored(tmp_path):
-    text = ("bf16 swiglu 7168 2048 256 8 0 100000 : 1 1 0 0 0\n"      # other dtype
-            "mxfp8 swiglu 7168 2048 256 8 1 4095 : 1 1 0 0 4   # small T\n"
-            "mxfp8 swiglu 7168 2048 256 8 4096 9000 : 3 0 512 1 0\n"
-            "mxfp8 swiglu 7168 2048 256 8 0 100000 : 2 1 0 0 0\n")
+    text = ("bf16 swiglu 7168 2048 256 8 0 100000 : 1 1 0 0 0 0\n"      # other dtype
+            "mxfp8 swiglu 7168 2048 256 8 1 4095 : 1 1 0 0 4 0   # small T\n"
+            "mxfp8 swiglu 7168 2048 256 8 4096 9000 : 3 0 512 1 0 1\n"
+            "mxfp8 swiglu 7168 2048 256 8 0 100000 : 2 1 0 0 0 0\n")
     path = _write(tmp_path, text)
     assert lib.moe_knob_cache_lookup(_shape(), 64, path=path)[0].as_dict()["gemm"] == 1
     kn, found = lib.moe_knob_cache_lookup(_shape(), 8192, path=path)
-    assert found and kn.as_dict() == {"gemm": 3, "down_fp8": 0, "band_rows": 512, "fc2_reduce": 1, "blocks_per_cu": 0}
+    assert found and kn.as_dict() == {"gemm": 3, "down_fp8": 0, "band_rows": 512, "fc2_reduce": 1, "blocks_per_cu": 0,
+                                      "load_balance": 1}
     assert lib.moe_knob_cache_lookup(_shape(), 9001, path=path)[0].as_dict()["gemm"] == 2
 
 
 @pytest.mark.parametrize("bad", [
-    "mxfp8 swiglu 7168 2048 256 8 4096 16384 3 1 2048 0 0\n",        # no ':'
-    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0\n",        # a knob missing
-    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0 7\n",    # one too many
-    "fp16 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0\n",       # unknown dtype
-    "mxfp8 gelu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0\n",        # unknown activation
-    "mxfp8 swiglu 7168 2048 256 8 4096 1e5 : 3 1 2048 0 0\n",        # not an integer
-    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 4 1 2048 0 0\n",      # gemm out of range
-    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 2 2048 0 0\n",      # down_fp8 not 0/1
-    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 -1 0 0\n",        # negative band
-    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 2 0\n",      # fc2_reduce not 0/1
-    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 17\n",     # blocks_per_cu out of range
-    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 99999999999 0 0\n",  # beyond 32 bits
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 3 1 2048 0 0 0\n",      # no ':'
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0\n",      # a knob missing
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0 0 7\n",  # one too many
+    "fp16 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0 0\n",     # unknown dtype
+    "mxfp8 gelu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0 0\n",      # unknown activation
+    "mxfp8 swiglu 7168 2048 256 8 4096 1e5 : 3 1 2048 0 0 0\n",      # not an integer
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 4 1 2048 0 0 0\n",    # gemm out of range
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 2 2048 0 0 0\n",    # down_fp8 not 0/1
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 -1 0 0 0\n",      # negative band
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 2 0 0\n",    # fc2_reduce not 0/1
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 17 0\n",   # blocks_per_cu out of range
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0 3\n",    # load_balance out of range
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 99999999999 0 0 0\n",  # beyond 32 bits
     # a malformed line after a line of another shape is still an error
-    "bf16 swiglu 64 128 8 2 1 10 : 0 1 0 0 0\nmxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0\n",
+    "bf16 swiglu 64 128 8 2 1 10 : 0 1 0 0 0 0\nmxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0\n",
 ])
 def test_malformed_lines_are_errors(tmp_path, bad):
     path = _write(tmp_path, bad)
     h = lib.load()
-    kn, found = lib.moe_knobs(9, 9, 9, 9, 9), ctypes.c_int32(7)
+    kn, found = lib.moe_knobs(9, 9, 9, 9, 9, 9), ctypes.c_int32(7)
     st = h.moe_knob_cache_lookup(os.fsencode(path), ctypes.byref(_shape()), 8192, ctypes.byref(kn),
                                  ctypes.byref(found))
     assert st == INVALID and found.value == 0
@@ -109,7 +112,8 @@ def test_lookup_null_arguments():
 @pytest.mark.parametrize("knobs,status", [
     ((-1, 1, 0, 0), INVALID), ((4, 1, 0, 0), INVALID), ((0, 2, 0, 0), INVALID), ((0, -1, 0, 0), INVALID),
     ((0, 1, -1, 0), INVALID), ((0, 1, (1 << 20) + 1, 0), INVALID), ((0, 1, 0, 2), INVALID),
-    ((0, 1, 0, 0, -1), INVALID), ((0, 1, 0, 0, 17), INVALID),
+    ((0, 1, 0, 0, -1), INVALID), ((0, 1, 0, 0, 17), INVALID), ((0, 1, 0, 0, 0, -1), INVALID),
+    ((0, 1, 0, 0, 0, 3), INVALID),
 ])
 def test_forward_knobs_rejects_bad_knobs_on_host(knobs, status):
     s = lib.make_shape(256, 512, 8, 2, 16, "bf16")
