@@ -375,7 +375,11 @@ MOE_API moe_status moe_forward_noalloc(const moe_shape* shape, int32_t T, const 
  *              chunk and each block's place in it every chunk (item costs
  *              follow the expert-major order, so a fixed slice can leave one
  *              XCD the costlier places chunk after chunk); 2: the slice
- *              rotates every fourth chunk, the place every chunk.
+ *              rotates every fourth chunk, the place every chunk; 3: no
+ *              chunks -- XCD x takes the n-blocks [x NB/8, (x+1) NB/8) of
+ *              every m-tile (NB = the GEMM's n-blocks of 256 weight rows), so
+ *              every XCD gets the same mix of full and ragged m-tiles; used
+ *              where NB and the grid are multiples of 8, else mode 0.
  *              Performance knob (each item is computed the same way wherever
  *              it runs); ignored by the decode-shaped items. */
 typedef struct moe_knobs {
@@ -394,7 +398,7 @@ MOE_API void moe_default_knobs(moe_knobs* knobs);
  * workspace as moe_forward; with the default knobs the results are bitwise
  * those of moe_forward.  MOE_ERR_INVALID_ARG for a knob out of range (gemm
  * outside [0, 3], down_fp8 / fc2_reduce outside {0, 1}, band_rows outside
- * [0, 2^20], blocks_per_cu outside [0, 16], load_balance outside [0, 2]);
+ * [0, 2^20], blocks_per_cu outside [0, 16], load_balance outside [0, 3]);
  * MOE_ERR_UNSUPPORTED for fc2_reduce with top_k == 1, for
  * gemm = 1 with more than 16 (65535 - num_experts) routed rows (T top_k), and
  * for gemm = 3 where T hidden or T top_k inter reaches 2^30 (the prefill-shaped

@@ -362,7 +362,7 @@ void moe_default_knobs(moe_knobs* kn) {
 static bool knobs_valid(const moe_knobs& kn) {
   return kn.gemm >= 0 && kn.gemm <= 3 && (kn.down_fp8 | 1) == 1 && (kn.fc2_reduce | 1) == 1 && kn.band_rows >= 0 &&
          kn.band_rows <= (1 << 20) && kn.blocks_per_cu >= 0 && kn.blocks_per_cu <= 16 && kn.load_balance >= 0 &&
-         kn.load_balance <= 2;
+         kn.load_balance <= 3;
 }
 
 moe_status moe_forward_knobs(const moe_shape* s, int32_t T, const void* packed, const float* logits,

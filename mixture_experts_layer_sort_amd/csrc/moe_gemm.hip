@@ -194,10 +194,10 @@ hipError_t launch_gemm13(int dt, bool gated, int E, int H, int I, int k, int T, 
   a.gated = gated;
   a.limit = gated ? plan.limit : 0.f;
   a.band = plan.band;
-  a.balance = plan.balance;
   a.red = nullptr;
   a.wts = nullptr;
   a.E = E; a.K = H; a.G = L.G13; a.KG = L.KG13; a.k = k; a.n_out = I;
+  a.balance = prefill_balance(true, plan.balance, a.G, grid);
   if (plan.variant == 2) return launch_prefill(weight_dt(dt), true, a, grid, s);
   return dispatch_gemm<true>(weight_dt(dt), plan.variant + 1, a, grid, s);
 }
@@ -221,10 +221,10 @@ hipError_t launch_gemm2(int dt, bool gated, int E, int H, int I, int k, int T, c
   a.gated = gated;
   a.limit = 0.f;
   a.band = plan.band;
-  a.balance = plan.balance;
   a.red = plan.red;
   a.wts = plan.wts;
   a.E = E; a.K = I; a.G = L.G2; a.KG = L.KG2; a.k = k; a.n_out = H;
+  a.balance = prefill_balance(false, plan.balance, a.G, grid);
   if (plan.variant == 2 && plan.down_fp8 && has_fp8_gemm(dt)) {
     a.wcodes = packed + L.w2_frag;
     a.act = hq;  // e4m3 codes

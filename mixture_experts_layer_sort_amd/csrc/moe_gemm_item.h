@@ -599,5 +599,10 @@ hipError_t launch_prefill(int dt, bool g13, const GemmArgs& a, int grid, hipStre
 // MXFP8 layers: the prefill-shaped down GEMM on the fp8 matrix instruction (a.wcodes: fragment
 // region, a.act / a.act_scales: e4m3 codes / e8m0 scales of the hq rows); g13 must be false
 hipError_t launch_prefill_f8(bool g13, const GemmArgs& a, int grid, hipStream_t s);
+// The load-balance mode the prefill kernels run for moe_knobs.load_balance:
+// mode 3 (the n-block split, pf_split_item) is for the gate/up GEMM and needs
+// its n-block count (weight row groups G / 4) and the grid to be multiples of
+// 8 (the XCDs), else the default chunked deal (0).
+int prefill_balance(bool g13, int balance, int G, int grid);
 
 }  // namespace moe

@@ -27,10 +27,18 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmArgs a) {
   __shared__ int wsum[4];
   const auto st = pf_make_stages<DT, ROWS>();
   const int total_mt = build_schedule(a.offsets, a.E, ROWS, cum, wsum);
-  const long long total = (long long)total_mt * ((a.G + kPfGroups - 1) / kPfGroups);
-  for (long long n = 0; n * gridDim.x < total; ++n) {
-    const long long w = n * gridDim.x + pf_chunk_slot(n, a.balance);
-    if (w < total) prefill_item<DT, G13, 2, ROWS>(a, w, cum, st);
+  const int NB = (a.G + kPfGroups - 1) / kPfGroups;
+  const long long total = (long long)total_mt * NB;
+  if constexpr (G13) {
+    for (long long n = 0; n * gridDim.x < total; ++n) {
+      const long long w = pf_round_item(n, total, NB, a.balance);
+      if (w >= 0) prefill_item<DT, G13, 2, ROWS, true>(a, w, cum, st);
+    }
+  } else {
+    for (long long n = 0; n * gridDim.x < total; ++n) {
+      const long long w = n * gridDim.x + pf_chunk_slot(n, a.balance);
+      if (w < total) prefill_item<DT, G13, 2, ROWS>(a, w, cum, st);
+    }
   }
 }
 
@@ -69,6 +77,11 @@ int prefill_f8_blocks_per_cu(bool g13) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_f8_ptr(g13), kGemmThreads, 0) != hipSuccess || n < 1)
     n = 1;
   return n;
+}
+
+int prefill_balance(bool g13, int balance, int G, int grid) {
+  const int NB = (G + kPfGroups - 1) / kPfGroups;
+  return balance == 3 && (!g13 || NB % 8 != 0 || grid % 8 != 0) ? 0 : balance;
 }
 
 hipError_t launch_prefill_f8(bool g13, const GemmArgs& a, int grid, hipStream_t s) {

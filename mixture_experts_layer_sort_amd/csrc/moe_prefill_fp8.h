@@ -193,12 +193,8 @@ __device__ __forceinline__ int f8_item(const GemmArgs& a, long long w, const int
   const int NB = (a.G + kPfGroups - 1) / kPfGroups;
   const int KG = a.KG, KS = 2 * a.KG;
   const int e = find_expert(cum, a.E, (int)(w / NB));
-  const int mts = cum[e + 1] - cum[e];
-  const long long local = w - (long long)cum[e] * NB;
-  const int band = (int)(local / (kBand * NB)), full = mts / kBand;
-  const int bsize = band < full ? kBand : mts - full * kBand;
-  const int inner = (int)(local - (long long)band * kBand * NB);
-  const int nb = inner / bsize, mt = band * kBand + inner % bsize;
+  int mt, nb;
+  pf_tile<false>(w, NB, kBand, a.balance, cum, e, mt, nb);
   const int r0 = a.offsets[e] + mt * kF8Rows, r_end = a.offsets[e + 1];
   // this wave's row group; a group past the end (G not a multiple of 4) reads group G-1 and discards it
   const int g = kPfGroups * nb + wv, gl = min(g, a.G - 1);

@@ -100,7 +100,8 @@ __device__ __forceinline__ int xcd_logical_block() {
 // place b).  `balance` (moe_knobs.load_balance) picks the slice and place:
 // 0: slice x, place b / 8 every chunk (xcd_logical_block); 1: slice
 // (x + n) % 8, place (b / 8 + n) % C; 2: slice (x + n / 4) % 8, place
-// (b / 8 + n) % C.  Each is a permutation of the chunk's places.
+// (b / 8 + n) % C.  Each is a permutation of the chunk's places.  (Mode 3
+// does not use chunks: pf_split_item.)
 __device__ __forceinline__ int pf_chunk_slot(long long n, int balance) {
   const int b = blockIdx.x, g = gridDim.x;
   if (g % 8 != 0) return b;
@@ -108,6 +109,56 @@ __device__ __forceinline__ int pf_chunk_slot(long long n, int balance) {
   if (balance == 1) return ((x + r) % 8) * C + (j + r) % C;
   if (balance == 2) return ((x + r / 4) % 8) * C + (j + r) % C;
   return x * C + j;
+}
+
+// Load-balance mode 3, the n-block split: XCD x takes the n-blocks
+// [x NB/8, (x+1) NB/8) of every m-tile, so the eight XCDs get the same mix of
+// full and ragged m-tiles (with the chunked deal the XCDs' sums differ by
+// ~10 %, as each holds a fixed slice of every chunk).  Its blocks take the
+// XCD's items i = b / 8 + n gridDim.x / 8 in round n, numbered m-tile-major (the
+// NB / 8 n-blocks of one m-tile are neighbours, so they share its token
+// rows); item i is w = (i / (NB/8)) NB + x NB/8 + i % (NB/8), decoded
+// m-tile-major (pf_tile).  The host selects the mode only for the gate/up
+// GEMM and only when NB and gridDim.x are multiples of 8, which makes it a
+// permutation of the items.
+__device__ __forceinline__ long long pf_split_item(long long i, int NB) {
+  const int nx = NB / 8, x = (int)(blockIdx.x % 8);
+  return (i / nx) * NB + x * nx + (int)(i % nx);
+}
+
+// This block's item in round n (rounds 0 .. total / gridDim.x, rounded up),
+// or -1 for none: the chunked deal (pf_chunk_slot) or the n-block split.
+// The split is built into the gate/up kernels only: the down kernels keep
+// the plain chunked loop (their item bodies are at the edge of the register
+// budget, and the extra branch there cost spills).
+__device__ __forceinline__ long long pf_round_item(long long n, long long total, int NB, int balance) {
+  if (balance == 3) {
+    const long long i = blockIdx.x / 8 + n * (gridDim.x / 8);
+    return i < total / 8 ? pf_split_item(i, NB) : -1;
+  }
+  const long long w = n * gridDim.x + pf_chunk_slot(n, balance);
+  return w < total ? w : -1;
+}
+
+// m-tile (within expert e) and n-block of item w.  Modes 0-2 number the
+// items expert-major, in bands of up to kBand m-tiles, n-block-major inside
+// a band; mode 3 numbers them m-tile-major (w = global m-tile NB + n-block).
+template <bool SPLIT>
+__device__ __forceinline__ void pf_tile(long long w, int NB, int kBand, int balance, const int* cum, int e,
+                                        int& mt, int& nb) {
+  if (SPLIT && balance == 3) {
+    const int wi = (int)w;  // item counts stay far below 2^31
+    mt = wi / NB - cum[e];
+    nb = wi % NB;
+    return;
+  }
+  const int mts = cum[e + 1] - cum[e];
+  const long long local = w - (long long)cum[e] * NB;
+  const int band = (int)(local / (kBand * NB)), full = mts / kBand;
+  const int bsize = band < full ? kBand : mts - full * kBand;
+  const int inner = (int)(local - (long long)band * kBand * NB);
+  nb = inner / bsize;
+  mt = band * kBand + inner % bsize;
 }
 
 // Wait until at most N of this wave's vector-memory operations are
@@ -309,9 +360,10 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
   }
 }
 
-// One prefill work item.  `w` numbers items expert-major; within an expert,
-// bands of up to pf_band m-tiles, n-block-major inside a band, so that
-// consecutive items share weight and token tiles.  `cum` holds the
+// One prefill work item.  `w` numbers items expert-major (pf_tile: bands of
+// up to pf_band m-tiles, n-block-major inside a band, so that consecutive
+// items share weight and token tiles; m-tile-major in load-balance mode 3,
+// which only kernels instantiated with SPLIT run).  `cum` holds the
 // per-expert ROWS-row m-tile prefix from build_schedule.  Returns the item's
 // expert; ends with every load landed and the block's LDS free for reuse.
 //
@@ -322,7 +374,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, f32x16_t (&acc)[2
 // rows a wave's tile is 64 x 128 (128 accumulator registers) and two waves
 // fit per SIMD, so one wave's LDS reads, loads and converts overlap the
 // other's MFMAs; the 256-row tile halves the weight bytes loaded per flop.
-template <int DT, bool G13, int TW, int ROWS>
+template <int DT, bool G13, int TW, int ROWS, bool SPLIT = false>
 __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, const int* cum,
                                             const PfStages<pf_stage_slots<DT, ROWS>()>& st) {
   static_assert(TW == 1 || TW == 2, "waves along tokens");
@@ -342,13 +394,14 @@ __device__ __forceinline__ int prefill_item(const GemmArgs& a, long long w, cons
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wg = wv & 3, th = wv >> 2;
   const int NB = (a.G + kPfGroups - 1) / kPfGroups;
   const int KS = a.KG * 2;  // K steps of 64
+  // w is the same for the whole block; said explicitly, else the compiler
+  // takes the split deal's index for a per-lane value and builds the weight
+  // buffer resources below in vector registers (a waterfall loop around
+  // every load of the K loop).  Item counts stay far below 2^31.
+  if constexpr (SPLIT) w = __builtin_amdgcn_readfirstlane((int)w);
   const int e = find_expert(cum, a.E, (int)(w / NB));
-  const int mts = cum[e + 1] - cum[e];
-  const long long local = w - (long long)cum[e] * NB;
-  const int band = (int)(local / (kBand * NB)), full = mts / kBand;
-  const int bsize = band < full ? kBand : mts - full * kBand;
-  const int inner = (int)(local - (long long)band * kBand * NB);
-  const int nb = inner / bsize, mt = band * kBand + inner % bsize;
+  int mt, nb;
+  pf_tile<SPLIT>(w, NB, kBand, a.balance, cum, e, mt, nb);
   const int r0 = a.offsets[e] + mt * ROWS, r_end = a.offsets[e + 1];
   // this wave's row group; a group past the end (G not a multiple of 4) reads group G-1 and discards it
   const int g = kPfGroups * nb + wg, gl = min(g, a.G - 1);

@@ -39,7 +39,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DEFAULT_WORKLOADS = ("bf16_decode", "mxfp8_decode", "nvfp4_decode_t8", "nvfp4_decode_t128", "mxfp8_prefill")
 BANDS = (0, 256, 512, 2048, 4096, 8192)
 DECODE_BLOCKS = (0, 2, 4, 5, 6, 8)
-LOAD_BALANCE = (0, 1, 2)
+LOAD_BALANCE = (0, 1, 2, 3)
 MAX_T = 1 << 24
 # Settings within this factor of the fastest count as tied (above the spread of single sweep runs:
 # repeated runs of one setting differ by up to ~4 %); of the tied settings the one with the fewest

@@ -31,7 +31,7 @@ W = mi.WORKLOADS
 MAX_SAMPLE_EXPERTS = 16
 # knob settings (gemm, down_fp8, band_rows, fc2_reduce) checked at full size
 KNOB_CASES = {"mxfp8_prefill": [(3, 0, 0, 0), (0, 1, 0, 1), (0, 1, 256, 0), (0, 1, 4096, 0), (0, 1, 0, 0, 0, 1),
-                                (0, 1, 0, 0, 0, 2)],
+                                (0, 1, 0, 0, 0, 2), (0, 1, 0, 0, 0, 3)],
               "mxfp8_decode": [(3, 0, 512, 0), (2, 1, 0, 0), (0, 1, 0, 1)]}
 
 

@@ -28,6 +28,8 @@ W = mi.WORKLOADS
 CASES = {
     # prefill-shaped by default (T k >= 64 E): MXFP8 with the fp8 down GEMM
     "mxfp8_prefill": W["mxfp8_prefill"].scaled(T=300, H=512, I=256, E=4, k=2),
+    # 8 n-blocks in both GEMMs: the n-block split (load_balance 3) runs
+    "mxfp8_prefill_split": W["mxfp8_prefill"].scaled(T=300, H=2048, I=1024, E=4, k=2),
     "bf16_mxfp8_prefill": W["bf16_mxfp8_prefill"].scaled(T=520, H=256, I=384, E=8, k=2),
     "nvfp4_prefill_relu2": W["nvfp4_decode_t128"].scaled(T=200, H=384, I=256, E=4, k=2, act="relu2"),
     # decode-shaped by default
@@ -44,7 +46,8 @@ def _knob_grid(w):
         if fc2 and w.k < 2:
             continue
         # performance knobs: the band and the item deal (prefill-shaped items) and the persistent grid
-        perf = ([(0, 0, 0), (128, 0, 0), (4096, 0, 0), (0, 2, 0), (0, 0, 1), (0, 2, 2), (128, 0, 2)] if gemm == 3
+        perf = ([(0, 0, 0), (128, 0, 0), (4096, 0, 0), (0, 2, 0), (0, 0, 1), (0, 2, 2), (128, 0, 2), (0, 0, 3),
+                 (0, 2, 3)] if gemm == 3
                 else [(0, 0, 0), (0, 1, 0), (0, 5, 0), (0, 0, 1)])
         for band, blocks, balance in perf:
             out.append((gemm, d, band, fc2, blocks, balance))

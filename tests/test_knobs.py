@@ -84,7 +84,7 @@ def test_first_matching_line_wins_and_comments_are_ignored(tmp_path):
     "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 -1 0 0 0\n",      # negative band
     "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 2 0 0\n",    # fc2_reduce not 0/1
     "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 17 0\n",   # blocks_per_cu out of range
-    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0 3\n",    # load_balance out of range
+    "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0 4\n",    # load_balance out of range
     "mxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 99999999999 0 0 0\n",  # beyond 32 bits
     # a malformed line after a line of another shape is still an error
     "bf16 swiglu 64 128 8 2 1 10 : 0 1 0 0 0 0\nmxfp8 swiglu 7168 2048 256 8 4096 16384 : 3 1 2048 0 0\n",
@@ -113,7 +113,7 @@ def test_lookup_null_arguments():
     ((-1, 1, 0, 0), INVALID), ((4, 1, 0, 0), INVALID), ((0, 2, 0, 0), INVALID), ((0, -1, 0, 0), INVALID),
     ((0, 1, -1, 0), INVALID), ((0, 1, (1 << 20) + 1, 0), INVALID), ((0, 1, 0, 2), INVALID),
     ((0, 1, 0, 0, -1), INVALID), ((0, 1, 0, 0, 17), INVALID), ((0, 1, 0, 0, 0, -1), INVALID),
-    ((0, 1, 0, 0, 0, 3), INVALID),
+    ((0, 1, 0, 0, 0, 4), INVALID),
 ])
 def test_forward_knobs_rejects_bad_knobs_on_host(knobs, status):
     s = lib.make_shape(256, 512, 8, 2, 16, "bf16")
