@@ -112,6 +112,16 @@ __device__ __forceinline__ int fused_f8_down_item(const GemmArgs& g, long long w
 template <int V>
 constexpr int fused_max_waves() { return V == 3 ? 1 : 8; }
 
+
+// The single-launch kernel's permutation (one block, LDS from the kernel's
+// dynamic shared memory) stays a called function: inlined, it pushes the
+// MXFP8 prefill instance of that kernel further into scratch memory.
+__device__ __noinline__ void fused_permute(const int* ids, int P, int E, int* offsets, int* sorted_pairs,
+                                           int* pair_pos, int* lds) {
+  permute_block<kGemmThreads / 64>(ids, P, E, offsets, sorted_pairs, pair_pos, reinterpret_cast<int(*)[1024]>(lds),
+                                   lds + (kGemmThreads / 64) * 1024);
+}
+
 template <int DT, int V>
 __global__ __launch_bounds__(kGemmThreads)
 void fused_kernel(FusedArgs a) {
@@ -132,11 +142,8 @@ void fused_kernel(FusedArgs a) {
   grid_barrier(a.sync, G);
 
   // 2. permutation
-  if (blockIdx.x == 0) {
-    int* lds = reinterpret_cast<int*>(smem);
-    permute_block<kGemmThreads / 64>(a.ids, a.T * a.k, a.E, a.offsets, a.sorted_pairs, a.pair_pos,
-                                     reinterpret_cast<int(*)[1024]>(lds), lds + (kGemmThreads / 64) * 1024);
-  }
+  if (blockIdx.x == 0)
+    fused_permute(a.ids, a.T * a.k, a.E, a.offsets, a.sorted_pairs, a.pair_pos, reinterpret_cast<int*>(smem));
   grid_barrier(a.sync, 2 * G);
 
   // 3. the two grouped GEMMs

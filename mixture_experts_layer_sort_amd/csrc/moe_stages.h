@@ -73,10 +73,16 @@ __device__ __forceinline__ void route_token_n(const float* __restrict__ logits, 
                                               int* __restrict__ ids, float* __restrict__ wts, int lane) {
   const float* row = logits + (size_t)t * E;
   uint64_t key[NV];
+  // every load in bounds and unconditional (slots past E read logit E - 1
+  // and get the lowest key), so the NV loads are in flight together rather
+  // than one after another behind per-slot branches
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
-    key[i] = e < E ? route_key(row[e], e) : 0ull;
+    key[i] = e < E ? route_key(v[i], e) : 0ull;
   }
   // this lane's keys in descending order (Batcher's odd-even merge sort network)
 #pragma unroll
@@ -130,7 +136,7 @@ template <int NWAVES>
 constexpr int permute_lds_ints() { return NWAVES * 1024 + 64 * NWAVES; }
 
 template <int NWAVES>
-__device__ void permute_block(const int* __restrict__ ids, int P, int E, int* __restrict__ offsets,
+__device__ __forceinline__ void permute_block(const int* __restrict__ ids, int P, int E, int* __restrict__ offsets,
                               int* __restrict__ sorted_pairs, int* __restrict__ pair_pos, int (*hist)[1024],
                               int* scan_tmp) {
   constexpr int kPermWaves = NWAVES, kPermThreads = 64 * NWAVES, kPer = 1024 / kPermThreads;
@@ -222,7 +228,7 @@ __device__ void permute_block(const int* __restrict__ ids, int P, int E, int* __
 
 // The same with its own static LDS.
 template <int NWAVES>
-__device__ void permute_block(const int* __restrict__ ids, int P, int E, int* __restrict__ offsets,
+__device__ __forceinline__ void permute_block(const int* __restrict__ ids, int P, int E, int* __restrict__ offsets,
                               int* __restrict__ sorted_pairs, int* __restrict__ pair_pos) {
   __shared__ int hist[NWAVES][1024];
   __shared__ int scan_tmp[64 * NWAVES];
@@ -290,14 +296,28 @@ __device__ __forceinline__ void combine_range(const uint16_t* __restrict__ y, co
     const long long e0 = i * 8;
     const int t = (int)(e0 / H), h = (int)(e0 % H);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const float wj = wts[(size_t)t * k + j];
-      const uint4 v = *reinterpret_cast<const uint4*>(y + ((size_t)t * k + j) * H + h);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    // slots in batches of 8: all loads of a batch are issued before the
+    // first use, so a token's k rows cost one memory latency per batch
+    // instead of one per slot; the sum keeps slot order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      float wj[8];
+      uint4 v[8];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        acc[2 * m] += wj * bf16_to_f32(u[m] & 0xFFFF);
-        acc[2 * m + 1] += wj * bf16_to_f32(u[m] >> 16);
+      for (int j = 0; j < 8; ++j) {
+        const int jj = min(j0 + j, k - 1);  // slots past k reload the last one, unused
+        wj[j] = wts[(size_t)t * k + jj];
+        v[j] = *reinterpret_cast<const uint4*>(y + ((size_t)t * k + jj) * H + h);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j0 + j < k) {
+          const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            acc[2 * m] += wj[j] * bf16_to_f32(u[m] & 0xFFFF);
+            acc[2 * m + 1] += wj[j] * bf16_to_f32(u[m] >> 16);
+          }
+        }
       }
     }
     uint4 o;
