@@ -97,10 +97,16 @@ __device__ __forceinline__ void route_token_n(const float* __restrict__ logits, 
   uint64_t mine = 0;
   for (int j = 0; j < k; ++j) {
     const uint64_t w = wave_max_u64(key[0]);  // uniform: pick j
-    const bool win = key[0] == w;              // the one lane that held it drops it
+    // the one lane that held it drops it: its keys move up one place.  The
+    // move is written as masked bit operations on a mask the compiler cannot
+    // see through; as selects it became a gather of every key from every
+    // place (NV^2 selects per round).
+    uint32_t m = key[0] == w ? 0xFFFFFFFFu : 0u;
+    asm volatile("" : "+v"(m));
+    const uint64_t m64 = ((uint64_t)m << 32) | m;
 #pragma unroll
-    for (int i = 0; i + 1 < NV; ++i) key[i] = win ? key[i + 1] : key[i];
-    key[NV - 1] = win ? 0ull : key[NV - 1];
+    for (int i = 0; i + 1 < NV; ++i) key[i] ^= (key[i] ^ key[i + 1]) & m64;
+    key[NV - 1] &= ~m64;
     mine = lane == j ? w : mine;
   }
   // slot `lane` < k: softmax over the picks, the denominator summed in pick order
