@@ -154,8 +154,17 @@ __device__ __forceinline__ void permute_block(const int* __restrict__ ids, int P
   // ids outside [0, E) are clamped: results are then unspecified but every access stays in bounds.
   // Loads go kAhead chunks of 64 at a time, so the wave waits for memory once per group, not per chunk.
   // (Loads past the segment read a clamped in-bounds address and are discarded, so they need no branch.)
+  // The first group's ids stay in registers for the ranking pass below (a
+  // segment of up to 64 kAhead pairs -- every decode batch -- is then read
+  // from memory once).
   constexpr int kAhead = 16;
-  for (int p = seg0 + lane; p < seg1; p += 64 * kAhead) {
+  int first[kAhead];
+#pragma unroll
+  for (int u = 0; u < kAhead; ++u) first[u] = ids[min(seg0 + lane + 64 * u, P - 1)];
+#pragma unroll
+  for (int u = 0; u < kAhead; ++u)
+    if (seg0 + lane + 64 * u < seg1) atomicAdd(&hist[w][min(max(first[u], 0), E - 1)], 1);
+  for (int p = seg0 + lane + 64 * kAhead; p < seg1; p += 64 * kAhead) {
     int v[kAhead];
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) v[u] = ids[min(p + 64 * u, P - 1)];
@@ -173,15 +182,18 @@ __device__ __forceinline__ void permute_block(const int* __restrict__ ids, int P
       for (int ww = 0; ww < kPermWaves; ++ww) tot[j] += hist[ww][e];
     local += tot[j];
   }
-  scan_tmp[tid] = local;
-  __syncthreads();
-  for (int d = 1; d < kPermThreads; d <<= 1) {  // Hillis-Steele inclusive scan
-    int add = tid >= d ? scan_tmp[tid - d] : 0;
-    __syncthreads();
-    scan_tmp[tid] += add;
-    __syncthreads();
+  // block exclusive scan of `local`: inclusive scans inside the waves, then
+  // the waves' totals
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
   }
-  int base = scan_tmp[tid] - local;
+  if (lane == 63) scan_tmp[w] = incl;
+  __syncthreads();
+  int base = incl - local;
+  for (int ww = 0; ww < w; ++ww) base += scan_tmp[ww];
   for (int j = 0; j < kPer; ++j) {
     int e = e0 + j;
     if (e < E) {
@@ -204,10 +216,8 @@ __device__ __forceinline__ void permute_block(const int* __restrict__ ids, int P
   // (The wave's LDS operations complete in order, so each chunk sees the
   // previous chunk's hist update without a fence.)
   int ring[kAhead];
-  if (seg0 < seg1) {
 #pragma unroll
-    for (int u = 0; u < kAhead; ++u) ring[u] = ids[min(seg0 + 64 * u + lane, P - 1)];
-  }
+  for (int u = 0; u < kAhead; ++u) ring[u] = first[u];
   for (int p0 = seg0; p0 < seg1; p0 += 64 * kAhead) {
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
