@@ -84,7 +84,9 @@ __device__ __forceinline__ void route_token_n(const float* __restrict__ logits, 
     const int e = lane + 64 * i;
     key[i] = e < E ? route_key(v[i], e) : 0ull;
   }
-  // this lane's keys in descending order (Batcher's odd-even merge sort network)
+  // this lane's keys in descending order (Batcher's odd-even merge sort
+  // network for the next power of two, less the comparators that touch a
+  // place >= NV: those places would hold the lowest keys, already last)
 #pragma unroll
   for (int p = 1; p < NV; p <<= 1)
 #pragma unroll
@@ -120,14 +122,18 @@ __device__ __forceinline__ void route_token_n(const float* __restrict__ logits, 
   }
 }
 
-// One token's routing with NV = ceil(E / 64) rounded up to a power of two
-// logits per lane (E <= 1024), so small expert counts skip empty slots.
+// One token's routing with NV = ceil(E / 64) logits per lane (E <= 1024),
+// rounded up to one of 1, 2, 4, 6, 8, 12, 16, so small expert counts skip
+// empty slots (the sorting network and the key moves grow with NV; the
+// 384-expert layers take 6).
 __device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
                                             int* __restrict__ ids, float* __restrict__ wts, int lane) {
   if (E <= 64) route_token_n<1>(logits, t, E, k, ids, wts, lane);
   else if (E <= 128) route_token_n<2>(logits, t, E, k, ids, wts, lane);
   else if (E <= 256) route_token_n<4>(logits, t, E, k, ids, wts, lane);
+  else if (E <= 384) route_token_n<6>(logits, t, E, k, ids, wts, lane);
   else if (E <= 512) route_token_n<8>(logits, t, E, k, ids, wts, lane);
+  else if (E <= 768) route_token_n<12>(logits, t, E, k, ids, wts, lane);
   else route_token_n<16>(logits, t, E, k, ids, wts, lane);
 }
 

@@ -223,7 +223,9 @@ def test_forward_routing_matches_staged(dtype, E, k):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (7, 8, 2), (64, 64, 6), (33, 256, 8), (5, 384, 8), (3, 1024, 32),
-                                   (200, 1000, 9), (4, 32, 32)])
+                                   (200, 1000, 9), (4, 32, 32),
+                                   # around the per-lane key counts (6, 12, 16 keys per lane)
+                                   (9, 257, 8), (9, 320, 8), (6, 700, 8), (4, 768, 16), (4, 769, 8)])
 def test_route_parity(T, E, k):
     rng = np.random.default_rng(T * 7 + E)
     l = (rng.standard_normal((T, E)) * 2).astype(np.float32)
