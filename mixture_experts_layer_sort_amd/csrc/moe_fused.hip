@@ -113,9 +113,16 @@ template <int V>
 constexpr int fused_max_waves() { return V == 3 ? 1 : 8; }
 
 
-// The single-launch kernel's permutation (one block, LDS from the kernel's
-// dynamic shared memory) stays a called function: inlined, it pushes the
-// MXFP8 prefill instance of that kernel further into scratch memory.
+// The single-launch kernel's x quantisation and permutation (one block, LDS
+// from the kernel's dynamic shared memory) stay called functions: inlined,
+// they push the MXFP8 prefill instance of that kernel further into scratch
+// memory.
+template <int DT>
+__device__ __noinline__ void fused_quantize_x(const uint16_t* x, long long n_elem, uint8_t* codes, uint8_t* scales,
+                                              uint16_t* deq, long long gtid, long long gstride) {
+  quantize_x_blocks<DT>(x, n_elem, codes, scales, deq, gtid, gstride);
+}
+
 __device__ __noinline__ void fused_permute(const int* ids, int P, int E, int* offsets, int* sorted_pairs,
                                            int* pair_pos, int* lds) {
   permute_block<kGemmThreads / 64>(ids, P, E, offsets, sorted_pairs, pair_pos, reinterpret_cast<int(*)[1024]>(lds),
@@ -138,7 +145,7 @@ void fused_kernel(FusedArgs a) {
 
   // 1. routing (one wave per token) and x quantisation
   for (int t = (int)(gtid >> 6); t < a.T; t += (int)(gstride >> 6)) route_token(a.logits, t, a.E, a.k, a.ids, a.wts, lane);
-  if (a.quant_x) quantize_x_blocks<DT>(a.x, (long long)a.T * a.H, a.xq, a.xq_scales, a.xq_deq, gtid, gstride);
+  if (a.quant_x) fused_quantize_x<DT>(a.x, (long long)a.T * a.H, a.xq, a.xq_scales, a.xq_deq, gtid, gstride);
   grid_barrier(a.sync, G);
 
   // 2. permutation

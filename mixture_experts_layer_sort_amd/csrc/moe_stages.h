@@ -258,7 +258,8 @@ __device__ __forceinline__ void permute_block(const int* __restrict__ ids, int P
 }
 
 template <int DT>
-__device__ void quantize_x_blocks(const uint16_t* __restrict__ x, long long n_elem, uint8_t* __restrict__ codes,
+__device__ __forceinline__ void quantize_x_blocks(const uint16_t* __restrict__ x, long long n_elem,
+                                                  uint8_t* __restrict__ codes,
                                   uint8_t* __restrict__ scales, uint16_t* __restrict__ deq, long long gtid,
                                   long long gstride) {
   if constexpr (DT == DT_BF16) {
@@ -269,10 +270,23 @@ __device__ void quantize_x_blocks(const uint16_t* __restrict__ x, long long n_el
   } else {
     // MXFP8: 8 lanes x 4 elements per block of 32; NVFP4: 4 lanes x 4 per 16
     constexpr int LPB = DT == DT_MXFP8 ? 8 : 4;
+    // U grid-stride steps per pass, their loads issued together (at clamped
+    // in-bounds addresses, no branch): 8 bytes per lane per step are too
+    // few bytes in flight to stream x at the memory's rate
+    constexpr int U = 4;
     const long long nthreads = n_elem / 4;
-    for (long long i = gtid; i < ((nthreads + 63) / 64) * 64; i += gstride) {
+    const long long lim = ((nthreads + 63) / 64) * 64;  // whole waves: the group maximum needs every lane
+    for (long long i0 = gtid; i0 < lim; i0 += U * gstride) {
+      uint2 rawu[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        rawu[u] = reinterpret_cast<const uint2*>(x)[min(i0 + u * gstride, nthreads - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+      const long long i = i0 + u * gstride;
+      if (i >= lim) break;  // the same for the whole wave (gtid and gstride keep waves 64-aligned)
       const bool ok = i < nthreads;
-      uint2 raw = ok ? reinterpret_cast<const uint2*>(x)[i] : make_uint2(0, 0);
+      const uint2 raw = ok ? rawu[u] : make_uint2(0, 0);
       float v[4] = {bf16_to_f32(raw.x & 0xFFFF), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xFFFF),
                     bf16_to_f32(raw.y >> 16)};
       float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
@@ -303,6 +317,7 @@ __device__ void quantize_x_blocks(const uint16_t* __restrict__ x, long long n_el
           if (sub == 0) scales[blk] = (uint8_t)sc_code;
           reinterpret_cast<uint2*>(deq)[i] = make_uint2(d[0] | (d[1] << 16), d[2] | (d[3] << 16));
         }
+      }
       }
     }
   }
