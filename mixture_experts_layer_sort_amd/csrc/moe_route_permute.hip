@@ -15,9 +15,14 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   if (t < T) route_token(logits, t, E, k, ids, wts, threadIdx.x & 63);
 }
 
-// Block 0: the stable counting sort (permute_block); blocks 1..: in-kernel
-// quantisation of the bf16 hidden states.
+// Blocks 0 .. nsort-1: the stable counting sort (one block: permute_block;
+// several, for large P: permute_chunk over chunks of `chunk` pairs); the
+// other blocks: in-kernel quantisation of the bf16 hidden states.
 constexpr int kPermThreads = 512;
+// Pairs up to which one block sorts (a decode batch); above it the sort is
+// split into chunks of at least kPermChunkMin pairs over at most
+// kPermMaxSortBlocks blocks, each of which counts all P ids once.
+constexpr int kPermOneBlockMax = 16384, kPermChunkMin = 4096, kPermMaxSortBlocks = 32;
 
 template <int DT>
 __global__ __launch_bounds__(kPermThreads) void permute_quant_kernel(const int* __restrict__ ids, int P, int E,
@@ -27,14 +32,23 @@ __global__ __launch_bounds__(kPermThreads) void permute_quant_kernel(const int* 
                                                                      const uint16_t* __restrict__ x, long long n_elem,
                                                                      uint8_t* __restrict__ xq_codes,
                                                                      uint8_t* __restrict__ xq_scales,
-                                                                     uint16_t* __restrict__ xq_deq, int do_quant) {
-  if (blockIdx.x == 0) {
-    permute_block<kPermThreads / 64>(ids, P, E, offsets, sorted_pairs, pair_pos);
+                                                                     uint16_t* __restrict__ xq_deq, int do_quant,
+                                                                     int nsort, int chunk) {
+  extern __shared__ int perm_lds[];  // sized by the launch for the sort blocks' path
+  constexpr int NW = kPermThreads / 64;
+  if ((int)blockIdx.x < nsort) {
+    if (nsort == 1) {
+      permute_block<NW>(ids, P, E, offsets, sorted_pairs, pair_pos, reinterpret_cast<int(*)[1024]>(perm_lds),
+                        perm_lds + NW * 1024);
+    } else {
+      const int c0 = min(P, (int)blockIdx.x * chunk);
+      permute_chunk<NW>(ids, P, E, c0, min(P, c0 + chunk), offsets, sorted_pairs, pair_pos, perm_lds);
+    }
     return;
   }
   if (!do_quant) return;
-  const long long gtid = (long long)(blockIdx.x - 1) * kPermThreads + threadIdx.x;
-  const long long gstride = (long long)(gridDim.x - 1) * kPermThreads;
+  const long long gtid = (long long)(blockIdx.x - nsort) * kPermThreads + threadIdx.x;
+  const long long gstride = (long long)(gridDim.x - nsort) * kPermThreads;
   quantize_x_blocks<DT>(x, n_elem, xq_codes, xq_scales, xq_deq, gtid, gstride);
 }
 
@@ -254,18 +268,32 @@ hipError_t launch_permute(int dt, const int* ids, int T, int k, int E, int H, in
   uint16_t* xq_deq = reinterpret_cast<uint16_t*>(xq + act_dequant_offset(dt, T, H));
   long long work = dt == DT_BF16 ? n_elem / 8 : n_elem / 4;
   int qblocks = do_quant ? (int)min((work + kPermThreads - 1) / kPermThreads, (long long)4096) : 0;
+  // sort blocks: one up to kPermOneBlockMax pairs, else chunks (multiples of
+  // 64 waves' steps) over at most kPermMaxSortBlocks blocks, none empty
+  int nsort = 1, chunk = P;
+  if (P > kPermOneBlockMax) {
+    const int per = kPermThreads;  // chunk granularity: one 64-pair step per wave
+    const int want = (int)min((long long)kPermMaxSortBlocks, ((long long)P + kPermChunkMin - 1) / kPermChunkMin);
+    chunk = (int)((((long long)P + want - 1) / want + per - 1) / per * per);
+    nsort = (P + chunk - 1) / chunk;
+  }
+  const size_t lds = sizeof(int) * (nsort == 1 ? permute_lds_ints<kPermThreads / 64>()
+                                               : permute_chunk_lds_ints<kPermThreads / 64>(E));
   switch (dt) {
     case DT_BF16:
-      hipLaunchKernelGGL(permute_quant_kernel<DT_BF16>, dim3(1 + qblocks), dim3(kPermThreads), 0, s, ids, P, E,
-                         offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, xq_deq, do_quant);
+      hipLaunchKernelGGL(permute_quant_kernel<DT_BF16>, dim3(nsort + qblocks), dim3(kPermThreads), lds, s, ids, P,
+                         E, offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, xq_deq, do_quant, nsort,
+                         chunk);
       break;
     case DT_MXFP8:
-      hipLaunchKernelGGL(permute_quant_kernel<DT_MXFP8>, dim3(1 + qblocks), dim3(kPermThreads), 0, s, ids, P, E,
-                         offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, xq_deq, do_quant);
+      hipLaunchKernelGGL(permute_quant_kernel<DT_MXFP8>, dim3(nsort + qblocks), dim3(kPermThreads), lds, s, ids, P,
+                         E, offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, xq_deq, do_quant, nsort,
+                         chunk);
       break;
     default:
-      hipLaunchKernelGGL(permute_quant_kernel<DT_NVFP4>, dim3(1 + qblocks), dim3(kPermThreads), 0, s, ids, P, E,
-                         offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, xq_deq, do_quant);
+      hipLaunchKernelGGL(permute_quant_kernel<DT_NVFP4>, dim3(nsort + qblocks), dim3(kPermThreads), lds, s, ids, P,
+                         E, offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, xq_deq, do_quant, nsort,
+                         chunk);
       break;
   }
   return hipGetLastError();

@@ -248,6 +248,129 @@ __device__ __forceinline__ void permute_block(const int* __restrict__ ids, int P
   }
 }
 
+// Lanes of a 64-pair step (valid ones) that hold the same expert id as this
+// lane: one ballot per id bit.
+__device__ __forceinline__ unsigned long long same_expert_lanes(int id, bool valid, int nbits) {
+  unsigned long long m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (id >> b) & 1;
+    const unsigned long long bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+// The same sort split over several blocks, for large P.  Block c sorts the
+// pairs of chunk [c0, c1): it counts the experts of all P pairs (each block
+// redundantly: P ids from L2 against one block's serial ranking of all P),
+// of the pairs before c0 and, per wave sub-segment, of its chunk; the
+// exclusive scan of the totals gives offsets (written by the block with
+// c0 == 0), offsets + the before-counts give the chunk's first position of
+// each expert, and its waves rank their sub-segments as permute_block does.
+// The result is the unique stable order, the same as permute_block's.
+// c0 and the chunk length are multiples of 64 NWAVES except the last
+// chunk's end (c1 == P).  LDS (ints): all[E], before[E], sub[NWAVES][E],
+// scan_tmp[64 NWAVES].
+template <int NWAVES>
+__host__ __device__ constexpr int permute_chunk_lds_ints(int E) { return (2 + NWAVES) * E + 64 * NWAVES; }
+
+template <int NWAVES>
+__device__ __forceinline__ void permute_chunk(const int* __restrict__ ids, int P, int E, int c0, int c1,
+                                              int* __restrict__ offsets, int* __restrict__ sorted_pairs,
+                                              int* __restrict__ pair_pos, int* lds) {
+  constexpr int kThreads = 64 * NWAVES, kAhead = 16;
+  int* all = lds;
+  int* before = lds + E;
+  int* sub = lds + 2 * E;  // [NWAVES][E]
+  int* scan_tmp = lds + (2 + NWAVES) * E;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < (2 + NWAVES) * E; i += kThreads) lds[i] = 0;
+  __syncthreads();
+  // 1. counts: wave w takes 64-aligned segment w of all P pairs, one LDS add
+  //    per pair (a 64-pair step lies wholly before, inside or after the
+  //    chunk, and inside one wave sub-segment of it)
+  const int S = ((P + NWAVES * 64 - 1) / (NWAVES * 64)) * 64;
+  const int SS = ((c1 - c0 + NWAVES * 64 - 1) / (NWAVES * 64)) * 64;  // chunk sub-segment per wave
+  const int seg0 = min(P, w * S), seg1 = min(P, (w + 1) * S);
+  for (int p0 = seg0; p0 < seg1; p0 += 64 * kAhead) {
+    int v[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) v[u] = ids[min(p0 + 64 * u + lane, P - 1)];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int q0 = p0 + 64 * u;  // the step's first pair (wave-uniform)
+      if (q0 >= seg1) break;
+      if (q0 + lane < seg1) {
+        const int id = min(max(v[u], 0), E - 1);
+        atomicAdd(&all[id], 1);
+        if (q0 < c0) atomicAdd(&before[id], 1);
+        else if (q0 < c1) atomicAdd(&sub[((q0 - c0) / SS) * E + id], 1);
+      }
+    }
+  }
+  __syncthreads();
+  // 2. offsets (exclusive scan of the totals over experts, kPer experts per
+  //    thread), then the first position of each expert in each wave's
+  //    sub-segment of the chunk
+  constexpr int kPer = 1024 / kThreads;
+  const int e0 = kPer * tid;
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) local += e0 + j < E ? all[e0 + j] : 0;
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) scan_tmp[w] = incl;
+  __syncthreads();
+  int off = incl - local;
+  for (int ww = 0; ww < w; ++ww) off += scan_tmp[ww];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = e0 + j;
+    if (e < E) {
+      if (c0 == 0) offsets[e] = off;
+      int b = off + before[e];
+      for (int ww = 0; ww < NWAVES; ++ww) {
+        const int c = sub[ww * E + e];
+        sub[ww * E + e] = b;
+        b += c;
+      }
+      off += all[e];
+    }
+  }
+  if (c0 == 0 && tid == 0) offsets[E] = P;
+  __syncthreads();
+  // 3. each wave ranks its sub-segment of the chunk in order (ballots on the
+  //    id bits give each pair's place among the step's pairs of its expert)
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int* mine = sub + w * E;
+  const int r0 = min(c1, c0 + w * SS), r1 = min(c1, c0 + (w + 1) * SS);
+  for (int p0 = r0; p0 < r1; p0 += 64 * kAhead) {
+    int v[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) v[u] = ids[min(p0 + 64 * u + lane, P - 1)];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      if (p0 + 64 * u >= r1) break;  // wave-uniform
+      const int p = p0 + 64 * u + lane;
+      const bool valid = p < r1;
+      const int id = valid ? min(max(v[u], 0), E - 1) : 0;
+      const unsigned long long m = same_expert_lanes(id, valid, nbits);
+      if (valid) {
+        const int pos = mine[id] + __popcll(m & lt);
+        sorted_pairs[pos] = p;
+        pair_pos[p] = pos;
+        if (lane == 63 - __clzll(m)) mine[id] += __popcll(m);
+      }
+    }
+  }
+}
+
 // The same with its own static LDS.
 template <int NWAVES>
 __device__ __forceinline__ void permute_block(const int* __restrict__ ids, int P, int E, int* __restrict__ offsets,
