@@ -331,8 +331,12 @@ static moe_status forward_staged(const moe_shape* s, int32_t T, int cap, const v
   p.wts = acc ? wts : nullptr;
   // the fp8 down GEMM reads the hq codes: the gate/up GEMM skips hq's 16-bit copy
   p.skip_hq_deq = p.variant == 2 && p.down_fp8 && has_fp8_gemm(dt);
-  hipError_t e = launch_route(logits, T, E, k, ids, wts, stream);
-  if (e == hipSuccess)
+  // a handful of tokens: routing and the sort in one launch
+  hipError_t e = T <= route_permute_max_tokens()
+                     ? launch_route_permute(dt, logits, T, k, E, H, ids, wts, offsets, sorted_pairs, pair_pos, x,
+                                            xq, stream)
+                     : launch_route(logits, T, E, k, ids, wts, stream);
+  if (e == hipSuccess && T > route_permute_max_tokens())
     e = launch_permute(dt, ids, T, k, E, H, offsets, sorted_pairs, pair_pos, x, xq, stream);
   if (e == hipSuccess)
     e = launch_gemm13(dt, gated(s), E, H, I, k, T, (const uint8_t*)packed, offsets, sorted_pairs, xq, hq,

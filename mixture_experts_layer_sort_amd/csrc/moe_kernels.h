@@ -15,6 +15,13 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, floa
 hipError_t launch_permute(int dt, const int* ids, int T, int k, int E, int H, int* offsets, int* sorted_pairs,
                           int* pair_pos, const uint16_t* x, uint8_t* xq, hipStream_t s);
 
+// Routing and permutation (+ x quantisation) in one launch, for T up to
+// route_permute_max_tokens(): the results of launch_route + launch_permute.
+int route_permute_max_tokens();
+hipError_t launch_route_permute(int dt, const float* logits, int T, int k, int E, int H, int* ids, float* wts,
+                                int* offsets, int* sorted_pairs, int* pair_pos, const uint16_t* x, uint8_t* xq,
+                                hipStream_t s);
+
 // Batched activation format: offsets and rows of the valid rows of x [E, M, H]
 // (counts clamped to [0, M]), and x quantised into xq (all E M rows; BF16
 // activations are used in place and xq is ignored).

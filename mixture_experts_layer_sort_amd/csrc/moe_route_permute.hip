@@ -52,6 +52,33 @@ __global__ __launch_bounds__(kPermThreads) void permute_quant_kernel(const int* 
   quantize_x_blocks<DT>(x, n_elem, xq_codes, xq_scales, xq_deq, gtid, gstride);
 }
 
+// Small batches (T <= the sorting block's waves): block 0 routes the tokens
+// (one wave each) and then sorts the pairs it wrote, so a decode step needs
+// one launch for routing and permutation instead of two; the other blocks
+// quantise x as in permute_quant_kernel.  Same routing and sort code, so the
+// same bits as moe_route followed by moe_permute.
+template <int DT>
+__global__ __launch_bounds__(kPermThreads) void route_permute_quant_kernel(
+    const float* __restrict__ logits, int T, int k, int E, int* ids, float* __restrict__ wts,
+    int* __restrict__ offsets, int* __restrict__ sorted_pairs, int* __restrict__ pair_pos,
+    const uint16_t* __restrict__ x, long long n_elem, uint8_t* __restrict__ xq_codes,
+    uint8_t* __restrict__ xq_scales, uint16_t* __restrict__ xq_deq, int do_quant) {
+  extern __shared__ int perm_lds[];
+  constexpr int NW = kPermThreads / 64;
+  if (blockIdx.x == 0) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int t = w; t < T; t += NW) route_token(logits, t, E, k, ids, wts, lane);
+    __syncthreads();  // the block's id stores before its sort reads them
+    permute_block<NW>(ids, T * k, E, offsets, sorted_pairs, pair_pos, reinterpret_cast<int(*)[1024]>(perm_lds),
+                      perm_lds + NW * 1024);
+    return;
+  }
+  if (!do_quant) return;
+  const long long gtid = (long long)(blockIdx.x - 1) * kPermThreads + threadIdx.x;
+  const long long gstride = (long long)(gridDim.x - 1) * kPermThreads;
+  quantize_x_blocks<DT>(x, n_elem, xq_codes, xq_scales, xq_deq, gtid, gstride);
+}
+
 // ------------------------------------------------------------------ batched activation format
 // Tokens arrive bucketed per expert, x [E, M, H] with counts[e] valid rows
 // (clamped to [0, M]).  The grouped GEMMs then run with one "pair" per valid
@@ -255,6 +282,30 @@ hipError_t launch_fold_global_scale(int count, long long scales_per_matrix, cons
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* wts, hipStream_t s) {
   hipLaunchKernelGGL(route_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, wts);
+  return hipGetLastError();
+}
+
+int route_permute_max_tokens() { return kPermThreads / 64; }
+
+hipError_t launch_route_permute(int dt, const float* logits, int T, int k, int E, int H, int* ids, float* wts,
+                                int* offsets, int* sorted_pairs, int* pair_pos, const uint16_t* x, uint8_t* xq,
+                                hipStream_t s) {
+  if (T > route_permute_max_tokens()) return hipErrorInvalidValue;
+  dt = act_dt(dt);
+  const long long n_elem = (long long)T * H;
+  const int do_quant = !(dt == DT_BF16 && (const void*)xq == (const void*)x);
+  uint8_t* xq_scales = xq + act_scale_offset(dt, T, H);
+  uint16_t* xq_deq = reinterpret_cast<uint16_t*>(xq + act_dequant_offset(dt, T, H));
+  const long long work = dt == DT_BF16 ? n_elem / 8 : n_elem / 4;
+  const int qblocks = do_quant ? (int)min((work + kPermThreads - 1) / kPermThreads, (long long)4096) : 0;
+  const size_t lds = sizeof(int) * permute_lds_ints<kPermThreads / 64>();
+#define MOE_RP(D)                                                                                              \
+  hipLaunchKernelGGL(route_permute_quant_kernel<D>, dim3(1 + qblocks), dim3(kPermThreads), lds, s, logits, T, k, \
+                     E, ids, wts, offsets, sorted_pairs, pair_pos, x, n_elem, xq, xq_scales, xq_deq, do_quant)
+  if (dt == DT_BF16) MOE_RP(DT_BF16);
+  else if (dt == DT_MXFP8) MOE_RP(DT_MXFP8);
+  else MOE_RP(DT_NVFP4);
+#undef MOE_RP
   return hipGetLastError();
 }
 
