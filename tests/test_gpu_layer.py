@@ -248,7 +248,7 @@ def test_route_parity(T, E, k):
                                         (3000, 1024, 4, "uniform"), (513, 7, 7, "uniform"),
                                         # just past the one-block sort (16384 pairs): chunks of the
                                         # multi-block sort with a short last chunk
-                                        (2048, 7, 8, "uniform"), (2049, 7, 8, "uniform"), (4097, 300, 4, "zipf"),
+                                        (2048, 8, 8, "uniform"), (2049, 8, 8, "uniform"), (4097, 300, 4, "zipf"),
                                         (2100, 64, 8, "all_one_expert"),
                                         # the largest accepted shapes: E = 1024 with k = 32, and
                                         # max_tokens * k = 2^24 pairs through the one-block sort
